@@ -1,0 +1,182 @@
+"""Benchmark of one NVFP4 routed-MoE layer on one MI355X.
+
+A step is the whole hot path on one batch of seeded synthetic input:
+moe_route -> nvfp4_quant -> moe_experts_fwd -> moe_finalize, replayed from HIP
+graphs (one per weight copy). The weights rotate over enough copies (>= 1 GiB)
+that the 256 MB Infinity Cache cannot hold them between uses, so weight bytes
+come from HBM (the cold-cache timing the flashinfer_ops page's tuning
+configuration asks for). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. ``roofline`` is the dominant kernel (the experts step)
+against HBM bandwidth: algorithmic bytes per launch (codes + e4m3 scales of the
+experts that have a route, the gathered input rows, the intermediate written and
+re-read, the GEMM2 rows written) over its average duration measured with HIP
+events on its own stream. ``cpu_baseline`` is the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_b8]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="decode_b8")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle's CPU-baseline sample (0 disables)")
+    ap.add_argument("--rotate-bytes", type=float, default=1.0e9)
+    return ap.parse_args()
+
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(wl, counts) -> dict:
+    """Bytes the experts step must move at least once per call."""
+    touched = int((counts > 0).sum())
+    H, I = wl.H, wl.I
+    per_expert = 2 * I * H // 2 + 2 * I * H // 16 + H * I // 2 + H * I // 16   # 27/16 I H
+    routes = int(counts.sum())
+    act = wl.T * (H // 2 + H // 16)                        # quantized input, read once
+    inter = routes * (I // 2 + I // 16) * 2                # intermediate written + read
+    rows = routes * H * 2                                  # GEMM2 bf16 rows written
+    return dict(weights=touched * per_expert, touched=touched, other=act + inter + rows,
+                total=touched * per_expert + act + inter + rows)
+
+
+def cpu_baseline(inp, seconds: float) -> dict:
+    from threadpoolctl import threadpool_info
+    from oracle.layer import layer as o_layer
+    wl = inp.wl
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        o_layer(inp)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": wl.T * wl.K * n / dt, "unit": "routed rows/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} whole-layer oracle evaluations of {wl.name} ({wl.T * wl.K} routes each), "
+                      f"{dt:.1f} s, numpy fp64 with BLAS on {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path: expert TP is reproduced sequentially on one GPU.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from nvfp4_block_scaled_route_amd import layer as LY
+    from nvfp4_block_scaled_route_amd import native as N
+    from nvfp4_block_scaled_route_amd import workloads as W
+
+    N.lib()
+    dev = "cuda:0"
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl)
+
+    def t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    g1a, g1c, g2a = t(inp.g1_alphas), t(inp.g1_scale_c), t(inp.g2_alphas)
+    logical = [t(inp.w13_codes), t(inp.w13_sf), t(inp.w2_codes), t(inp.w2_sf)]
+    wbytes = sum(x.numel() for x in logical)
+    copies = max(4, int(np.ceil(args.rotate_bytes / wbytes)))
+    weights = [LY.pack_weights(*logical, g1a, g1c, g2a) for _ in range(copies)]
+    del logical
+    x, gscale, logits = t(inp.x_bf16), t(inp.a1_gscale), t(inp.logits)
+    norm_w = t(inp.norm_weight_bf16)
+    shape = LY.LayerShape(wl.T, wl.H, wl.I, wl.E, wl.K, wl.tile_m, wl.tp)
+    bufs = LY.Buffers(shape, dev)
+    slices = None
+
+    def step(w, stream=None):
+        sl = None if wl.tp == 1 else [LY.slice_weights(w, r, wl.tp, wl.H, wl.I) for r in range(wl.tp)]
+        LY.run_layer(bufs, x, gscale, logits, None, None, w, norm_w, wl.gain_center, wl.eps,
+                     bool(wl.weight_before_norm), slices=sl, stream=stream)
+
+    # eager warm-up, then one graph per weight copy, captured on a side stream
+    for i in range(3):
+        step(weights[i % copies])
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    graphs = []
+    for w in weights:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(w)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+
+    # timed region: K whole-layer steps
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # the dominant kernel, timed with HIP events on the stream it is launched on;
+    # a sleep kernel ahead of each timed launch keeps host enqueue time out of it
+    counts = bufs.meta[bufs.layout.expert_counts:bufs.layout.expert_counts + wl.E].cpu().numpy()
+    ab = algorithmic_bytes(wl, counts)
+    s = torch.cuda.current_stream()
+    n_k = min(args.steps, 400)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    I_part = wl.I // wl.tp
+    for i in range(n_k):
+        w = weights[i % copies]
+        sl = [w] if wl.tp == 1 else [LY.slice_weights(w, r, wl.tp, wl.H, wl.I) for r in range(wl.tp)]
+        torch.cuda._sleep(20000)
+        ev[i][0].record(s)
+        for r, ww in enumerate(sl):
+            N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H, I_part,
+                              wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], s)
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    achieved = ab["total"] / (k_ms * 1e-3) / 1e9
+
+    routes = wl.T * wl.K
+    out = {
+        "metric": "routed rows/s per MoE layer; HBM GB/s (decode) & MFMA util (prefill) vs peak",
+        "value": routes / (ms_per_step * 1e-3),
+        "unit": "routed rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
+                   "tp": wl.tp, "tile_m": wl.tile_m, "weight_copies": copies},
+        "roofline": {"bound": "hbm", "kernel": "moe_experts_fwd (GEMM1+SwiGLU+requant, GEMM2)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
+                     "experts_touched": ab["touched"], "kernel_ms": k_ms},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

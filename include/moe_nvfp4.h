@@ -1,0 +1,246 @@
+/*
+ * moe_nvfp4.h -- C-ABI of libmoe_nvfp4.so: one MoE layer's NVFP4 routed-expert
+ * computation on an AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on four pages of the vLLM API reference:
+ *   [expert_tp]      vllm.models.muse_spark.nvidia.specialized_decode.runtime.expert_tp
+ *   [flashinfer_ops] vllm.models.muse_spark.nvidia.specialized_decode.runtime.flashinfer_ops
+ *   [runner]         vllm.models.muse_spark.nvidia.muse_moe_runner
+ *   [model]          vllm.models.muse_spark.nvidia.model
+ * A layer runs, on one stream, in this order:
+ *   moe_route -> nvfp4_quant -> moe_experts_fwd -> moe_finalize
+ * (the model page, "_prepared_nvfp4_forward", prepares the quantized input and
+ * the routing; the runner page, "MuseSparkTrtLlmNvFp4Experts.apply_routed", runs
+ * the experts up to the GEMM2 rows and hands them to "MusePostExpertFinalize").
+ *
+ * Conventions for every call
+ *   - Pointers named in the comments as "device" point to device memory of the
+ *     current HIP device; the caller allocates, owns and frees all of it. The
+ *     library allocates, frees and synchronizes nothing: a call validates its
+ *     arguments on the host, enqueues its kernels on `stream` (a hipStream_t,
+ *     NULL = the default stream) and returns. Nothing is read back to the host,
+ *     so every call can be captured into a HIP graph.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Return 0 on success or a negative MOE_E* code. Validation happens before
+ *     any launch, so a refused call leaves no partial work. moe_last_error()
+ *     returns the calling thread's message for its last failed call.
+ *   - Sizes are in elements unless named *_bytes or *_stride_bytes.
+ *   - bf16 values are passed as their uint16 bit patterns; e4m3 scales as
+ *     bytes (OCP float8 e4m3fn: bias 7, max 448, 0x7F/0xFF NaN).
+ *
+ * NVFP4 as this library stores it (the expert_tp page, "StockNvfp4"): two e2m1
+ * codes per byte, element 2j in the low nibble of byte j; one e4m3 scale per 16
+ * consecutive elements of a row; plus one fp32 global scale per tensor.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_NVFP4_ABI_VERSION 1
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
+#define MOE_EUNSUPPORTED (-2) /* a shape the kernels do not take (divisibility, limits) */
+#define MOE_ELAUNCH (-3)      /* a HIP launch failed */
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 1024  /* E and E_local */
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_HIDDEN 16384  /* H in moe_finalize */
+
+int moe_abi_version(void);
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------ sizing
+ * rows_max: the padded permuted rows a routing of T tokens x K routes over
+ * E_local experts can need with tile m:
+ *   (min(E_local, T*K) + (T*K - min(E_local, T*K)) / m) * m
+ * -- the bound of the flashinfer_ops page, "gemm2_rows", without that op's
+ * 128 KiB floor. Returns -1 for invalid arguments. */
+int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
+
+/* The int32 routing-metadata buffer written by moe_route and read by
+ * moe_experts_fwd / moe_finalize. Fields are indices into the buffer (int32
+ * units); every field starts at a multiple of 64. Contents after moe_route:
+ *   num_tiles       [1]          tiles holding routes (sum over experts of ceil(count/m))
+ *   total_rows      [1]          num_tiles * m
+ *   expert_offsets  [E_local+1]  first permuted row of each local expert; last = total_rows
+ *   expert_counts   [E_local]    routes per local expert
+ *   exp2perm        [T*K]        permuted row of route t*K+k, or -1 (padding token
+ *                                or expert not local: "not served here")
+ *   perm2tok        [rows_max]   token of each permuted row; -1 for padding rows
+ *                                and for every row >= total_rows
+ *   tile_expert     [rows_max/m] local expert of each tile; -1 beyond num_tiles
+ * Order (the counting-sort reading of the flashinfer_ops page's metadata,
+ * "FlashInferOps.slot"): experts ascending, routes of one expert in ascending
+ * t*K+k, each expert's rows padded to a multiple of m. */
+typedef struct moe_meta_layout {
+    int64_t num_tiles;
+    int64_t total_rows;
+    int64_t expert_offsets;
+    int64_t expert_counts;
+    int64_t exp2perm;
+    int64_t perm2tok;
+    int64_t tile_expert;
+    int64_t total_ints; /* buffer length in int32 */
+    int64_t rows_max;
+    int64_t tiles_max;
+} moe_meta_layout;
+
+int moe_meta_layout_get(int T, int K, int E_local, int tile_m, moe_meta_layout* out);
+
+/* ------------------------------------------------------------------ routing
+ * Top-k routing of MuseSpark1x (the runner page, "validate_deployment": sigmoid
+ * scores, plus an expert bias, sum-renormalized, no expert groups; the model
+ * page, "MuseSpark1xMoE": router_score_division_eps 1e-15, renormalize,
+ * e_score_correction_bias; "_prepared_nvfp4_forward": padding tokens route
+ * nowhere), then the permutation metadata above.
+ *   s_e   = sigmoid(logit_e), by a fixed fp32 algorithm (Cody-Waite range
+ *           reduction, degree-7 Taylor polynomial, no fused multiply-add)
+ *   key_e = s_e + bias_e; the K largest keys, ties to the lower expert index,
+ *           listed by key descending
+ *   w_k   = s_{e_k} / (sum_k s_{e_k} + 1e-15) * route_scale, fp32, sum over k in order
+ * The bias takes part in the selection only.
+ *   logits       device fp32 [T, E], row stride logits_row_stride (>= E), finite
+ *   expert_bias  device fp32 [E] or NULL (zeros)
+ *   is_padding   device uint8 [T] or NULL; nonzero: the token's ids are -1, weights 0
+ *   topk_ids     device int32 [T, K] out: global expert ids
+ *   topk_weights device fp32 [T, K] out
+ *   meta         device int32 [layout.total_ints] out (moe_meta_layout_get with
+ *                the same T, K, local_num_experts, tile_m)
+ * tile_m must be a multiple of 16, at most 256. Experts outside
+ * [local_expert_offset, local_expert_offset + local_num_experts) are not served
+ * here (exp2perm -1), as on an expert-parallel rank. */
+int moe_route(const float* logits, int64_t logits_row_stride, const float* expert_bias,
+              const uint8_t* is_padding, int T, int E, int K, float route_scale, int tile_m,
+              int local_expert_offset, int local_num_experts, int32_t* topk_ids,
+              float* topk_weights, int32_t* meta, void* stream);
+
+/* ------------------------------------------------------------------ quantizer
+ * NVFP4 quantization of the expert input with one global scale, scales in the
+ * plain row-major layout (the model page, "_prepared_nvfp4_forward":
+ * scaled_fp4_quant(x, global_scale, is_sf_swizzled_layout=False)). Per block of
+ * 16 values of a row, with every step one correctly rounded fp32 operation:
+ *   amax = max |x_i|;  s = (amax * gscale) / 6;  sf = e4m3(s)   (nearest even, saturating)
+ *   d = decode(sf);  code_i = 0 if d == 0, else e2m1(x_i * (gscale / d))
+ *   (e2m1: nearest even, saturating to 6; the sign bit follows the product)
+ *   x       device bf16 [T, H], row stride x_row_stride elements (>= H)
+ *   gscale  device fp32 [1]: the input global scale (a1_gscale = 1 / a13)
+ *   codes   device uint8 [T, H/2] out;  sf device uint8 [T, H/16] out
+ * H % 16 == 0. */
+int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
+                uint8_t* codes, uint8_t* sf, void* stream);
+
+/* ------------------------------------------------------------------ weights
+ * The converted weight layout the expert kernels read. The property the pages
+ * require of it (the expert_tp page, module docstring, "slice_views"): an
+ * expert-TP slice of the converted weights -- intermediate columns
+ * [r I', (r+1) I') -- is, byte for byte, the converted layout of the slice, so
+ * slices are views. This library's layout has it for I' % 64 == 0:
+ *   An NVFP4 matrix of N rows and K columns (N % 16 == 0, K % 64 == 0) is stored
+ *   per expert as [N/16 row groups][K/64 k-tiles] tiles; a tile holds 16 rows x
+ *   64 columns as 512 code bytes (array *_codes) and 64 scale bytes (array *_sf).
+ *   In a tile, element (n, k) is nibble (j & 1) of code byte
+ *   ((q*16 + n)*2 + s)*4 + j/2 with s = k/32, q = (k%32)/8, j = k%8, and the
+ *   scale of block b = k/16 of row n is scale byte ((b%2)*16 + n)*2 + b/2.
+ *   (One lane of a 64-wide wave reads 8 contiguous code bytes and 2 scale bytes
+ *   of a tile: its operand for two 16x16x32 MFMA steps.)
+ *   w13 [E, 2I, H] (N = 2I, K = H): converted row 32c + w is gate row 16c + w for
+ *   w < 16 and up row I + 16c + (w - 16) otherwise (the gated interleave), so
+ *   slice r is converted row groups [2rI'/16, 2(r+1)I'/16).
+ *   w2 [E, H, I] (N = H, K = I): slice r is k-tiles [rI'/64, (r+1)I'/64) of every
+ *   row group.
+ * moe_pack_w13 / moe_pack_w2 convert from the logical layout (the expert_tp
+ * page, "StockNvfp4": codes [E, N, K/2], scales [E, N, K/16], row-major; w13
+ * rows [0, I) gate = w1, [I, 2I) up = w3) into this one. Device buffers, no
+ * overlap; the outputs have the same byte counts as the inputs. */
+int moe_pack_w13(const uint8_t* codes, const uint8_t* sf, int E, int I, int H, uint8_t* out_codes,
+                 uint8_t* out_sf, void* stream);
+int moe_pack_w2(const uint8_t* codes, const uint8_t* sf, int E, int H, int I, uint8_t* out_codes,
+                uint8_t* out_sf, void* stream);
+
+/* Converted experts as the expert kernels take them: base pointers and byte
+ * strides, so that an expert-TP slice is passed as a view with no copy
+ * (the expert_tp page, "TpExperts", "slice_views").
+ *   w13, w13_sf: expert e, row group g at base + e*expert_stride + g*group_stride
+ *                (k-tiles of a row group contiguous: 512 / 64 bytes each)
+ *   w2, w2_sf:   likewise; for slice r of tp of a full-width w2 the base moves
+ *                by r*(I'/64) tiles and group_stride stays the full width's
+ *   g1_alphas, g1_scale_c, g2_alphas: device fp32 [E_local], the folded scalars
+ *     (the runner page, "process_weights_after_loading": g1_alphas = a13*w1_gs,
+ *     g1_scale_c = a13*w3_gs/a2, g2_alphas = a2*w2_gs; the expert_tp page: they
+ *     do not depend on the slice). */
+typedef struct moe_nvfp4_weights {
+    const uint8_t* w13;
+    const uint8_t* w13_sf;
+    const uint8_t* w2;
+    const uint8_t* w2_sf;
+    int64_t w13_expert_stride_bytes;
+    int64_t w13_group_stride_bytes;
+    int64_t w13_sf_expert_stride_bytes;
+    int64_t w13_sf_group_stride_bytes;
+    int64_t w2_expert_stride_bytes;
+    int64_t w2_group_stride_bytes;
+    int64_t w2_sf_expert_stride_bytes;
+    int64_t w2_sf_group_stride_bytes;
+    const float* g1_alphas;
+    const float* g1_scale_c;
+    const float* g2_alphas;
+} moe_nvfp4_weights;
+
+/* ------------------------------------------------------------------ experts
+ * The routed experts up to the GEMM2 rows, as the op with do_finalize=False
+ * computes them (the runner page, "MuseSparkTrtLlmNvFp4Experts.apply_routed";
+ * the flashinfer_ops page, "routed_experts_from_metadata"). For every permuted
+ * row p that holds a route (token t = perm2tok[p], expert e of its tile):
+ *   acc1[n]  = sum_h dq(a[t, h]) * dq(w13[e, n, h])      n < 2I, fp32 accumulate
+ *   g = acc1_gate * g1_alphas[e];  u = acc1_up * g1_scale_c[e];  h = silu(g) * u
+ *   (inter_codes[p], inter_sf[p]) = NVFP4 of h along I with global scale 1
+ *   acc2[n]  = sum_i dq(h[i]) * dq(w2[e, n, i])           n < H
+ *   rows[p, n] = bf16(acc2[n] * g2_alphas[e])             nearest even
+ * dq(.) = e2m1 code * e4m3 scale of its block; every product is exact in the
+ * f16 MFMA operands. Padding rows are not written.
+ *   a_codes, a_sf  device [T, H/2], [T, H/16]  (nvfp4_quant's output)
+ *   meta           moe_route's metadata for the same T, K, E_local, tile_m
+ *   w              converted experts (host struct; pointers in it are device)
+ *   inter_codes, inter_sf  device [rows_max, I/2], [rows_max, I/16]: the
+ *                  requantized intermediate (written, then read by GEMM2)
+ *   rows           device bf16 [rows_max, rows_stride] out, rows_stride >= H
+ * H % 64 == 0, I % 64 == 0, tile_m % 16 == 0. */
+int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const int32_t* meta,
+                    const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                    int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
+                    int64_t rows_stride, void* stream);
+
+/* ------------------------------------------------------------------ finalize
+ * Post-expert finalize (the runner page, "MusePostExpertFinalize",
+ * "_finalize_native", "_finalize_chunk", "_effective_weight"): for each token t
+ *   r_k = route k's GEMM2 row, rows[exp2perm[t,k]] (zero if the index is -1);
+ *         with n_partials > 1 the partials are summed in fp32 and rounded once
+ *         to bf16 before the norm (tensor-parallel K-partials; the expert_tp
+ *         page, "probe_rel_l2"; the runner page, "_finalize_chunk")
+ *   gamma = fp32(norm_weight) + gain_center         (norm_weight NULL: ones)
+ *   weight_before_norm: y = z / sqrt(mean(z^2) + eps), z = gamma * r
+ *   otherwise:          y = gamma * (r / sqrt(mean(r^2) + eps))
+ *   out[t] = bf16(sum_k topk_weights[t,k] * y_k)    fp32, k ascending
+ *   rows          device bf16, partial q's row p at rows + q*partial_stride + p*rows_stride
+ *   exp2perm      device int32 [T, K] (the meta buffer's field)
+ *   topk_weights  device fp32 [T, K]
+ *   norm_weight   device bf16 [H] or NULL
+ *   out           device bf16 [T, H]
+ * H % 8 == 0, H <= MOE_MAX_HIDDEN, 1 <= n_partials <= 16. */
+int moe_finalize(const uint16_t* rows, int64_t rows_stride, int n_partials,
+                 int64_t partial_stride, const int32_t* exp2perm, const float* topk_weights,
+                 const uint16_t* norm_weight, float gain_center, float eps,
+                 int weight_before_norm, int T, int K, int H, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

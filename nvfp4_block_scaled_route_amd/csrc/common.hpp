@@ -1,0 +1,153 @@
+// Shared device helpers and host error plumbing of libmoe_nvfp4 (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_nvfp4.h"
+
+namespace moe {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ host side
+int fail(int code, const char* fmt, ...);          // sets the thread's message, returns code
+int check_launch(const char* what);                // MOE_ELAUNCH on a pending launch error
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m);
+
+// ------------------------------------------------------------------ codecs
+// e2m1: nearest value of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,
+// saturating at 6; the sign bit follows the input (NaN encodes to +0). Each
+// threshold is a midpoint of the grid; >= where the upper neighbour has the
+// even code, > where the lower one has.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    if (!(v == v)) return 0u;
+    const float a = __builtin_fabsf(v);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// e4m3fn (bias 7, subnormals m * 2^-9, max 448): nearest even, saturating to
+// +-448; NaN encodes to 0x7F. Works on the fp32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    if (!(v == v)) return 0x7Fu;
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = __builtin_fabsf(v);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {                       // below 2^-6: the subnormal grid
+        code = (uint32_t)__builtin_rintf(a * 512.0f); // exact scaling, ties to even
+    } else {
+        const uint32_t ab = __float_as_uint(a);
+        uint32_t e = (ab >> 23) - 120u;               // biased e4m3 exponent, 1 .. 15
+        uint32_t m = (ab >> 20) & 7u;
+        const uint32_t rem = ab & 0xFFFFFu;
+        if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+        if (m == 8u) { m = 0u; ++e; }
+        code = (e << 3) | m;
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return code | sign;
+}
+
+// e4m3fn byte -> fp32 (exact; NaN codes are not decoded).
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float mag = e == 0u ? (float)m * 0.001953125f
+                              : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// The NVFP4 block scale and the element multiplier of one 16-value block:
+// s = (amax * gscale) / 6 -> e4m3 byte; r = gscale / decode(byte) (0 when the
+// scale decodes to 0). One correctly rounded fp32 operation per step.
+struct BlockScale {
+    uint32_t byte;
+    float r;
+};
+__device__ __forceinline__ BlockScale nvfp4_block_scale(float amax, float gscale) {
+#pragma clang fp contract(off)
+    const float s = __fdiv_rn(__fmul_rn(amax, gscale), 6.0f);
+    BlockScale out;
+    out.byte = e4m3_encode(s);
+    const float d = e4m3_decode(out.byte);
+    out.r = d == 0.0f ? 0.0f : __fdiv_rn(gscale, d);
+    return out;
+}
+
+// The e2m1 code of one element given its block's multiplier (code 0 when the
+// block scale is 0).
+__device__ __forceinline__ uint32_t nvfp4_code(float x, const BlockScale& bs) {
+    return bs.r == 0.0f ? 0u : e2m1_encode(__fmul_rn(x, bs.r));
+}
+
+// ------------------------------------------------------------------ sigmoid
+// s(l) = 1 / (1 + exp(-l)). exp by Cody and Waite's range reduction
+// x = n ln2 + r, with ln2 split so that n * ln2_hi is exact, and the degree-7
+// Taylor polynomial of e^r in Horner form; every step is a separate, correctly
+// rounded fp32 operation (no fused multiply-add). exp(x) for x > 80 gives a
+// sigmoid of 0, for x < -20 a sigmoid of 1 (e^x is below half an ulp of 1).
+__device__ __forceinline__ float sigmoid32(float l) {
+#pragma clang fp contract(off)
+    const float x = -l;
+    if (x > 80.0f) return 0.0f;
+    if (x < -20.0f) return 1.0f;
+    const float n = __builtin_rintf(__fmul_rn(x, 1.4426950408889634f));
+    float r = __fsub_rn(x, __fmul_rn(n, 0.693359375f));
+    r = __fsub_rn(r, __fmul_rn(n, (float)(0.6931471805599453 - 0.693359375)));
+    float p = (float)(1.0 / 5040.0);
+    p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 720.0));
+    p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 120.0));
+    p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 24.0));
+    p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 6.0));
+    p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+    const float e = __builtin_ldexpf(p, (int)n);
+    return __fdiv_rn(1.0f, __fadd_rn(1.0f, e));
+}
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {   // nearest even
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return 0x7FC0u;   // NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------ NVFP4 -> f16 operands
+// 8 e2m1 codes (a u32, element 0 in the low nibble) times one e4m3 scale -> the
+// 8 exact f16 products. The hardware pack-convert applies only the exponent of
+// its scale operand, so it runs at scale 1 and the e4m3 scale (exact in f16)
+// multiplies after it; every product e2m1 * e4m3 has at most 6 significant bits
+// and lies in [2^-10, 2688], so it is exact in f16.
+__device__ __forceinline__ half8 nvfp4x8_to_f16(uint32_t codes, _Float16 scale) {
+    const half2v s = {scale, scale};
+    const half2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+    const half2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+    const half2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+    const half2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+    half8 out;
+    out[0] = v0[0]; out[1] = v0[1]; out[2] = v1[0]; out[3] = v1[1];
+    out[4] = v2[0]; out[5] = v2[1]; out[6] = v3[0]; out[7] = v3[1];
+    return out;
+}
+
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) { return (_Float16)e4m3_decode(b); }
+
+// ------------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max16(float v) {      // max over 16-lane rows
+    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 1));
+    return v;
+}
+
+}  // namespace moe

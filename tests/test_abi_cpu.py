@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports every function include/moe_nvfp4.h declares,
+and its host-side sizing and validation behave as documented. No GPU: every
+call here returns before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from nvfp4_block_scaled_route_amd import native as N
+from oracle.permute import rows_max as oracle_rows_max
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    decl = declared_functions()
+    assert set(decl) == set(N.EXPORTS), decl
+
+
+def test_library_exports_every_declared_symbol():
+    L = N.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+
+
+@pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
+                                     (4096, 8, 128, 128), (32, 8, 128, 16), (1, 1, 1, 16),
+                                     (0, 8, 8, 16), (3, 5, 1000, 256)])
+def test_rows_max_matches_oracle(T, K, E, m):
+    assert N.moe_rows_max(T, K, E, m) == oracle_rows_max(T, K, E, m)
+    lay = N.moe_meta_layout_get(T, K, E, m)
+    assert lay.rows_max == oracle_rows_max(T, K, E, m) and lay.tiles_max * m == lay.rows_max
+    fields = [lay.expert_offsets, lay.expert_counts, lay.exp2perm, lay.perm2tok, lay.tile_expert]
+    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max]
+    assert all(f % 64 == 0 for f in fields)
+    for (f, n), nxt in zip(zip(fields, sizes), fields[1:] + [lay.total_ints]):
+        assert f + n <= nxt
+    assert lay.num_tiles < 64 and lay.total_rows < 64 and lay.num_tiles != lay.total_rows
+
+
+def test_invalid_sizes_are_refused():
+    L = N.lib()
+    f = ctypes.c_float
+    assert L.moe_rows_max(-1, 8, 8, 16) == -1
+    with pytest.raises(N.MoeError):
+        N.moe_meta_layout_get(8, 8, 64, 24)            # tile not a multiple of 16
+    cases = [
+        (L.moe_route, (None, 8, None, None, 4, 8, 9, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EUNSUPPORTED),  # K > E
+        (L.moe_route, (None, 8, None, None, 4, 2000, 2, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_route, (None, 8, None, None, 4, 8, 2, f(1.0), 8, 0, 8, None, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_route, (None, 4, None, None, 4, 8, 2, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EINVAL),  # stride < E
+        (L.nvfp4_quant, (None, 24, None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
+        (L.nvfp4_quant, (None, 32, None, 4, 32, None, None, None), N.MOE_EINVAL),         # NULL
+        (L.moe_pack_w13, (None, None, 2, 24, 64, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_pack_w2, (None, None, 2, 64, 96, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_finalize, (None, 64, 1, 0, None, None, None, f(1.0), f(1e-6), 1, 4, 2, 60, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_finalize, (None, 64, 17, 0, None, None, None, f(1.0), f(1e-6), 1, 4, 2, 64, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_finalize, (None, 64, 1, 0, None, None, None, f(1.0), f(1e-6), 1, 4, 2, 64, None, None), N.MOE_EINVAL),
+    ]
+    for fn, args, want in cases:
+        assert fn(*args) == want, (fn.__name__, L.moe_last_error())
+        assert L.moe_last_error()
+
+
+def test_experts_refusals():
+    L = N.lib()
+    w = N.MoeNvfp4Weights()
+    args = lambda H, I, m: (None, None, None, ctypes.byref(w), 4, 2, 8, H, I, m, None, None, None, H, None)
+    assert L.moe_experts_fwd(*args(96, 128, 16)) == N.MOE_EUNSUPPORTED     # H % 64
+    assert L.moe_experts_fwd(*args(256, 96, 16)) == N.MOE_EUNSUPPORTED     # I % 64
+    assert L.moe_experts_fwd(*args(256, 128, 48 + 1)) == N.MOE_EUNSUPPORTED
+    assert L.moe_experts_fwd(*args(256, 128, 16)) == N.MOE_EINVAL          # NULL pointers
+    assert L.moe_experts_fwd(None, None, None, None, 4, 2, 8, 256, 128, 16, None, None, None, 256, None) == N.MOE_EINVAL
+    # strides too small for the shape: checked before any launch
+    w.w13 = w.w13_sf = w.w2 = w.w2_sf = 256
+    w.g1_alphas = w.g1_scale_c = w.g2_alphas = 256
+    assert L.moe_experts_fwd(256, 256, 256, ctypes.byref(w), 4, 2, 8, 256, 128, 16, 256, 256, 256, 256, None) == N.MOE_EINVAL
+    assert b"stride" in L.moe_last_error()
+
+
+def test_zero_tokens_is_a_no_op_without_device():
+    L = N.lib()
+    assert L.nvfp4_quant(None, 64, None, 0, 64, None, None, None) == N.MOE_OK
+    assert L.moe_finalize(None, 64, 1, 0, None, None, None, ctypes.c_float(1.0), ctypes.c_float(1e-6), 1, 0, 2, 64, None, None) == N.MOE_OK

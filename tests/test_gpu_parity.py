@@ -1,0 +1,374 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Bit-exact: the NVFP4 quantizer's codes and scales, the routing ids and weights,
+every field of the permutation metadata, the weight converter. Floating point:
+the final bf16 outputs and the GEMM2 route rows within rel-L2 1e-2 (the
+pages' rel-L2 probe criterion, the expert_tp page, "probe_rel_l2"); the
+requantized intermediate is reported, and its scale bytes and codes must agree
+except at rare fp32 rounding boundaries (several results are correct there)."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_route_amd import layer as LY
+from nvfp4_block_scaled_route_amd import native as N
+from nvfp4_block_scaled_route_amd import workloads as W
+from oracle import formats as F
+from oracle import layout as OL
+from oracle.finalize import finalize as o_finalize
+from oracle.layer import layer as o_layer, layer_sampled, quantize_input, rel_l2
+from oracle.permute import permute as o_permute
+from oracle.quant import quantize_nvfp4
+from oracle.routing import route as o_route
+
+from .gpu_common import DEV, dev, host, run_layer, say, upload_weights
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache[name] = W.make_inputs(W.WORKLOADS[name])
+        return cache[name]
+    return get
+
+
+# ------------------------------------------------------------------ quantizer
+def _gpu_quant(x_bf16: np.ndarray, gscale: float):
+    T, H = x_bf16.shape
+    codes = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
+    sf = torch.empty((T, H // 16), dtype=torch.uint8, device=DEV)
+    say(f"nvfp4_quant T={T} H={H} gscale={gscale}")
+    N.nvfp4_quant(dev(x_bf16), dev(np.array([gscale], np.float32)), codes, sf)
+    torch.cuda.synchronize()
+    return host(codes), host(sf)
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_quant_bit_exact_on_workload(inputs, name):
+    inp = inputs(name)
+    codes, sf = _gpu_quant(inp.x_bf16, float(inp.a1_gscale[0]))
+    oc, osf = quantize_input(inp)
+    assert np.array_equal(sf, osf)
+    assert np.array_equal(codes, oc)
+
+
+def _edge_rows():
+    rng = np.random.default_rng(11)
+    rows = []
+    z = np.zeros(64, np.float32)
+    rows.append(z.copy())                                       # all zero
+    r = z.copy(); r[5] = 7.0; rows.append(r)                    # single spike
+    rows.append(np.full(64, -0.0, np.float32))                  # negative zeros
+    rows.append(np.full(64, 3e-40, np.float32))                 # underflowing scale
+    rows.append(np.array([2.0 ** -9 * 6 * (i % 3) for i in range(64)], np.float32))
+    r = (F.E2M1[rng.integers(0, 16, 64)] * 0.75).astype(np.float32); r[::16] = 6 * 0.75
+    rows.append(r)                                              # exact grid
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    r = np.tile(np.concatenate([mids, -mids]), 4); r[::16] = 6.0
+    rows.append(r)                                              # ties
+    rows.append(np.full(64, 3.0e38, np.float32))                # huge
+    rows.append((rng.standard_normal(64) * 1e4).astype(np.float32))
+    rows.append((rng.standard_normal(64) * 1e-6).astype(np.float32))
+    x = np.stack(rows)
+    return F.f32_to_bf16(x)
+
+
+@pytest.mark.parametrize("gscale", [1.0, 0.37, 3.5, 448.0, 1e-3])
+def test_quant_bit_exact_edge_blocks(gscale):
+    x = _edge_rows()
+    rng = np.random.default_rng(5)
+    extra = F.f32_to_bf16((rng.standard_normal((37, 64 * 3)) *
+                           np.exp2(rng.integers(-20, 20, (37, 1)))).astype(np.float32))
+    for xb in (x, extra):
+        codes, sf = _gpu_quant(xb, gscale)
+        oc, osf = quantize_nvfp4(F.bf16_to_f64(xb).astype(np.float32), gscale)
+        assert np.array_equal(sf, osf)
+        assert np.array_equal(codes, oc)
+
+
+def test_quant_all_bf16_patterns():
+    """Every finite bf16 value passes through the quantizer, in blocks that
+    mix magnitudes, at several global scales."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = F.bf16_to_f64(bits)
+    bits = bits[np.isfinite(v)]
+    rng = np.random.default_rng(2)
+    for trial in range(3):
+        perm = rng.permutation(bits.size)
+        n = (bits.size // 64) * 64
+        xb = bits[perm][:n].reshape(-1, 64)
+        for g in (1.0, 2.0 ** -100, 5.25):
+            codes, sf = _gpu_quant(xb, g)
+            oc, osf = quantize_nvfp4(F.bf16_to_f64(xb).astype(np.float32), g)
+            assert np.array_equal(sf, osf) and np.array_equal(codes, oc)
+
+
+# ------------------------------------------------------------------ routing
+def _gpu_route(logits, bias, K, tile_m, offset=0, local=None, padding=None, route_scale=1.0):
+    T, E = logits.shape
+    local = E if local is None else local
+    L = N.moe_meta_layout_get(T, K, local, tile_m)
+    ids = torch.full((T, K), 12345, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), 7.0, dtype=torch.float32, device=DEV)
+    meta = torch.full((L.total_ints + 64,), -777, dtype=torch.int32, device=DEV)
+    say(f"moe_route T={T} E={E} K={K} m={tile_m} local=[{offset},+{local})")
+    N.moe_route(dev(logits), None if bias is None else dev(bias),
+                None if padding is None else dev(padding.astype(np.uint8)), K, route_scale,
+                tile_m, offset, local, ids, w, meta)
+    torch.cuda.synchronize()
+    return host(ids), host(w), host(meta), L
+
+
+def _check_route(logits, bias, K, tile_m, offset=0, local=None, padding=None, route_scale=1.0):
+    T, E = logits.shape
+    local = E if local is None else local
+    ids, w, meta, L = _gpu_route(logits, bias, K, tile_m, offset, local, padding, route_scale)
+    oids, ow = o_route(logits, bias, K, route_scale, padding)
+    assert np.array_equal(ids, oids)
+    assert np.array_equal(w.view(np.uint32), ow.view(np.uint32))
+    om = o_permute(oids, offset, local, tile_m)
+    assert meta[L.num_tiles] == om["num_tiles"] and meta[L.total_rows] == om["total_rows"]
+    assert np.array_equal(meta[L.expert_offsets:L.expert_offsets + local + 1], om["offsets"])
+    assert np.array_equal(meta[L.expert_counts:L.expert_counts + local], om["counts"])
+    assert np.array_equal(meta[L.exp2perm:L.exp2perm + T * K], om["exp2perm"].reshape(-1))
+    assert np.array_equal(meta[L.perm2tok:L.perm2tok + L.rows_max], om["perm2tok"])
+    assert np.array_equal(meta[L.tile_expert:L.tile_expert + L.tiles_max], om["tile_expert"])
+    assert np.all(meta[L.total_ints:] == -777)                   # nothing written past the buffer
+    return ids, w, meta
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_route_bit_exact_on_workload(inputs, name):
+    inp = inputs(name)
+    _check_route(inp.logits, inp.expert_bias, inp.wl.K, inp.wl.tile_m)
+
+
+@pytest.mark.parametrize("T,E,K,m", [(1, 8, 1, 16), (7, 100, 5, 32), (9, 64, 8, 16),
+                                     (300, 256, 6, 64), (33, 1024, 32, 256), (2048, 16, 4, 128)])
+def test_route_shapes_bias_padding(T, E, K, m):
+    rng = np.random.default_rng(T * 131 + E)
+    logits = (rng.standard_normal((T, E)) * 8).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    pad = rng.random(T) < 0.1
+    _check_route(logits, bias, K, m, padding=pad, route_scale=1.5)
+
+
+def test_route_ties_and_wide_logits():
+    rng = np.random.default_rng(3)
+    T, E, K = 4096, 64, 8
+    logits = rng.choice(np.array([-30, -1, 0, 0.5, 2, 30], np.float32), (T, E))
+    _check_route(logits, None, K, 16)
+    wide = rng.uniform(-90, 90, (T, E)).astype(np.float32)
+    _check_route(wide, None, K, 16)
+
+
+def test_route_sigmoid_bits_many_tokens():
+    rng = np.random.default_rng(4)
+    logits = (rng.standard_normal((65536, 32)) * 6).astype(np.float32)
+    _check_route(logits, None, 8, 128)
+
+
+def test_route_expert_parallel_subset():
+    rng = np.random.default_rng(6)
+    logits = rng.standard_normal((40, 64)).astype(np.float32)
+    _, _, meta = _check_route(logits, None, 8, 16, offset=16, local=16)
+
+
+def test_route_zero_tokens():
+    L = N.moe_meta_layout_get(0, 8, 64, 16)
+    meta = torch.full((L.total_ints,), -5, dtype=torch.int32, device=DEV)
+    ids = torch.empty((0, 8), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, 8), dtype=torch.float32, device=DEV)
+    N.moe_route(torch.empty((0, 64), dtype=torch.float32, device=DEV), None, None, 8, 1.0, 16, 0,
+                64, ids, w, meta)
+    torch.cuda.synchronize()
+    m = host(meta)
+    assert m[L.num_tiles] == 0 and m[L.total_rows] == 0
+    assert np.all(m[L.expert_offsets:L.expert_offsets + 65] == 0)
+
+
+# ------------------------------------------------------------------ weight converter
+@pytest.mark.parametrize("E,H,I", [(3, 256, 128), (4, 512, 256), (2, 2048, 768)])
+def test_pack_bit_exact(E, H, I):
+    rng = np.random.default_rng(E * H + I)
+    w13c = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
+    w13s = rng.integers(0, 256, (E, 2 * I, H // 16), dtype=np.uint8)
+    w2c = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w2s = rng.integers(0, 256, (E, H, I // 16), dtype=np.uint8)
+    say(f"moe_pack E={E} H={H} I={I}")
+    w = LY.pack_weights(dev(w13c), dev(w13s), dev(w2c), dev(w2s),
+                        *(torch.ones(E, device=DEV) for _ in range(3)))
+    torch.cuda.synchronize()
+    o13 = OL.convert_w13(w13c, w13s)
+    o2 = OL.convert_w2(w2c, w2s)
+    assert np.array_equal(host(w.w13).reshape(-1), o13[0].reshape(-1))
+    assert np.array_equal(host(w.w13_sf).reshape(-1), o13[1].reshape(-1))
+    assert np.array_equal(host(w.w2).reshape(-1), o2[0].reshape(-1))
+    assert np.array_equal(host(w.w2_sf).reshape(-1), o2[1].reshape(-1))
+
+
+# ------------------------------------------------------------------ finalize
+@pytest.mark.parametrize("wbn,npart,use_norm", [(1, 1, True), (0, 1, True), (1, 8, True),
+                                                (1, 1, False), (0, 3, False)])
+def test_finalize_against_oracle(wbn, npart, use_norm):
+    rng = np.random.default_rng(7 + npart)
+    T, K, H, R = 37, 8, 4096, 400
+    parts = [F.f32_to_bf16((rng.standard_normal((R, H)) * rng.uniform(0.1, 50)).astype(np.float32))
+             for _ in range(npart)]
+    e2p = rng.integers(-1, R, (T, K)).astype(np.int32)
+    wts = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    nw = F.f32_to_bf16(rng.uniform(-0.1, 0.1, H).astype(np.float32)) if use_norm else None
+    rows = torch.stack([dev(p) for p in parts])
+    out = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    say(f"moe_finalize T={T} K={K} H={H} partials={npart} wbn={wbn}")
+    N.moe_finalize(rows, npart, rows.stride(0), dev(e2p), dev(wts),
+                   None if nw is None else dev(nw), 1.0, 1e-6, wbn, T, K, H, out)
+    torch.cuda.synchronize()
+    got = F.bf16_to_f64(host(out))
+    if npart > 1:
+        want = o_finalize(None, e2p, wts, nw, 1.0, 1e-6, wbn, partials=parts)
+    else:
+        want = o_finalize(parts[0], e2p, wts, nw, 1.0, 1e-6, wbn)
+    want = F.bf16_to_f64(want)
+    assert rel_l2(got, want) < 1e-3
+    # fp32 against fp64 norm arithmetic: at most one bf16 step of the row's
+    # magnitude apart (the k-sum can cancel, so not of each element's own)
+    scale = np.abs(want).max(axis=1, keepdims=True)
+    assert np.all(np.abs(got - want) <= scale * 2.0 ** -7)
+
+
+# ------------------------------------------------------------------ whole layer
+def _compare_layer(res, ref, name):
+    p = ref["rows_idx"]
+    # routing and metadata: bit-exact
+    assert np.array_equal(res["ids"], ref["ids"])
+    assert np.array_equal(res["weights"].view(np.uint32), ref["weights"].view(np.uint32))
+    assert np.array_equal(res["exp2perm"], ref["meta"]["exp2perm"])
+    assert np.array_equal(res["perm2tok"], ref["meta"]["perm2tok"])
+    assert np.array_equal(res["a_codes"], ref["a_codes"]) and np.array_equal(res["a_sf"], ref["a_sf"])
+    # intermediate: agree except at rounding boundaries
+    sf_diff = np.mean(res["inter_sf"][p] != ref["h_sf"])
+    code_diff = np.mean(F.unpack_nibbles(res["inter_codes"][p]) != F.unpack_nibbles(ref["h_codes"]))
+    rows_rel = rel_l2(F.bf16_to_f64(res["rows"][0][p]), F.bf16_to_f64(ref["rows"][p]))
+    out_rel = rel_l2(F.bf16_to_f64(res["out"]), F.bf16_to_f64(ref["out"]))
+    say(f"{name}: inter scale diff {sf_diff:.2e}, code diff {code_diff:.2e}, "
+        f"rows rel-L2 {rows_rel:.2e}, out rel-L2 {out_rel:.2e}")
+    assert sf_diff < 1e-2 and code_diff < 2e-2
+    assert rows_rel < TOL
+    assert out_rel < TOL
+    return out_rel
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_b8"])
+def test_layer_parity_full_oracle(inputs, name):
+    inp = inputs(name)
+    res = run_layer(inp)
+    ref = o_layer(inp)
+    _compare_layer(res, ref, name)
+
+
+@pytest.mark.parametrize("tile_m", [32, 64, 256])
+def test_layer_parity_other_tiles(inputs, tile_m):
+    inp = inputs("decode_b8")
+    res = run_layer(inp, tile_m=tile_m)
+    ref = o_layer(inp, tile_m=tile_m)
+    _compare_layer(res, ref, f"decode_b8 m={tile_m}")
+
+
+def test_layer_parity_padding_tokens(inputs):
+    inp = inputs("tiny")
+    pad = np.array([False, True, False, False])
+    res = run_layer(inp, is_padding=pad)
+    ref = o_layer(inp, is_padding=pad)
+    _compare_layer(res, ref, "tiny padded")
+    assert np.all(res["ids"][1] == -1) and np.all(F.bf16_to_f64(res["out"][1]) == 0)
+
+
+@pytest.mark.slow
+def test_layer_parity_decode_b64_zipf(inputs):
+    inp = inputs("decode_b64_zipf")
+    res = run_layer(inp)
+    ref = o_layer(inp)
+    _compare_layer(res, ref, "decode_b64_zipf")
+    counts = res["counts"]
+    say(f"decode_b64_zipf: {int((counts > 0).sum())} experts touched, hottest {int(counts.max())} routes")
+
+
+def _compare_sampled(res, inp, tokens, name):
+    ref = layer_sampled(inp, tokens)
+    e2p = res["exp2perm"][tokens]
+    served = e2p >= 0
+    assert np.array_equal(served, ref["served"])
+    got_rows = F.bf16_to_f64(res["rows"][0][np.maximum(e2p, 0)])[served]
+    want_rows = F.bf16_to_f64(ref["route_rows"])[served]
+    rows_rel = rel_l2(got_rows, want_rows)
+    out_rel = rel_l2(F.bf16_to_f64(res["out"][tokens]), F.bf16_to_f64(ref["out"]))
+    say(f"{name}: sampled {len(tokens)} tokens, rows rel-L2 {rows_rel:.2e}, out rel-L2 {out_rel:.2e}")
+    assert rows_rel < TOL and out_rel < TOL
+    return ref
+
+
+@pytest.mark.slow
+def test_layer_parity_prefill_sampled(inputs):
+    inp = inputs("prefill_t4096")
+    res = run_layer(inp)
+    # routing, metadata and the quantizer over all tokens: bit-exact
+    a_codes, a_sf = quantize_input(inp)
+    assert np.array_equal(res["a_codes"], a_codes) and np.array_equal(res["a_sf"], a_sf)
+    oids, ow = o_route(inp.logits, inp.expert_bias, inp.wl.K)
+    assert np.array_equal(res["ids"], oids)
+    om = o_permute(oids, 0, inp.wl.E, inp.wl.tile_m)
+    assert np.array_equal(res["exp2perm"], om["exp2perm"])
+    assert np.array_equal(res["perm2tok"], om["perm2tok"])
+    tokens = np.random.default_rng(0).choice(inp.wl.T, 12, replace=False)
+    tokens = np.concatenate([tokens, [0, inp.wl.T - 1]])
+    _compare_sampled(res, inp, tokens, "prefill_t4096")
+
+
+@pytest.mark.slow
+def test_expert_tp_slices(inputs):
+    """Expert TP on one GPU: 8 slices of all experts at I' = 256, each a byte view
+    of the converted weights, give K-partial GEMM2 rows whose fp32 sum (one bf16
+    rounding) matches the full-width rows; the finalize on the summed partials
+    matches the oracle."""
+    inp = inputs("expert_tp8_b32")
+    wl = inp.wl
+    w = upload_weights(inp)
+    full = run_layer(inp, weights=w, tp=1)
+    sliced = run_layer(inp, weights=w, tp=wl.tp)
+    assert np.array_equal(full["exp2perm"], sliced["exp2perm"])
+    p = np.nonzero(full["perm2tok"] >= 0)[0]
+    part_sum = np.zeros((p.size, wl.H), np.float32)
+    for r in range(wl.tp):
+        part_sum = (part_sum + F.bf16_to_f64(sliced["rows"][r][p]).astype(np.float32)).astype(np.float32)
+    summed = F.bf16_to_f64(F.f32_to_bf16(part_sum))
+    probe = rel_l2(summed, F.bf16_to_f64(full["rows"][0][p]))
+    out_rel = rel_l2(F.bf16_to_f64(sliced["out"]), F.bf16_to_f64(full["out"]))
+    say(f"expert TP: slice-sum probe rel-L2 {probe:.2e}, finalize(partials) vs full {out_rel:.2e}")
+    assert probe < TOL and out_rel < TOL
+    tokens = np.arange(0, wl.T, 4)
+    _compare_sampled(full, inp, tokens, "expert_tp8 full width")
+    ref = layer_sampled(inp, tokens)
+    got = F.bf16_to_f64(sliced["out"][tokens])
+    assert rel_l2(got, F.bf16_to_f64(ref["out"])) < TOL
+
+
+def test_layer_leaves_padding_rows_untouched_and_is_deterministic(inputs):
+    inp = inputs("decode_b8")
+    w = upload_weights(inp)
+    a = run_layer(inp, weights=w, fill_rows=0x3F3F)
+    b = run_layer(inp, weights=w, fill_rows=0x3F3F)
+    pad = a["perm2tok"] < 0
+    assert np.all(a["rows"][0][pad] == 0x3F3F)
+    for k in ("rows", "out", "inter_codes", "inter_sf", "meta"):
+        x, y = a[k], b[k]
+        if k.startswith("inter"):
+            x, y = x[~pad[:x.shape[0]]], y[~pad[:y.shape[0]]]
+        assert np.array_equal(x, y), k
