@@ -48,8 +48,8 @@ def algorithmic_bytes(wl, counts) -> dict:
     H, I = wl.H, wl.I
     per_expert = 2 * I * H // 2 + 2 * I * H // 16 + H * I // 2 + H * I // 16   # 27/16 I H
     routes = int(counts.sum())
-    act = wl.T * (H // 2 + H // 16)                        # quantized input, read once
-    inter = routes * (I // 2 + I // 16) * 2                # intermediate written + read
+    act = wl.T * H * 2                                     # f16 input expansion, read once
+    inter = routes * (I // 2 + I // 16 + 2 * I * 2)        # NVFP4 intermediate written, f16 form written + read
     rows = routes * H * 2                                  # GEMM2 bf16 rows written
     return dict(weights=touched * per_expert, touched=touched, other=act + inter + rows,
                 total=touched * per_expert + act + inter + rows)
@@ -149,8 +149,8 @@ def main():
         torch.cuda._sleep(20000)
         ev[i][0].record(s)
         for r, ww in enumerate(sl):
-            N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H, I_part,
-                              wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], s)
+            N.moe_experts_fwd(bufs.a_dq, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H, I_part, wl.tile_m,
+                              bufs.inter_codes, bufs.inter_sf, bufs.inter_dq, bufs.rows[r], s)
         ev[i][1].record(s)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -167,7 +167,7 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
                    "tp": wl.tp, "tile_m": wl.tile_m, "weight_copies": copies},
-        "roofline": {"bound": "hbm", "kernel": "moe_experts_fwd (GEMM1+SwiGLU+requant, GEMM2)",
+        "roofline": {"bound": "hbm", "kernel": "moe_experts_fwd (gemm1_kernel: GEMM1+SwiGLU+requant, gemm2_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],

@@ -133,9 +133,13 @@ int moe_route(const float* logits, int64_t logits_row_stride, const float* exper
  *   x       device bf16 [T, H], row stride x_row_stride elements (>= H)
  *   gscale  device fp32 [1]: the input global scale (a1_gscale = 1 / a13)
  *   codes   device uint8 [T, H/2] out;  sf device uint8 [T, H/16] out
+ *   dq      device f16 [T, H] out: the exact f16 expansion of the result,
+ *           e2m1(code_i) * e4m3(sf) per element (in the globally scaled domain;
+ *           every such product is an f16 value). It is the form moe_experts_fwd
+ *           consumes: the MFMA operand, decoded once here.
  * H % 16 == 0. */
 int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
-                uint8_t* codes, uint8_t* sf, void* stream);
+                uint8_t* codes, uint8_t* sf, uint16_t* dq, void* stream);
 
 /* ------------------------------------------------------------------ weights
  * The converted weight layout the expert kernels read. The property the pages
@@ -204,19 +208,23 @@ typedef struct moe_nvfp4_weights {
  *   (inter_codes[p], inter_sf[p]) = NVFP4 of h along I with global scale 1
  *   acc2[n]  = sum_i dq(h[i]) * dq(w2[e, n, i])           n < H
  *   rows[p, n] = bf16(acc2[n] * g2_alphas[e])             nearest even
- * dq(.) = e2m1 code * e4m3 scale of its block; every product is exact in the
- * f16 MFMA operands. Padding rows are not written.
- *   a_codes, a_sf  device [T, H/2], [T, H/16]  (nvfp4_quant's output)
+ * dq(.) = e2m1 code * e4m3 scale of its block; every such value is exact in
+ * the f16 MFMA operands. Padding rows are not written.
+ *   a_dq           device f16 [T, H]: the NVFP4 input as nvfp4_quant's dq output
+ *                  (exact f16 expansion of its codes and scales)
  *   meta           moe_route's metadata for the same T, K, E_local, tile_m
  *   w              converted experts (host struct; pointers in it are device)
- *   inter_codes, inter_sf  device [rows_max, I/2], [rows_max, I/16]: the
- *                  requantized intermediate (written, then read by GEMM2)
+ *   inter_codes, inter_sf  device [rows_max, I/2], [rows_max, I/16] out: the
+ *                  requantized intermediate
+ *   inter_dq       device f16 [rows_max, I] out: its exact f16 expansion, which
+ *                  GEMM2 reads
  *   rows           device bf16 [rows_max, rows_stride] out, rows_stride >= H
- * H % 64 == 0, I % 64 == 0, tile_m % 16 == 0. */
-int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const int32_t* meta,
-                    const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
-                    int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
-                    int64_t rows_stride, void* stream);
+ * Two launches on `stream` (GEMM1 with the SwiGLU/requant epilogue, then GEMM2).
+ * H % 64 == 0, I % 64 == 0, H <= 8192, I <= 4096, tile_m % 16 == 0. */
+int moe_experts_fwd(const uint16_t* a_dq, const int32_t* meta, const moe_nvfp4_weights* w,
+                    int T, int K, int E_local, int H, int I, int tile_m, uint8_t* inter_codes,
+                    uint8_t* inter_sf, uint16_t* inter_dq, uint16_t* rows, int64_t rows_stride,
+                    void* stream);
 
 /* ------------------------------------------------------------------ finalize
  * Post-expert finalize (the runner page, "MusePostExpertFinalize",

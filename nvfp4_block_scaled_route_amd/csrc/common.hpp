@@ -126,20 +126,27 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {   // nearest even
 // 8 exact f16 products. The hardware pack-convert applies only the exponent of
 // its scale operand, so it runs at scale 1 and the e4m3 scale (exact in f16)
 // multiplies after it; every product e2m1 * e4m3 has at most 6 significant bits
-// and lies in [2^-10, 2688], so it is exact in f16.
-__device__ __forceinline__ half8 nvfp4x8_to_f16(uint32_t codes, _Float16 scale) {
-    const half2v s = {scale, scale};
-    const half2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
-    const half2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
-    const half2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
-    const half2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+// and lies in [2^-10, 2688], so it is exact in f16. `scale` holds the f16 scale
+// in both halves.
+__device__ __forceinline__ half8 nvfp4x8_to_f16(uint32_t codes, half2v scale) {
+    const half2v v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * scale;
+    const half2v v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * scale;
+    const half2v v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * scale;
+    const half2v v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * scale;
     half8 out;
     out[0] = v0[0]; out[1] = v0[1]; out[2] = v1[0]; out[3] = v1[1];
     out[4] = v2[0]; out[5] = v2[1]; out[6] = v3[0]; out[7] = v3[1];
     return out;
 }
 
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) { return (_Float16)e4m3_decode(b); }
+// Two e4m3 bytes (bits 0-7 and 8-15) -> two exact f16 values (the hardware
+// OCP e4m3 -> f16 conversion; scale 1 leaves the values unchanged).
+__device__ __forceinline__ half2v e4m3x2_to_f16(uint32_t two_bytes) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_bytes, 1.0f, false);
+}
+
+__device__ __forceinline__ half2v splat_lo(half2v v) { half2v r = {v[0], v[0]}; return r; }
+__device__ __forceinline__ half2v splat_hi(half2v v) { half2v r = {v[1], v[1]}; return r; }
 
 // ------------------------------------------------------------------ wave reductions
 __device__ __forceinline__ float wave_max16(float v) {      // max over 16-lane rows

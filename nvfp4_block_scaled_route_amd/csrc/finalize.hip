@@ -4,16 +4,18 @@
 // "_effective_weight". Tensor-parallel K-partial rows are summed in fp32 and
 // rounded once to bf16 before the norm (the expert_tp page, "probe_rel_l2").
 //
-// One 256-thread workgroup per token. A thread owns 8-element column chunks
-// c = tid, tid + 256, ...; pass 1 forms all K sums of squares (one block-wide
-// reduction for all routes at once), pass 2 re-reads the rows (cache hits) and
-// accumulates sum_k w_k * y_k in fp32, k ascending.
+// One 512-thread workgroup (8 waves) per token. Pass 1: wave w forms the sum of
+// squares of routes k = w, w + 8, ... (a lane walks 8-column chunks lane,
+// lane + 64, ...; then a fixed-order wave reduction), so no block-wide
+// reduction is needed. Pass 2: a thread owns 8-column chunks tid, tid + 512, ...
+// and accumulates sum_k w_k * y_k in fp32, k ascending. Rows are re-read in
+// pass 2 (cache hits). Every order is fixed: the output is deterministic.
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kFinThreads = 256;
-constexpr int kFinMaxChunks = MOE_MAX_HIDDEN / 8 / kFinThreads;   // 8
+constexpr int kFinThreads = 512;
+constexpr int kFinWaves = kFinThreads / 64;
 
 struct FinArgs {
     const uint16_t* rows;
@@ -29,18 +31,20 @@ struct FinArgs {
     uint16_t* out;
 };
 
-// 8 values of route row p at columns [8c, 8c + 8): partials summed in fp32,
-// rounded once to bf16 when there is more than one.
+// 8 values of route row p at columns [8c, 8c + 8): partials summed in fp32 in
+// order, rounded once to bf16 when there is more than one.
 __device__ __forceinline__ void load_row8(const FinArgs& a, int p, int c, float v[8]) {
     const uint16_t* base = a.rows + (int64_t)p * a.rows_stride + 8 * c;
     uint4 q = *reinterpret_cast<const uint4*>(base);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu); v[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+        for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu); v[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+    }
     if (a.n_partials > 1) {
         for (int part = 1; part < a.n_partials; ++part) {
             q = *reinterpret_cast<const uint4*>(base + part * a.partial_stride);
-            uint32_t u[4] = {q.x, q.y, q.z, q.w};
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[2 * i] = __fadd_rn(v[2 * i], bf16_to_f32(u[i] & 0xFFFFu));
@@ -52,80 +56,68 @@ __device__ __forceinline__ void load_row8(const FinArgs& a, int p, int c, float 
     }
 }
 
+__device__ __forceinline__ void gamma8(const FinArgs& a, int c, float g[8]) {
+    if (a.norm_weight) {
+        const uint4 q = *reinterpret_cast<const uint4*>(a.norm_weight + 8 * c);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            g[2 * i] = __fadd_rn(bf16_to_f32(w[i] & 0xFFFFu), a.gain_center);
+            g[2 * i + 1] = __fadd_rn(bf16_to_f32(w[i] >> 16), a.gain_center);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = __fadd_rn(1.0f, a.gain_center);
+    }
+}
+
 __global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinArgs a) {
-    __shared__ float red[kFinThreads / 64][MOE_MAX_TOPK];
+    __shared__ int s_perm[MOE_MAX_TOPK];
+    __shared__ float s_w[MOE_MAX_TOPK];
+    __shared__ float s_inv[MOE_MAX_TOPK];
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nchunks = a.H >> 3;
-    float gamma[kFinMaxChunks][8];
-#pragma unroll
-    for (int j = 0; j < kFinMaxChunks; ++j) {
-        const int c = tid + j * kFinThreads;
-        if (c < nchunks) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                gamma[j][i] = __fadd_rn(a.norm_weight ? bf16_to_f32(a.norm_weight[8 * c + i]) : 1.0f,
-                                        a.gain_center);
-        }
+    if (tid < a.K) {
+        s_perm[tid] = a.exp2perm[(int64_t)t * a.K + tid];
+        s_w[tid] = a.weights[(int64_t)t * a.K + tid];
     }
-    int perm[MOE_MAX_TOPK];
-    float ss[MOE_MAX_TOPK];
+    __syncthreads();
+    // pass 1: one wave per route
+    for (int k = wv; k < a.K; k += kFinWaves) {
+        const int p = s_perm[k];
+        float ss = 0.0f;
+        if (p >= 0) {
+            for (int c = lane; c < nchunks; c += 64) {
+                float v[8], g[8];
+                load_row8(a, p, c, v);
+                if (a.weight_before_norm) gamma8(a, c, g);
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        perm[k] = k < a.K ? a.exp2perm[(int64_t)t * a.K + k] : -1;
-        ss[k] = 0.0f;
-        if (perm[k] >= 0) {
-#pragma unroll
-            for (int j = 0; j < kFinMaxChunks; ++j) {
-                const int c = tid + j * kFinThreads;
-                if (c < nchunks) {
-                    float v[8];
-                    load_row8(a, perm[k], c, v);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float z = a.weight_before_norm ? __fmul_rn(gamma[j][i], v[i]) : v[i];
-                        ss[k] = __fadd_rn(ss[k], __fmul_rn(z, z));
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    const float z = a.weight_before_norm ? __fmul_rn(g[i], v[i]) : v[i];
+                    ss = __fadd_rn(ss, __fmul_rn(z, z));
                 }
             }
         }
-    }
-    // block-wide sums of squares, all routes at once
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        if (k < a.K) {
-            float s = ss[k];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) s = __fadd_rn(s, __shfl_xor(s, off));
-            if (lane == 0) red[wv][k] = s;
-        }
+        for (int off = 32; off >= 1; off >>= 1) ss = __fadd_rn(ss, __shfl_xor(ss, off));
+        if (lane == 0) s_inv[k] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss, (float)a.H), a.eps)));
     }
     __syncthreads();
-    float inv[MOE_MAX_TOPK];
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK; ++k) {
-        inv[k] = 0.0f;
-        if (k < a.K) {
-            float s = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kFinThreads / 64; ++w) s = __fadd_rn(s, red[w][k]);
-            inv[k] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(s, (float)a.H), a.eps)));
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < kFinMaxChunks; ++j) {
-        const int c = tid + j * kFinThreads;
-        if (c >= nchunks) continue;
+    // pass 2: weighted sum over routes
+    for (int c = tid; c < nchunks; c += kFinThreads) {
+        float g[8];
+        gamma8(a, c, g);
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int k = 0; k < a.K; ++k) {
-            if (perm[k] < 0) continue;          // a zero row normalizes to zero
-            const float wk = a.weights[(int64_t)t * a.K + k];
+            const int p = s_perm[k];
+            if (p < 0) continue;            // a zero row normalizes to zero
+            const float wk = s_w[k], inv = s_inv[k];
             float v[8];
-            load_row8(a, perm[k], c, v);
+            load_row8(a, p, c, v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float y = a.weight_before_norm
-                                    ? __fmul_rn(__fmul_rn(gamma[j][i], v[i]), inv[k])
-                                    : __fmul_rn(gamma[j][i], __fmul_rn(v[i], inv[k]));
+                const float y = a.weight_before_norm ? __fmul_rn(__fmul_rn(g[i], v[i]), inv)
+                                                     : __fmul_rn(g[i], __fmul_rn(v[i], inv));
                 acc[i] = __fadd_rn(acc[i], __fmul_rn(y, wk));
             }
         }

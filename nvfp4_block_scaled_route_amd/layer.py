@@ -79,12 +79,14 @@ class Buffers:
         u8, i32, i16 = torch.uint8, torch.int32, torch.int16
         self.a_codes = torch.empty((s.T, s.H // 2), dtype=u8, device=device)
         self.a_sf = torch.empty((s.T, s.H // 16), dtype=u8, device=device)
+        self.a_dq = torch.empty((s.T, s.H), dtype=i16, device=device)
         self.ids = torch.empty((s.T, s.K), dtype=i32, device=device)
         self.weights = torch.empty((s.T, s.K), dtype=torch.float32, device=device)
         self.meta = torch.full((L.total_ints,), -1, dtype=i32, device=device)
         I_slice = s.I // s.tp
         self.inter_codes = torch.empty((max(L.rows_max, 1), I_slice // 2), dtype=u8, device=device)
         self.inter_sf = torch.empty((max(L.rows_max, 1), I_slice // 16), dtype=u8, device=device)
+        self.inter_dq = torch.empty((max(L.rows_max, 1), I_slice), dtype=i16, device=device)
         self.rows = torch.empty((s.tp, max(L.rows_max, 1), s.H), dtype=i16, device=device)
         self.out = torch.empty((s.T, s.H), dtype=i16, device=device)
 
@@ -108,11 +110,11 @@ def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, we
     s = bufs.shape
     N.moe_route(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
                 bufs.ids, bufs.weights, bufs.meta, stream)
-    N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, stream)
+    N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, bufs.a_dq, stream)
     parts = slices if slices is not None else [weights]
     I_part = s.I // len(parts)
     for r, w in enumerate(parts):
-        N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, w, s.T, s.K, s.E, s.H, I_part,
-                          s.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
+        N.moe_experts_fwd(bufs.a_dq, bufs.meta, w, s.T, s.K, s.E, s.H, I_part, s.tile_m,
+                          bufs.inter_codes, bufs.inter_sf, bufs.inter_dq, bufs.rows[r], stream)
     N.moe_finalize(bufs.rows, len(parts), bufs.rows.stride(0), bufs.exp2perm, bufs.weights,
                    norm_weight, gain_center, eps, weight_before_norm, s.T, s.K, s.H, bufs.out, stream)

@@ -18,8 +18,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 
 # Every symbol include/moe_nvfp4.h declares.
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout_get",
-           "moe_route", "nvfp4_quant", "moe_pack_w13", "moe_pack_w2", "moe_experts_fwd",
-           "moe_finalize")
+           "moe_route", "nvfp4_quant", "moe_pack_w13", "moe_pack_w2",
+           "moe_experts_fwd", "moe_finalize")
 
 
 class MoeMetaLayout(ctypes.Structure):
@@ -61,11 +61,11 @@ def lib() -> ctypes.CDLL:
         "moe_rows_max": (i64, [i32, i32, i32, i32]),
         "moe_meta_layout_get": (i32, [i32, i32, i32, i32, ctypes.POINTER(MoeMetaLayout)]),
         "moe_route": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp]),
-        "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp]),
+        "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp, vp]),
         "moe_pack_w13": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
         "moe_pack_w2": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
-        "moe_experts_fwd": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
-                                  i32, i32, i32, vp, vp, vp, i64, vp]),
+        "moe_experts_fwd": (i32, [vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
+                                  i32, i32, i32, vp, vp, vp, vp, i64, vp]),
         "moe_finalize": (i32, [vp, i64, i32, i64, vp, vp, vp, f32, f32, i32, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -119,10 +119,10 @@ def moe_route(logits, expert_bias, is_padding, K, route_scale, tile_m, local_exp
                            _stream(stream)), "moe_route")
 
 
-def nvfp4_quant(x, gscale, codes, sf, stream=None) -> None:
+def nvfp4_quant(x, gscale, codes, sf, dq, stream=None) -> None:
     T, H = x.shape
     _check(lib().nvfp4_quant(_ptr(x), x.stride(0), _ptr(gscale), T, H, _ptr(codes), _ptr(sf),
-                             _stream(stream)), "nvfp4_quant")
+                             _ptr(dq), _stream(stream)), "nvfp4_quant")
 
 
 def moe_pack_w13(codes, sf, E, I, H, out_codes, out_sf, stream=None) -> None:
@@ -168,11 +168,11 @@ class Weights:
             _ptr(self.g1_alphas), _ptr(self.g1_scale_c), _ptr(self.g2_alphas))
 
 
-def moe_experts_fwd(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, tile_m,
-                    inter_codes, inter_sf, rows, stream=None) -> None:
+def moe_experts_fwd(a_dq, meta, weights: Weights, T, K, E_local, H, I, tile_m,
+                    inter_codes, inter_sf, inter_dq, rows, stream=None) -> None:
     ws = weights.struct()
-    _check(lib().moe_experts_fwd(_ptr(a_codes), _ptr(a_sf), _ptr(meta), ctypes.byref(ws), T, K,
-                                 E_local, H, I, tile_m, _ptr(inter_codes), _ptr(inter_sf),
+    _check(lib().moe_experts_fwd(_ptr(a_dq), _ptr(meta), ctypes.byref(ws), T, K, E_local, H, I,
+                                 tile_m, _ptr(inter_codes), _ptr(inter_sf), _ptr(inter_dq),
                                  _ptr(rows), rows.stride(0), _stream(stream)), "moe_experts_fwd")
 
 
