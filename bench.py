@@ -9,9 +9,9 @@ configuration asks for). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. ``roofline`` is the dominant kernel (the experts step)
 against HBM bandwidth: algorithmic bytes per launch (codes + e4m3 scales of the
-experts that have a route, the gathered input rows, the intermediate written and
-re-read, the GEMM2 rows written) over its average duration measured with HIP
-events on its own stream. ``cpu_baseline`` is the CPU oracle timed on a bounded
+experts that have a route, the NVFP4 input read once, the NVFP4 intermediate
+written and re-read, the GEMM2 rows written) over its average duration measured
+with HIP events on its own stream. ``cpu_baseline`` is the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload decode_b8]
@@ -48,8 +48,8 @@ def algorithmic_bytes(wl, counts) -> dict:
     H, I = wl.H, wl.I
     per_expert = 2 * I * H // 2 + 2 * I * H // 16 + H * I // 2 + H * I // 16   # 27/16 I H
     routes = int(counts.sum())
-    act = wl.T * H * 2                                     # f16 input expansion, read once
-    inter = routes * (I // 2 + I // 16 + 2 * I * 2)        # NVFP4 intermediate written, f16 form written + read
+    act = wl.T * (H // 2 + H // 16)                        # NVFP4 input, read once
+    inter = 2 * routes * (I // 2 + I // 16)                # NVFP4 intermediate, written and read
     rows = routes * H * 2                                  # GEMM2 bf16 rows written
     return dict(weights=touched * per_expert, touched=touched, other=act + inter + rows,
                 total=touched * per_expert + act + inter + rows)
@@ -149,8 +149,8 @@ def main():
         torch.cuda._sleep(20000)
         ev[i][0].record(s)
         for r, ww in enumerate(sl):
-            N.moe_experts_fwd(bufs.a_dq, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H, I_part, wl.tile_m,
-                              bufs.inter_codes, bufs.inter_sf, bufs.inter_dq, bufs.rows[r], s)
+            N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H,
+                              I_part, wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], s)
         ev[i][1].record(s)
     torch.cuda.synchronize()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 1
+#define MOE_NVFP4_ABI_VERSION 2
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -52,7 +52,7 @@ extern "C" {
 /* Limits of this build. */
 #define MOE_MAX_EXPERTS 1024  /* E and E_local */
 #define MOE_MAX_TOPK 32
-#define MOE_MAX_HIDDEN 16384  /* H in moe_finalize */
+#define MOE_MAX_HIDDEN 16384  /* H, and I in moe_experts_fwd */
 
 int moe_abi_version(void);
 const char* moe_last_error(void);
@@ -133,13 +133,10 @@ int moe_route(const float* logits, int64_t logits_row_stride, const float* exper
  *   x       device bf16 [T, H], row stride x_row_stride elements (>= H)
  *   gscale  device fp32 [1]: the input global scale (a1_gscale = 1 / a13)
  *   codes   device uint8 [T, H/2] out;  sf device uint8 [T, H/16] out
- *   dq      device f16 [T, H] out: the exact f16 expansion of the result,
- *           e2m1(code_i) * e4m3(sf) per element (in the globally scaled domain;
- *           every such product is an f16 value). It is the form moe_experts_fwd
- *           consumes: the MFMA operand, decoded once here.
+ * These two arrays are moe_experts_fwd's activation input as they are.
  * H % 16 == 0. */
 int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
-                uint8_t* codes, uint8_t* sf, uint16_t* dq, void* stream);
+                uint8_t* codes, uint8_t* sf, void* stream);
 
 /* ------------------------------------------------------------------ weights
  * The converted weight layout the expert kernels read. The property the pages
@@ -147,19 +144,23 @@ int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, in
  * expert-TP slice of the converted weights -- intermediate columns
  * [r I', (r+1) I') -- is, byte for byte, the converted layout of the slice, so
  * slices are views. This library's layout has it for I' % 64 == 0:
- *   An NVFP4 matrix of N rows and K columns (N % 16 == 0, K % 64 == 0) is stored
- *   per expert as [N/16 row groups][K/64 k-tiles] tiles; a tile holds 16 rows x
- *   64 columns as 512 code bytes (array *_codes) and 64 scale bytes (array *_sf).
- *   In a tile, element (n, k) is nibble (j & 1) of code byte
- *   ((q*16 + n)*2 + s)*4 + j/2 with s = k/32, q = (k%32)/8, j = k%8, and the
- *   scale of block b = k/16 of row n is scale byte ((b%2)*16 + n)*2 + b/2.
- *   (One lane of a 64-wide wave reads 8 contiguous code bytes and 2 scale bytes
- *   of a tile: its operand for two 16x16x32 MFMA steps.)
+ *   An NVFP4 matrix of N rows and K columns (N % 32 == 0, K % 64 == 0) is stored
+ *   per expert as [N/32 row pairs][K/64 k-tiles]; a row pair is two groups of 16
+ *   rows (half h = 0, 1), and a k-tile of a pair holds its 32 rows x 64 columns
+ *   as 1024 code bytes (array *_codes) and 128 scale bytes (array *_sf). The
+ *   tile has 64 slots s = q*16 + n, one per 16-column block q of row n, holding
+ *   that block of both halves: element k (k < 64, i = k % 16, q = k / 16) of row
+ *   n of half h is nibble (i & 1) of code byte (s*2 + h)*8 + i/2, and the block's
+ *   scale is scale byte s*2 + h.
+ *   (Lane s of a 64-wide wave reads one 16-byte slot and its 2 scale bytes: a
+ *   whole 16-element block of both halves, its operands for two 16x16x32 MFMA
+ *   steps with the lane's K indices 16q + 8j + [0, 8), j = 0, 1.)
  *   w13 [E, 2I, H] (N = 2I, K = H): converted row 32c + w is gate row 16c + w for
- *   w < 16 and up row I + 16c + (w - 16) otherwise (the gated interleave), so
- *   slice r is converted row groups [2rI'/16, 2(r+1)I'/16).
- *   w2 [E, H, I] (N = H, K = I): slice r is k-tiles [rI'/64, (r+1)I'/64) of every
- *   row group.
+ *   w < 16 and up row I + 16c + (w - 16) otherwise (the gated interleave): pair c
+ *   is the gate (half 0) and up (half 1) rows of intermediates [16c, 16c + 16),
+ *   so slice r is pairs [rI'/16, (r+1)I'/16).
+ *   w2 [E, H, I] (N = H, K = I): pair c is output columns [32c, 32c + 32); slice
+ *   r is k-tiles [rI'/64, (r+1)I'/64) of every pair.
  * moe_pack_w13 / moe_pack_w2 convert from the logical layout (the expert_tp
  * page, "StockNvfp4": codes [E, N, K/2], scales [E, N, K/16], row-major; w13
  * rows [0, I) gate = w1, [I, 2I) up = w3) into this one. Device buffers, no
@@ -172,10 +173,10 @@ int moe_pack_w2(const uint8_t* codes, const uint8_t* sf, int E, int H, int I, ui
 /* Converted experts as the expert kernels take them: base pointers and byte
  * strides, so that an expert-TP slice is passed as a view with no copy
  * (the expert_tp page, "TpExperts", "slice_views").
- *   w13, w13_sf: expert e, row group g at base + e*expert_stride + g*group_stride
- *                (k-tiles of a row group contiguous: 512 / 64 bytes each)
+ *   w13, w13_sf: expert e, row pair c at base + e*expert_stride + c*pair_stride
+ *                (k-tiles of a pair contiguous: 1024 / 128 bytes each)
  *   w2, w2_sf:   likewise; for slice r of tp of a full-width w2 the base moves
- *                by r*(I'/64) tiles and group_stride stays the full width's
+ *                by r*(I'/64) k-tiles and pair_stride stays the full width's
  *   g1_alphas, g1_scale_c, g2_alphas: device fp32 [E_local], the folded scalars
  *     (the runner page, "process_weights_after_loading": g1_alphas = a13*w1_gs,
  *     g1_scale_c = a13*w3_gs/a2, g2_alphas = a2*w2_gs; the expert_tp page: they
@@ -186,13 +187,13 @@ typedef struct moe_nvfp4_weights {
     const uint8_t* w2;
     const uint8_t* w2_sf;
     int64_t w13_expert_stride_bytes;
-    int64_t w13_group_stride_bytes;
+    int64_t w13_pair_stride_bytes;
     int64_t w13_sf_expert_stride_bytes;
-    int64_t w13_sf_group_stride_bytes;
+    int64_t w13_sf_pair_stride_bytes;
     int64_t w2_expert_stride_bytes;
-    int64_t w2_group_stride_bytes;
+    int64_t w2_pair_stride_bytes;
     int64_t w2_sf_expert_stride_bytes;
-    int64_t w2_sf_group_stride_bytes;
+    int64_t w2_sf_pair_stride_bytes;
     const float* g1_alphas;
     const float* g1_scale_c;
     const float* g2_alphas;
@@ -209,22 +210,21 @@ typedef struct moe_nvfp4_weights {
  *   acc2[n]  = sum_i dq(h[i]) * dq(w2[e, n, i])           n < H
  *   rows[p, n] = bf16(acc2[n] * g2_alphas[e])             nearest even
  * dq(.) = e2m1 code * e4m3 scale of its block; every such value is exact in
- * the f16 MFMA operands. Padding rows are not written.
- *   a_dq           device f16 [T, H]: the NVFP4 input as nvfp4_quant's dq output
- *                  (exact f16 expansion of its codes and scales)
+ * f16, the MFMA operand type, and the accumulation is fp32. Padding rows are
+ * not written.
+ *   a_codes, a_sf  device [T, H/2], [T, H/16]: the NVFP4 input, row-major, as
+ *                  nvfp4_quant writes it
  *   meta           moe_route's metadata for the same T, K, E_local, tile_m
  *   w              converted experts (host struct; pointers in it are device)
  *   inter_codes, inter_sf  device [rows_max, I/2], [rows_max, I/16] out: the
- *                  requantized intermediate
- *   inter_dq       device f16 [rows_max, I] out: its exact f16 expansion, which
- *                  GEMM2 reads
+ *                  requantized intermediate, row-major (GEMM2's input)
  *   rows           device bf16 [rows_max, rows_stride] out, rows_stride >= H
  * Two launches on `stream` (GEMM1 with the SwiGLU/requant epilogue, then GEMM2).
- * H % 64 == 0, I % 64 == 0, H <= 8192, I <= 4096, tile_m % 16 == 0. */
-int moe_experts_fwd(const uint16_t* a_dq, const int32_t* meta, const moe_nvfp4_weights* w,
-                    int T, int K, int E_local, int H, int I, int tile_m, uint8_t* inter_codes,
-                    uint8_t* inter_sf, uint16_t* inter_dq, uint16_t* rows, int64_t rows_stride,
-                    void* stream);
+ * H % 64 == 0, I % 64 == 0, H and I <= MOE_MAX_HIDDEN, tile_m % 16 == 0. */
+int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const int32_t* meta,
+                    const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                    int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
+                    int64_t rows_stride, void* stream);
 
 /* ------------------------------------------------------------------ finalize
  * Post-expert finalize (the runner page, "MusePostExpertFinalize",

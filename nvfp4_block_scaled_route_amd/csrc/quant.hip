@@ -1,9 +1,6 @@
 // nvfp4_quant: NVFP4 quantization of the expert input (one global scale,
 // row-major e4m3 block scales) -- the model page, "_prepared_nvfp4_forward".
-// Besides the codes and scales it writes the exact f16 expansion of the result,
-// e2m1(code) * e4m3(scale) per element, which is the GEMM's MFMA operand (so the
-// experts never decode the activation again).
-// HBM-bound: one thread owns one 16-value block (32 bytes in, 8 + 1 + 32 out).
+// HBM-bound: one thread owns one 16-value block (32 bytes in, 8 + 1 out).
 #include "common.hpp"
 
 namespace moe {
@@ -12,8 +9,7 @@ __global__ void __launch_bounds__(256) nvfp4_quant_kernel(const uint16_t* __rest
                                                           int64_t x_row_stride,
                                                           const float* __restrict__ gscale_p,
                                                           int T, int H, uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ sf,
-                                                          uint16_t* __restrict__ dq) {
+                                                          uint8_t* __restrict__ sf) {
     const int blocks_per_row = H >> 4;
     const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blk >= (int64_t)T * blocks_per_row) return;
@@ -38,23 +34,18 @@ __global__ void __launch_bounds__(256) nvfp4_quant_kernel(const uint16_t* __rest
     for (int i = 0; i < 8; ++i) hi |= nvfp4_code(v[8 + i], bs) << (4 * i);
     *reinterpret_cast<uint2*>(codes + (int64_t)t * (H >> 1) + b * 8) = make_uint2(lo, hi);
     sf[(int64_t)t * blocks_per_row + b] = (uint8_t)bs.byte;
-    const half2v d = splat_lo(e4m3x2_to_f16(bs.byte));
-    const half8 v0 = nvfp4x8_to_f16(lo, d), v1 = nvfp4x8_to_f16(hi, d);
-    uint4* out = reinterpret_cast<uint4*>(dq + (int64_t)t * H + b * 16);
-    out[0] = *reinterpret_cast<const uint4*>(&v0);
-    out[1] = *reinterpret_cast<const uint4*>(&v1);
 }
 
 }  // namespace moe
 
 extern "C" int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T,
-                           int H, uint8_t* codes, uint8_t* sf, uint16_t* dq, void* stream) {
+                           int H, uint8_t* codes, uint8_t* sf, void* stream) {
     using namespace moe;
     if (T < 0 || H < 0) return fail(MOE_EINVAL, "nvfp4_quant: negative size T=%d H=%d", T, H);
     if (H % 16) return fail(MOE_EUNSUPPORTED, "nvfp4_quant: H=%d is not a multiple of 16", H);
     if (T == 0 || H == 0) return MOE_OK;
-    if (!x || !gscale || !codes || !sf || !dq) return fail(MOE_EINVAL, "nvfp4_quant: NULL pointer");
-    if (!aligned16(x) || !aligned16(codes) || !aligned16(sf) || !aligned16(gscale) || !aligned16(dq))
+    if (!x || !gscale || !codes || !sf) return fail(MOE_EINVAL, "nvfp4_quant: NULL pointer");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(sf) || !aligned16(gscale))
         return fail(MOE_EINVAL, "nvfp4_quant: pointers must be 16-byte aligned");
     if (x_row_stride < H || x_row_stride % 8)
         return fail(MOE_EINVAL, "nvfp4_quant: row stride %lld must be >= H and a multiple of 8",
@@ -63,6 +54,6 @@ extern "C" int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float*
     const int64_t grid = (blocks + 255) / 256;
     if (grid > 0x7FFFFFFF) return fail(MOE_EUNSUPPORTED, "nvfp4_quant: too large");
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, x,
-                       x_row_stride, gscale, T, H, codes, sf, dq);
+                       x_row_stride, gscale, T, H, codes, sf);
     return check_launch("nvfp4_quant");
 }

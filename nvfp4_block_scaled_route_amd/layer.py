@@ -31,31 +31,31 @@ def pack_weights(w13_codes, w13_sf, w2_codes, w2_sf, g1_alphas, g1_scale_c, g2_a
     N.moe_pack_w2(w2_codes, w2_sf, E, H, I, c2, s2, stream)
     return N.Weights(
         w13=c13, w13_sf=s13, w2=c2, w2_sf=s2,
-        w13_expert_stride=2 * I * H // 2, w13_group_stride=(H // 64) * 512,
-        w13_sf_expert_stride=2 * I * H // 16, w13_sf_group_stride=(H // 64) * 64,
-        w2_expert_stride=H * I // 2, w2_group_stride=(I // 64) * 512,
-        w2_sf_expert_stride=H * I // 16, w2_sf_group_stride=(I // 64) * 64,
+        w13_expert_stride=2 * I * H // 2, w13_pair_stride=(H // 64) * 1024,
+        w13_sf_expert_stride=2 * I * H // 16, w13_sf_pair_stride=(H // 64) * 128,
+        w2_expert_stride=H * I // 2, w2_pair_stride=(I // 64) * 1024,
+        w2_sf_expert_stride=H * I // 16, w2_sf_pair_stride=(I // 64) * 128,
         g1_alphas=g1_alphas, g1_scale_c=g1_scale_c, g2_alphas=g2_alphas)
 
 
 def slice_weights(full: N.Weights, r: int, tp: int, H: int, I: int) -> N.Weights:
-    """Expert-TP slice r of tp as byte views (no copy): w13 row groups
-    [2rI'/16, 2(r+1)I'/16), w2 k-tiles [rI'/64, (r+1)I'/64) of every row group."""
+    """Expert-TP slice r of tp as byte views (no copy): w13 row pairs
+    [rI'/16, (r+1)I'/16), w2 k-tiles [rI'/64, (r+1)I'/64) of every row pair."""
     s = I // tp
     if s % 64:
         raise ValueError(f"slice width {s} is not a multiple of 64")
-    g13 = 2 * s // 16 * r
+    p13 = s // 16 * r
     t2 = s // 64 * r
     return N.Weights(
         w13=full.w13, w13_sf=full.w13_sf, w2=full.w2, w2_sf=full.w2_sf,
-        w13_expert_stride=full.w13_expert_stride, w13_group_stride=full.w13_group_stride,
-        w13_sf_expert_stride=full.w13_sf_expert_stride, w13_sf_group_stride=full.w13_sf_group_stride,
-        w2_expert_stride=full.w2_expert_stride, w2_group_stride=full.w2_group_stride,
-        w2_sf_expert_stride=full.w2_sf_expert_stride, w2_sf_group_stride=full.w2_sf_group_stride,
+        w13_expert_stride=full.w13_expert_stride, w13_pair_stride=full.w13_pair_stride,
+        w13_sf_expert_stride=full.w13_sf_expert_stride, w13_sf_pair_stride=full.w13_sf_pair_stride,
+        w2_expert_stride=full.w2_expert_stride, w2_pair_stride=full.w2_pair_stride,
+        w2_sf_expert_stride=full.w2_sf_expert_stride, w2_sf_pair_stride=full.w2_sf_pair_stride,
         g1_alphas=full.g1_alphas, g1_scale_c=full.g1_scale_c, g2_alphas=full.g2_alphas,
-        w13_offset=full.w13_offset + g13 * full.w13_group_stride,
-        w13_sf_offset=full.w13_sf_offset + g13 * full.w13_sf_group_stride,
-        w2_offset=full.w2_offset + t2 * 512, w2_sf_offset=full.w2_sf_offset + t2 * 64)
+        w13_offset=full.w13_offset + p13 * full.w13_pair_stride,
+        w13_sf_offset=full.w13_sf_offset + p13 * full.w13_sf_pair_stride,
+        w2_offset=full.w2_offset + t2 * 1024, w2_sf_offset=full.w2_sf_offset + t2 * 128)
 
 
 @dataclass
@@ -79,14 +79,12 @@ class Buffers:
         u8, i32, i16 = torch.uint8, torch.int32, torch.int16
         self.a_codes = torch.empty((s.T, s.H // 2), dtype=u8, device=device)
         self.a_sf = torch.empty((s.T, s.H // 16), dtype=u8, device=device)
-        self.a_dq = torch.empty((s.T, s.H), dtype=i16, device=device)
         self.ids = torch.empty((s.T, s.K), dtype=i32, device=device)
         self.weights = torch.empty((s.T, s.K), dtype=torch.float32, device=device)
         self.meta = torch.full((L.total_ints,), -1, dtype=i32, device=device)
         I_slice = s.I // s.tp
         self.inter_codes = torch.empty((max(L.rows_max, 1), I_slice // 2), dtype=u8, device=device)
         self.inter_sf = torch.empty((max(L.rows_max, 1), I_slice // 16), dtype=u8, device=device)
-        self.inter_dq = torch.empty((max(L.rows_max, 1), I_slice), dtype=i16, device=device)
         self.rows = torch.empty((s.tp, max(L.rows_max, 1), s.H), dtype=i16, device=device)
         self.out = torch.empty((s.T, s.H), dtype=i16, device=device)
 
@@ -110,11 +108,11 @@ def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, we
     s = bufs.shape
     N.moe_route(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
                 bufs.ids, bufs.weights, bufs.meta, stream)
-    N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, bufs.a_dq, stream)
+    N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, stream)
     parts = slices if slices is not None else [weights]
     I_part = s.I // len(parts)
     for r, w in enumerate(parts):
-        N.moe_experts_fwd(bufs.a_dq, bufs.meta, w, s.T, s.K, s.E, s.H, I_part, s.tile_m,
-                          bufs.inter_codes, bufs.inter_sf, bufs.inter_dq, bufs.rows[r], stream)
+        N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, w, s.T, s.K, s.E, s.H, I_part,
+                          s.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
     N.moe_finalize(bufs.rows, len(parts), bufs.rows.stride(0), bufs.exp2perm, bufs.weights,
                    norm_weight, gain_center, eps, weight_before_norm, s.T, s.K, s.H, bufs.out, stream)

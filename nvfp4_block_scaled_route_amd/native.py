@@ -32,10 +32,10 @@ class MoeNvfp4Weights(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_sf", ctypes.c_void_p),
                 ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p)] + \
                [(n, ctypes.c_int64) for n in (
-                   "w13_expert_stride_bytes", "w13_group_stride_bytes",
-                   "w13_sf_expert_stride_bytes", "w13_sf_group_stride_bytes",
-                   "w2_expert_stride_bytes", "w2_group_stride_bytes",
-                   "w2_sf_expert_stride_bytes", "w2_sf_group_stride_bytes")] + \
+                   "w13_expert_stride_bytes", "w13_pair_stride_bytes",
+                   "w13_sf_expert_stride_bytes", "w13_sf_pair_stride_bytes",
+                   "w2_expert_stride_bytes", "w2_pair_stride_bytes",
+                   "w2_sf_expert_stride_bytes", "w2_sf_pair_stride_bytes")] + \
                [("g1_alphas", ctypes.c_void_p), ("g1_scale_c", ctypes.c_void_p),
                 ("g2_alphas", ctypes.c_void_p)]
 
@@ -61,11 +61,11 @@ def lib() -> ctypes.CDLL:
         "moe_rows_max": (i64, [i32, i32, i32, i32]),
         "moe_meta_layout_get": (i32, [i32, i32, i32, i32, ctypes.POINTER(MoeMetaLayout)]),
         "moe_route": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp]),
-        "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp, vp]),
+        "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp]),
         "moe_pack_w13": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
         "moe_pack_w2": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
-        "moe_experts_fwd": (i32, [vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
-                                  i32, i32, i32, vp, vp, vp, vp, i64, vp]),
+        "moe_experts_fwd": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
+                                  i32, i32, i32, vp, vp, vp, i64, vp]),
         "moe_finalize": (i32, [vp, i64, i32, i64, vp, vp, vp, f32, f32, i32, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -119,10 +119,10 @@ def moe_route(logits, expert_bias, is_padding, K, route_scale, tile_m, local_exp
                            _stream(stream)), "moe_route")
 
 
-def nvfp4_quant(x, gscale, codes, sf, dq, stream=None) -> None:
+def nvfp4_quant(x, gscale, codes, sf, stream=None) -> None:
     T, H = x.shape
     _check(lib().nvfp4_quant(_ptr(x), x.stride(0), _ptr(gscale), T, H, _ptr(codes), _ptr(sf),
-                             _ptr(dq), _stream(stream)), "nvfp4_quant")
+                             _stream(stream)), "nvfp4_quant")
 
 
 def moe_pack_w13(codes, sf, E, I, H, out_codes, out_sf, stream=None) -> None:
@@ -143,13 +143,13 @@ class Weights:
     w2: torch.Tensor
     w2_sf: torch.Tensor
     w13_expert_stride: int
-    w13_group_stride: int
+    w13_pair_stride: int
     w13_sf_expert_stride: int
-    w13_sf_group_stride: int
+    w13_sf_pair_stride: int
     w2_expert_stride: int
-    w2_group_stride: int
+    w2_pair_stride: int
     w2_sf_expert_stride: int
-    w2_sf_group_stride: int
+    w2_sf_pair_stride: int
     g1_alphas: torch.Tensor
     g1_scale_c: torch.Tensor
     g2_alphas: torch.Tensor
@@ -162,17 +162,17 @@ class Weights:
         return MoeNvfp4Weights(
             _ptr(self.w13) + self.w13_offset, _ptr(self.w13_sf) + self.w13_sf_offset,
             _ptr(self.w2) + self.w2_offset, _ptr(self.w2_sf) + self.w2_sf_offset,
-            self.w13_expert_stride, self.w13_group_stride, self.w13_sf_expert_stride,
-            self.w13_sf_group_stride, self.w2_expert_stride, self.w2_group_stride,
-            self.w2_sf_expert_stride, self.w2_sf_group_stride,
+            self.w13_expert_stride, self.w13_pair_stride, self.w13_sf_expert_stride,
+            self.w13_sf_pair_stride, self.w2_expert_stride, self.w2_pair_stride,
+            self.w2_sf_expert_stride, self.w2_sf_pair_stride,
             _ptr(self.g1_alphas), _ptr(self.g1_scale_c), _ptr(self.g2_alphas))
 
 
-def moe_experts_fwd(a_dq, meta, weights: Weights, T, K, E_local, H, I, tile_m,
-                    inter_codes, inter_sf, inter_dq, rows, stream=None) -> None:
+def moe_experts_fwd(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, tile_m,
+                    inter_codes, inter_sf, rows, stream=None) -> None:
     ws = weights.struct()
-    _check(lib().moe_experts_fwd(_ptr(a_dq), _ptr(meta), ctypes.byref(ws), T, K, E_local, H, I,
-                                 tile_m, _ptr(inter_codes), _ptr(inter_sf), _ptr(inter_dq),
+    _check(lib().moe_experts_fwd(_ptr(a_codes), _ptr(a_sf), _ptr(meta), ctypes.byref(ws), T, K,
+                                 E_local, H, I, tile_m, _ptr(inter_codes), _ptr(inter_sf),
                                  _ptr(rows), rows.stride(0), _stream(stream)), "moe_experts_fwd")
 
 

@@ -13,15 +13,19 @@ this project's own, chosen for the MI355X kernels, and keeps that property
 whenever I' % 64 == 0.
 
 Layout, per expert, of an NVFP4 matrix with N rows and K columns
-(N % 16 == 0, K % 64 == 0):
-  * codes: [N/16 row groups][K/64 k-tiles][512 bytes]. Element (n, k) of a tile
-    (n < 16, k < 64) is nibble (j & 1) of byte ((q * 16 + n) * 2 + s) * 4 + j / 2
-    with s = k / 32, q = (k % 32) / 8, j = k % 8 (low nibble for even j);
-  * scales: [N/16][K/64][64 bytes]. Block b = k / 16 of row n is byte
-    ((b % 2) * 16 + n) * 2 + b / 2;
+(N % 32 == 0, K % 64 == 0). Rows come in pairs of 16-row groups (32 rows);
+row rho of a pair is row n = rho % 16 of half h = rho // 16. Per pair, the
+K/64 k-tiles follow each other; a k-tile holds 64 slots s = q * 16 + n, one
+per (16-column block q = k // 16 of the tile, row n), and each slot holds that
+block for both halves:
+  * codes: [N/32 pairs][K/64 k-tiles][1024 bytes]. Element (rho, k) of a tile
+    (k < 64, i = k % 16) is nibble (i & 1) of byte (s * 2 + h) * 8 + i // 2
+    (low nibble for even i);
+  * scales: [N/32][K/64][128 bytes]. The scale of block q of row rho is byte
+    s * 2 + h;
   * w13 only: converted row 32c + w is logical row 16c + w for w < 16 (gate)
-    and I + 16c + (w - 16) for w >= 16 (up), so every 32 rows hold the gate
-    and up rows of the same 16 intermediates.
+    and I + 16c + (w - 16) for w >= 16 (up), so pair c holds the gate rows
+    (half 0) and the up rows (half 1) of intermediates [16c, 16c + 16).
 """
 from __future__ import annotations
 
@@ -29,8 +33,9 @@ import numpy as np
 
 from .formats import pack_nibbles, unpack_nibbles
 
-ROWS = 16        # rows per row group
+ROWS = 16        # rows per group; two groups per pair
 KTILE = 64       # elements per k-tile
+BLOCK = 16       # elements per scale block
 
 
 def interleave_gate_up(rows: np.ndarray) -> np.ndarray:
@@ -43,22 +48,22 @@ def interleave_gate_up(rows: np.ndarray) -> np.ndarray:
 
 
 def convert_codes(codes: np.ndarray) -> np.ndarray:
-    """[E, N, K/2] bytes -> [E, N/16, K/64, 512] bytes."""
+    """[E, N, K/2] bytes -> [E, N/32, K/64, 1024] bytes."""
     E, N, half = codes.shape
     K = half * 2
-    nib = unpack_nibbles(codes).reshape(E, N // ROWS, ROWS, K // KTILE, 2, 4, 8)
-    #                                   e  g         n     t           s  q  j
-    t = nib.transpose(0, 1, 3, 5, 2, 4, 6).reshape(E, N // ROWS, K // KTILE, 1024)
+    nib = unpack_nibbles(codes).reshape(E, N // 32, 2, ROWS, K // KTILE, 4, BLOCK)
+    #                                   e  p        h  n     c           q  i
+    t = nib.transpose(0, 1, 4, 5, 3, 2, 6).reshape(E, N // 32, K // KTILE, 2048)
     return pack_nibbles(t)
 
 
 def convert_scales(sf: np.ndarray) -> np.ndarray:
-    """[E, N, K/16] bytes -> [E, N/16, K/64, 64] bytes."""
+    """[E, N, K/16] bytes -> [E, N/32, K/64, 128] bytes."""
     E, N, nb = sf.shape
-    K = nb * 16
-    s = sf.reshape(E, N // ROWS, ROWS, K // KTILE, 2, 2)
-    #                e  g         n     t          b/2 b%2
-    return np.ascontiguousarray(s.transpose(0, 1, 3, 5, 2, 4)).reshape(E, N // ROWS, K // KTILE, 64)
+    K = nb * BLOCK
+    s = sf.reshape(E, N // 32, 2, ROWS, K // KTILE, 4)
+    #                e  p        h  n     c           q
+    return np.ascontiguousarray(s.transpose(0, 1, 4, 5, 3, 2)).reshape(E, N // 32, K // KTILE, 128)
 
 
 def convert_w13(codes, sf):
@@ -86,12 +91,12 @@ def logical_slice_w2(codes, sf, r: int, tp: int):
 
 
 def view_slice_w13(conv: np.ndarray, r: int, tp: int) -> np.ndarray:
-    """Byte view of slice r of converted w13 codes or scales [E, 2I/16, H/64, b]."""
-    g = conv.shape[1] // tp
-    return conv[:, r * g:(r + 1) * g]
+    """Byte view of slice r of converted w13 codes or scales [E, 2I/32, H/64, b]."""
+    p = conv.shape[1] // tp
+    return conv[:, r * p:(r + 1) * p]
 
 
 def view_slice_w2(conv: np.ndarray, r: int, tp: int) -> np.ndarray:
-    """Byte view of slice r of converted w2 codes or scales [E, H/16, I/64, b]."""
+    """Byte view of slice r of converted w2 codes or scales [E, H/32, I/64, b]."""
     t = conv.shape[2] // tp
     return conv[:, :, r * t:(r + 1) * t]

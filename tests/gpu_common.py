@@ -62,7 +62,7 @@ def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | Non
     L = bufs.layout
     meta = host(bufs.meta)
     res = dict(
-        a_codes=host(bufs.a_codes), a_sf=host(bufs.a_sf), a_dq=host(bufs.a_dq), ids=host(bufs.ids),
+        a_codes=host(bufs.a_codes), a_sf=host(bufs.a_sf), ids=host(bufs.ids),
         weights=host(bufs.weights), meta=meta, layout=L,
         num_tiles=int(meta[L.num_tiles]), total_rows=int(meta[L.total_rows]),
         offsets=meta[L.expert_offsets:L.expert_offsets + wl.E + 1],
@@ -71,6 +71,5 @@ def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | Non
         perm2tok=meta[L.perm2tok:L.perm2tok + L.rows_max],
         tile_expert=meta[L.tile_expert:L.tile_expert + L.tiles_max],
         inter_codes=host(bufs.inter_codes), inter_sf=host(bufs.inter_sf),
-        inter_dq=host(bufs.inter_dq),
         rows=host(bufs.rows), out=host(bufs.out))
     return res

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
@@ -59,10 +59,11 @@ def test_invalid_sizes_are_refused():
         (L.moe_route, (None, 8, None, None, 4, 2000, 2, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_route, (None, 8, None, None, 4, 8, 2, f(1.0), 8, 0, 8, None, None, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_route, (None, 4, None, None, 4, 8, 2, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EINVAL),  # stride < E
-        (L.nvfp4_quant, (None, 24, None, 4, 24, None, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
-        (L.nvfp4_quant, (None, 32, None, 4, 32, None, None, None, None), N.MOE_EINVAL),         # NULL
+        (L.nvfp4_quant, (None, 24, None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
+        (L.nvfp4_quant, (None, 32, None, 4, 32, None, None, None), N.MOE_EINVAL),         # NULL
         (L.moe_pack_w13, (None, None, 2, 24, 64, None, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_pack_w2, (None, None, 2, 64, 96, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_pack_w2, (None, None, 2, 48, 64, None, None, None), N.MOE_EUNSUPPORTED),   # H % 32
         (L.moe_finalize, (None, 64, 1, 0, None, None, None, f(1.0), f(1e-6), 1, 4, 2, 60, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_finalize, (None, 64, 17, 0, None, None, None, f(1.0), f(1e-6), 1, 4, 2, 64, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_finalize, (None, 64, 1, 0, None, None, None, f(1.0), f(1e-6), 1, 4, 2, 64, None, None), N.MOE_EINVAL),
@@ -75,22 +76,22 @@ def test_invalid_sizes_are_refused():
 def test_experts_refusals():
     L = N.lib()
     w = N.MoeNvfp4Weights()
-    args = lambda H, I, m: (None, None, ctypes.byref(w), 4, 2, 8, H, I, m, None, None, None, None, H, None)
+    args = lambda H, I, m: (None, None, None, ctypes.byref(w), 4, 2, 8, H, I, m, None, None, None, H, None)
     assert L.moe_experts_fwd(*args(96, 128, 16)) == N.MOE_EUNSUPPORTED     # H % 64
     assert L.moe_experts_fwd(*args(256, 96, 16)) == N.MOE_EUNSUPPORTED     # I % 64
     assert L.moe_experts_fwd(*args(256, 128, 48 + 1)) == N.MOE_EUNSUPPORTED
     assert L.moe_experts_fwd(*args(256, 128, 16)) == N.MOE_EINVAL          # NULL pointers
-    assert L.moe_experts_fwd(None, None, None, 4, 2, 8, 256, 128, 16, None, None, None, None, 256, None) == N.MOE_EINVAL
-    assert L.moe_experts_fwd(*args(256, 8192, 16)) == N.MOE_EUNSUPPORTED   # I above the limit
-    assert L.moe_experts_fwd(*args(16384, 128, 16)) == N.MOE_EUNSUPPORTED  # H above the limit
+    assert L.moe_experts_fwd(None, None, None, None, 4, 2, 8, 256, 128, 16, None, None, None, 256, None) == N.MOE_EINVAL
+    assert L.moe_experts_fwd(*args(256, 16384 + 64, 16)) == N.MOE_EUNSUPPORTED   # I above the limit
+    assert L.moe_experts_fwd(*args(16384 + 64, 128, 16)) == N.MOE_EUNSUPPORTED   # H above the limit
     # strides too small for the shape: checked before any launch
     w.w13 = w.w13_sf = w.w2 = w.w2_sf = 256
     w.g1_alphas = w.g1_scale_c = w.g2_alphas = 256
-    assert L.moe_experts_fwd(256, 256, ctypes.byref(w), 4, 2, 8, 256, 128, 16, 256, 256, 256, 256, 256, None) == N.MOE_EINVAL
+    assert L.moe_experts_fwd(256, 256, 256, ctypes.byref(w), 4, 2, 8, 256, 128, 16, 256, 256, 256, 256, None) == N.MOE_EINVAL
     assert b"stride" in L.moe_last_error()
 
 
 def test_zero_tokens_is_a_no_op_without_device():
     L = N.lib()
-    assert L.nvfp4_quant(None, 64, None, 0, 64, None, None, None, None) == N.MOE_OK
+    assert L.nvfp4_quant(None, 64, None, 0, 64, None, None, None) == N.MOE_OK
     assert L.moe_finalize(None, 64, 1, 0, None, None, None, ctypes.c_float(1.0), ctypes.c_float(1e-6), 1, 0, 2, 64, None, None) == N.MOE_OK

@@ -18,7 +18,7 @@ from oracle import layout as OL
 from oracle.finalize import finalize as o_finalize
 from oracle.layer import layer as o_layer, layer_sampled, quantize_input, rel_l2
 from oracle.permute import permute as o_permute
-from oracle.quant import dequantize_nvfp4, quantize_nvfp4
+from oracle.quant import quantize_nvfp4
 from oracle.routing import route as o_route
 
 from .gpu_common import DEV, dev, host, run_layer, say, upload_weights
@@ -44,14 +44,10 @@ def _gpu_quant(x_bf16: np.ndarray, gscale: float):
     T, H = x_bf16.shape
     codes = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
     sf = torch.empty((T, H // 16), dtype=torch.uint8, device=DEV)
-    dq = torch.empty((T, H), dtype=torch.float16, device=DEV)
     say(f"nvfp4_quant T={T} H={H} gscale={gscale}")
-    N.nvfp4_quant(dev(x_bf16), dev(np.array([gscale], np.float32)), codes, sf, dq)
+    N.nvfp4_quant(dev(x_bf16), dev(np.array([gscale], np.float32)), codes, sf)
     torch.cuda.synchronize()
-    c, s = host(codes), host(sf)
-    # the f16 expansion is exactly the dequantized NVFP4 value of every element
-    assert np.array_equal(dq.cpu().numpy().astype(np.float64), dequantize_nvfp4(c, s))
-    return c, s
+    return host(codes), host(sf)
 
 
 @pytest.mark.parametrize("name", W.ORDER)
@@ -199,7 +195,7 @@ def test_route_zero_tokens():
 
 
 # ------------------------------------------------------------------ weight converter
-@pytest.mark.parametrize("E,H,I", [(3, 256, 128), (4, 512, 256), (2, 2048, 768)])
+@pytest.mark.parametrize("E,H,I", [(3, 256, 128), (4, 512, 256), (2, 2048, 768), (1, 64, 64)])
 def test_pack_bit_exact(E, H, I):
     rng = np.random.default_rng(E * H + I)
     w13c = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
@@ -258,11 +254,6 @@ def _compare_layer(res, ref, name):
     assert np.array_equal(res["perm2tok"], ref["meta"]["perm2tok"])
     assert np.array_equal(res["a_codes"], ref["a_codes"]) and np.array_equal(res["a_sf"], ref["a_sf"])
     # intermediate: agree except at rounding boundaries
-    # the f16 intermediate GEMM2 reads is the exact expansion of the NVFP4 one
-    assert np.array_equal(res["inter_dq"][p].view(np.float16).astype(np.float64),
-                          dequantize_nvfp4(res["inter_codes"][p], res["inter_sf"][p]))
-    assert np.array_equal(res["a_dq"].view(np.float16).astype(np.float64),
-                          dequantize_nvfp4(res["a_codes"], res["a_sf"]))
     sf_diff = np.mean(res["inter_sf"][p] != ref["h_sf"])
     code_diff = np.mean(F.unpack_nibbles(res["inter_codes"][p]) != F.unpack_nibbles(ref["h_codes"]))
     rows_rel = rel_l2(F.bf16_to_f64(res["rows"][0][p]), F.bf16_to_f64(ref["rows"][p]))

@@ -143,7 +143,7 @@ def test_rel_l2_closed_form():
 # ------------------------------------------------------------------ layout
 def test_converted_layout_addresses():
     rng = np.random.default_rng(5)
-    E, N, K = 2, 32, 128
+    E, N, K = 2, 64, 128
     codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
     sf = rng.integers(0, 256, (E, N, K // 16), dtype=np.uint8)
     cc = LY.convert_codes(codes).reshape(E, -1)
@@ -151,17 +151,17 @@ def test_converted_layout_addresses():
     nib = F.unpack_nibbles(codes)
     tiles_k = K // 64
     for e in range(E):
-        for n in range(N):
+        for row in range(N):
+            p, h, n = row // 32, (row % 32) // 16, row % 16
             for k in range(K):
-                g, nl, t, kl = n // 16, n % 16, k // 64, k % 64
-                s, q, j = kl // 32, (kl % 32) // 8, kl % 8
-                byte = ((g * tiles_k + t) * 512) + ((q * 16 + nl) * 2 + s) * 4 + j // 2
-                v = (cc[e, byte] >> (4 * (j & 1))) & 15
-                assert v == nib[e, n, k]
+                t, q, i = k // 64, (k % 64) // 16, k % 16
+                byte = (p * tiles_k + t) * 1024 + ((q * 16 + n) * 2 + h) * 8 + i // 2
+                v = (cc[e, byte] >> (4 * (i & 1))) & 15
+                assert v == nib[e, row, k]
             for b in range(K // 16):
-                g, nl, t, bl = n // 16, n % 16, b // 4, b % 4
-                byte = (g * tiles_k + t) * 64 + ((bl % 2) * 16 + nl) * 2 + bl // 2
-                assert cs[e, byte] == sf[e, n, b]
+                t, q = b // 4, b % 4
+                byte = (p * tiles_k + t) * 128 + (q * 16 + n) * 2 + h
+                assert cs[e, byte] == sf[e, row, b]
 
 
 def test_gate_up_interleave_rows():
