@@ -9,6 +9,7 @@
  *   [model]          vllm.models.muse_spark.nvidia.model
  * A layer runs, on one stream, in this order:
  *   moe_route -> nvfp4_quant -> moe_experts_fwd -> moe_finalize
+ * (moe_route_quant is the first two in one launch)
  * (the model page, "_prepared_nvfp4_forward", prepares the quantized input and
  * the routing; the runner page, "MuseSparkTrtLlmNvFp4Experts.apply_routed", runs
  * the experts up to the GEMM2 rows and hands them to "MusePostExpertFinalize").
@@ -137,6 +138,19 @@ int moe_route(const float* logits, int64_t logits_row_stride, const float* exper
  * H % 16 == 0. */
 int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
                 uint8_t* codes, uint8_t* sf, void* stream);
+
+/* ------------------------------------------------------------------ routing + quantizer
+ * moe_route and nvfp4_quant in one launch: the same outputs as moe_route(...)
+ * followed by nvfp4_quant(x, x_row_stride, gscale, T, H, codes, sf) on the
+ * same stream, bit for bit (the quantizer does not depend on the routing, so
+ * its workgroups run beside the routing ones). Arguments and checks are those
+ * of the two calls; H is the quantizer's row length. */
+int moe_route_quant(const float* logits, int64_t logits_row_stride, const float* expert_bias,
+                    const uint8_t* is_padding, int T, int E, int K, float route_scale,
+                    int tile_m, int local_expert_offset, int local_num_experts,
+                    int32_t* topk_ids, float* topk_weights, int32_t* meta, const uint16_t* x,
+                    int64_t x_row_stride, const float* gscale, int H, uint8_t* codes,
+                    uint8_t* sf, void* stream);
 
 /* ------------------------------------------------------------------ weights
  * The converted weight layout the expert kernels read. The property the pages

@@ -13,6 +13,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ host side
 int fail(int code, const char* fmt, ...);          // sets the thread's message, returns code
+int quant_check(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
+                uint8_t* codes, uint8_t* sf, const char* name);   // nvfp4_quant's validation
 int check_launch(const char* what);                // MOE_ELAUNCH on a pending launch error
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m);
@@ -119,6 +121,34 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {   // nearest even
     const uint32_t u = __float_as_uint(f);
     if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return 0x7FC0u;   // NaN
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------ NVFP4 quantizer block
+// One 16-value block (row t, block b) of a bf16 matrix -> 8 code bytes and its
+// e4m3 scale byte, in nvfp4_quant's layout (row-major codes and scales).
+__device__ __forceinline__ void quantize_block16(const uint16_t* __restrict__ x, int64_t x_row_stride,
+                                                 float gscale, int H, int t, int b,
+                                                 uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ sf) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + t * x_row_stride + b * 16);
+    const uint4 p0 = src[0], p1 = src[1];
+    const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        amax = fmaxf(amax, fmaxf(__builtin_fabsf(v[2 * i]), __builtin_fabsf(v[2 * i + 1])));
+    }
+    const BlockScale bs = nvfp4_block_scale(amax, gscale);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= nvfp4_code(v[i], bs) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= nvfp4_code(v[8 + i], bs) << (4 * i);
+    *reinterpret_cast<uint2*>(codes + (int64_t)t * (H >> 1) + b * 8) = make_uint2(lo, hi);
+    sf[(int64_t)t * (H >> 4) + b] = (uint8_t)bs.byte;
 }
 
 // ------------------------------------------------------------------ NVFP4 -> f16 operands

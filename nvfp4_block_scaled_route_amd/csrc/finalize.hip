@@ -4,18 +4,18 @@
 // "_effective_weight". Tensor-parallel K-partial rows are summed in fp32 and
 // rounded once to bf16 before the norm (the expert_tp page, "probe_rel_l2").
 //
-// One 512-thread workgroup (8 waves) per token. Pass 1: wave w forms the sum of
-// squares of routes k = w, w + 8, ... (a lane walks 8-column chunks lane,
-// lane + 64, ...; then a fixed-order wave reduction), so no block-wide
-// reduction is needed. Pass 2: a thread owns 8-column chunks tid, tid + 512, ...
-// and accumulates sum_k w_k * y_k in fp32, k ascending. Rows are re-read in
-// pass 2 (cache hits). Every order is fixed: the output is deterministic.
+// One workgroup per token; a thread owns C 8-column chunks (C = 1, or 2 above
+// 8192 columns). Routes go in batches of 8 whose row loads issue together: the
+// sum of squares of each route (a fixed-order wave reduction, then the waves
+// in order), then sum_k w_k * y_k in fp32, k ascending, from the rows still in
+// registers (batches past the first 8 routes are read again). Every order is
+// fixed: the output is deterministic.
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kFinThreads = 512;
-constexpr int kFinWaves = kFinThreads / 64;
+constexpr int kFinBatch = 8;
+constexpr int kFinMaxThreads = 1024;
 
 struct FinArgs {
     const uint16_t* rows;
@@ -31,102 +31,148 @@ struct FinArgs {
     uint16_t* out;
 };
 
-// 8 values of route row p at columns [8c, 8c + 8): partials summed in fp32 in
-// order, rounded once to bf16 when there is more than one.
-__device__ __forceinline__ void load_row8(const FinArgs& a, int p, int c, float v[8]) {
+__device__ __forceinline__ void unpack8(const uint4& q, float v[8]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu); v[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+}
+
+// Route row p at columns [8c, 8c + 8) as 8 bf16 values: with several partials
+// their fp32 sum in order, rounded once to bf16.
+__device__ __forceinline__ uint4 load_row8(const FinArgs& a, int p, int c) {
     const uint16_t* base = a.rows + (int64_t)p * a.rows_stride + 8 * c;
     uint4 q = *reinterpret_cast<const uint4*>(base);
-    {
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    if (a.n_partials == 1) return q;
+    float v[8];
+    unpack8(q, v);
+    for (int part = 1; part < a.n_partials; ++part) {
+        float u[8];
+        unpack8(*reinterpret_cast<const uint4*>(base + part * a.partial_stride), u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu); v[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+        for (int i = 0; i < 8; ++i) v[i] = __fadd_rn(v[i], u[i]);
     }
-    if (a.n_partials > 1) {
-        for (int part = 1; part < a.n_partials; ++part) {
-            q = *reinterpret_cast<const uint4*>(base + part * a.partial_stride);
-            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = __fadd_rn(v[2 * i], bf16_to_f32(u[i] & 0xFFFFu));
-                v[2 * i + 1] = __fadd_rn(v[2 * i + 1], bf16_to_f32(u[i] >> 16));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i]));
-    }
+    q.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    q.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    q.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+    q.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+    return q;
 }
 
 __device__ __forceinline__ void gamma8(const FinArgs& a, int c, float g[8]) {
     if (a.norm_weight) {
-        const uint4 q = *reinterpret_cast<const uint4*>(a.norm_weight + 8 * c);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        unpack8(*reinterpret_cast<const uint4*>(a.norm_weight + 8 * c), g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            g[2 * i] = __fadd_rn(bf16_to_f32(w[i] & 0xFFFFu), a.gain_center);
-            g[2 * i + 1] = __fadd_rn(bf16_to_f32(w[i] >> 16), a.gain_center);
-        }
+        for (int i = 0; i < 8; ++i) g[i] = __fadd_rn(g[i], a.gain_center);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) g[i] = __fadd_rn(1.0f, a.gain_center);
     }
 }
 
-__global__ void __launch_bounds__(kFinThreads) finalize_kernel(FinArgs a) {
-    __shared__ int s_perm[MOE_MAX_TOPK];
-    __shared__ float s_w[MOE_MAX_TOPK];
+// The rows of routes [k0, k0 + 8) at the thread's chunks (zeros where absent).
+template <int C>
+__device__ __forceinline__ void load_batch(const FinArgs& a, const int32_t* ep, int k0, int tid,
+                                           int nthreads, int nchunks, uint4 raw[C][kFinBatch]) {
+#pragma unroll
+    for (int kk = 0; kk < kFinBatch; ++kk) {
+        const int k = k0 + kk;
+        const int p = k < a.K ? ep[k] : -1;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int chunk = tid + c * nthreads;
+            raw[c][kk] = make_uint4(0u, 0u, 0u, 0u);
+            if (p >= 0 && chunk < nchunks) raw[c][kk] = load_row8(a, p, chunk);
+        }
+    }
+}
+
+template <int C>
+__global__ void __launch_bounds__(kFinMaxThreads) finalize_kernel(FinArgs a) {
+    __shared__ float s_part[kFinMaxThreads / 64][kFinBatch];
     __shared__ float s_inv[MOE_MAX_TOPK];
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nthreads = blockDim.x, nwaves = nthreads >> 6;
     const int nchunks = a.H >> 3;
-    if (tid < a.K) {
-        s_perm[tid] = a.exp2perm[(int64_t)t * a.K + tid];
-        s_w[tid] = a.weights[(int64_t)t * a.K + tid];
-    }
-    __syncthreads();
-    // pass 1: one wave per route
-    for (int k = wv; k < a.K; k += kFinWaves) {
-        const int p = s_perm[k];
-        float ss = 0.0f;
-        if (p >= 0) {
-            for (int c = lane; c < nchunks; c += 64) {
-                float v[8], g[8];
-                load_row8(a, p, c, v);
-                if (a.weight_before_norm) gamma8(a, c, g);
+    const int32_t* ep = a.exp2perm + (int64_t)t * a.K;
+    const float* wp = a.weights + (int64_t)t * a.K;
+    float g[C][8];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+        if (tid + c * nthreads < nchunks) gamma8(a, tid + c * nthreads, g[c]);
+    uint4 raw[C][kFinBatch];
+
+    // sums of squares, batch by batch
+    for (int k0 = 0; k0 < a.K; k0 += kFinBatch) {
+        load_batch<C>(a, ep, k0, tid, nthreads, nchunks, raw);
+        float ss[kFinBatch];
+#pragma unroll
+        for (int kk = 0; kk < kFinBatch; ++kk) {
+            ss[kk] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (tid + c * nthreads >= nchunks) continue;
+                float v[8];
+                unpack8(raw[c][kk], v);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float z = a.weight_before_norm ? __fmul_rn(g[i], v[i]) : v[i];
-                    ss = __fadd_rn(ss, __fmul_rn(z, z));
+                    const float z = a.weight_before_norm ? __fmul_rn(g[c][i], v[i]) : v[i];
+                    ss[kk] = __fadd_rn(ss[kk], __fmul_rn(z, z));
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ss[kk] = __fadd_rn(ss[kk], __shfl_xor(ss[kk], off));
+        }
+        if (lane < kFinBatch) {
+            float mine = ss[0];
+#pragma unroll
+            for (int kk = 1; kk < kFinBatch; ++kk) mine = lane == kk ? ss[kk] : mine;
+            s_part[wv][lane] = mine;
+        }
+        __syncthreads();
+        if (tid < kFinBatch && k0 + tid < a.K) {
+            float total = 0.0f;
+            for (int w = 0; w < nwaves; ++w) total = __fadd_rn(total, s_part[w][tid]);
+            s_inv[k0 + tid] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(total, (float)a.H), a.eps)));
+        }
+        __syncthreads();
+    }
+
+    // weighted sum over the routes, k ascending
+    float acc[C][8];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
+    for (int k0 = 0; k0 < a.K; k0 += kFinBatch) {
+        if (a.K > kFinBatch) load_batch<C>(a, ep, k0, tid, nthreads, nchunks, raw);
+#pragma unroll
+        for (int kk = 0; kk < kFinBatch; ++kk) {
+            const int k = k0 + kk;
+            if (k >= a.K || ep[k] < 0) continue;     // a missing row normalizes to zero
+            const float wk = wp[k], inv = s_inv[k];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                float v[8];
+                unpack8(raw[c][kk], v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float y = a.weight_before_norm ? __fmul_rn(__fmul_rn(g[c][i], v[i]), inv)
+                                                         : __fmul_rn(g[c][i], __fmul_rn(v[i], inv));
+                    acc[c][i] = __fadd_rn(acc[c][i], __fmul_rn(y, wk));
                 }
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) ss = __fadd_rn(ss, __shfl_xor(ss, off));
-        if (lane == 0) s_inv[k] = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(ss, (float)a.H), a.eps)));
     }
-    __syncthreads();
-    // pass 2: weighted sum over routes
-    for (int c = tid; c < nchunks; c += kFinThreads) {
-        float g[8];
-        gamma8(a, c, g);
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int k = 0; k < a.K; ++k) {
-            const int p = s_perm[k];
-            if (p < 0) continue;            // a zero row normalizes to zero
-            const float wk = s_w[k], inv = s_inv[k];
-            float v[8];
-            load_row8(a, p, c, v);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float y = a.weight_before_norm ? __fmul_rn(__fmul_rn(g[i], v[i]), inv)
-                                                     : __fmul_rn(g[i], __fmul_rn(v[i], inv));
-                acc[i] = __fadd_rn(acc[i], __fmul_rn(y, wk));
-            }
-        }
+    for (int c = 0; c < C; ++c) {
+        const int chunk = tid + c * nthreads;
+        if (chunk >= nchunks) continue;
         uint4 o;
-        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
-        *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.H + 8 * c) = o;
+        o.x = f32_to_bf16(acc[c][0]) | (f32_to_bf16(acc[c][1]) << 16);
+        o.y = f32_to_bf16(acc[c][2]) | (f32_to_bf16(acc[c][3]) << 16);
+        o.z = f32_to_bf16(acc[c][4]) | (f32_to_bf16(acc[c][5]) << 16);
+        o.w = f32_to_bf16(acc[c][6]) | (f32_to_bf16(acc[c][7]) << 16);
+        *reinterpret_cast<uint4*>(a.out + (int64_t)t * a.H + 8 * chunk) = o;
     }
 }
 
@@ -157,6 +203,13 @@ extern "C" int moe_finalize(const uint16_t* rows, int64_t rows_stride, int n_par
     a.partial_stride = partial_stride; a.exp2perm = exp2perm; a.weights = topk_weights;
     a.norm_weight = norm_weight; a.gain_center = gain_center; a.eps = eps;
     a.weight_before_norm = weight_before_norm ? 1 : 0; a.T = T; a.K = K; a.H = H; a.out = out;
-    hipLaunchKernelGGL(finalize_kernel, dim3(T), dim3(kFinThreads), 0, (hipStream_t)stream, a);
+    // threads: every 8-column chunk owned once, at most 1024 threads of 1 or 2 chunks
+    const int nchunks = H / 8;
+    const int C = nchunks > kFinMaxThreads ? 2 : 1;
+    const int threads = ((nchunks + C - 1) / C + 63) / 64 * 64;
+    if (C == 1)
+        hipLaunchKernelGGL(finalize_kernel<1>, dim3(T), dim3(threads), 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(finalize_kernel<2>, dim3(T), dim3(threads), 0, (hipStream_t)stream, a);
     return check_launch("moe_finalize");
 }

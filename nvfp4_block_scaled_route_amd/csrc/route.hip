@@ -1,17 +1,26 @@
-// moe_route: MuseSpark1x top-k routing and the permutation metadata.
+// moe_route / moe_route_quant: MuseSpark1x top-k routing and the permutation
+// metadata (and, fused into the same launch, the NVFP4 input quantizer).
 //   the runner page, "validate_deployment" (sigmoid + expert bias + sum
 //   renormalize, no groups, route scale 1); the model page, "MuseSpark1xMoE"
 //   (division eps 1e-15) and "_prepared_nvfp4_forward" (padding tokens -> -1);
 //   the flashinfer_ops page, "FlashInferOps.slot" / "gemm2_rows" (metadata).
 //
-// Phase 1, top-k: one 64-wide wave per token; lane l holds experts l, l+64, ...
-// Each of the K rounds takes the wave-wide best (key desc, index asc) among the
-// experts not taken yet. Lane k keeps the k-th choice; the renormalizing sum runs
-// over k in order.
-// Phase 2, permutation: one workgroup. Routes are processed in chunks of 512 in
-// expanded order; within a wave, routes of the same expert are matched with
-// ballots over the expert index bits, giving each route its rank among earlier
-// routes of its expert (a stable counting sort, no atomics, deterministic).
+// Top-k, one 64-wide wave per token. Selection keys are totally ordered by
+// (key descending, expert index ascending), so every expert's place in the
+// ranking is unique: for E <= 256 each lane counts, against the wave's keys in
+// LDS, the experts that beat its own, and the experts with rank < K land in
+// slot `rank` -- the K choices in key order with no serial rounds. Larger E
+// takes K rounds of a wave-wide arg-max. The renormalizing sum then runs over
+// the K slots in order.
+// Permutation, one workgroup: routes per expert are counted with LDS atomics,
+// the padded offsets scanned, and a second pass gives every route its rank
+// among the earlier routes of its expert (ballot matching over the expert
+// index bits within a wave, a scan across waves: a stable counting sort, no
+// ordering atomics, deterministic) and scatters it at once.
+// Small batches run top-k and the permutation in one workgroup, the top-k ids
+// staying in LDS; larger ones take a top-k grid, then the permutation.
+// moe_route_quant appends the quantizer's workgroups to the first launch: they
+// need nothing from the routing and run beside it.
 #include "common.hpp"
 
 namespace moe {
@@ -19,6 +28,10 @@ namespace moe {
 constexpr int kRouteThreads = 512;                 // 8 waves
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;  // 16
+constexpr int kRankMaxExperts = 256;               // rank-count top-k up to here
+constexpr int kFusedMaxTokens = 32;                // one workgroup routes up to here
+
+enum RouteMode { kTopkOnly = 0, kPermuteOnly = 1, kFused = 2 };
 
 struct RouteArgs {
     const float* logits;
@@ -32,17 +45,108 @@ struct RouteArgs {
     float* weights;
     int32_t* meta;
     moe_meta_layout L;
+    // fused quantizer (x == nullptr: none)
+    const uint16_t* x;
+    int64_t x_row_stride;
+    const float* gscale;
+    int H;
+    uint8_t* codes;
+    uint8_t* sf;
+    int route_blocks;      // workgroups [0, route_blocks) route, the rest quantize
 };
+
+// fp32 -> uint32 with the same order (finite inputs; -0 is first made +0 so
+// that it ties with +0 as the fp32 comparison does)
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(__fadd_rn(f, 0.0f));
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
     return ka > kb || (ka == kb && ia < ib);
 }
 
-__device__ void topk_token(const RouteArgs& a, int t, int lane) {
-    int32_t* ids = a.ids + (int64_t)t * a.K;
-    float* wts = a.weights + (int64_t)t * a.K;
+__device__ __forceinline__ int epad(int E) { return (E + 3) & ~3; }
+
+// LDS of the top-k: per wave Epad keys, then per wave K (expert, score) slots.
+__device__ __forceinline__ uint32_t* topk_keys(int32_t* base) { return reinterpret_cast<uint32_t*>(base); }
+__device__ __forceinline__ uint2* topk_slots(int32_t* base, int E) {
+    return reinterpret_cast<uint2*>(base + kRouteWaves * epad(E));
+}
+
+// Writes token t's ids and weights (and its ids into s_ids when given).
+__device__ __forceinline__ void emit(const RouteArgs& a, int t, int lane, int id, float wt,
+                                     int32_t* s_ids) {
+    a.ids[(int64_t)t * a.K + lane] = id;
+    a.weights[(int64_t)t * a.K + lane] = wt;
+    if (s_ids) s_ids[t * a.K + lane] = id;
+}
+
+// Rank-count top-k of token t by wave w (E <= kRankMaxExperts). Called by every
+// thread of the workgroup (it holds two barriers); `active` is false for waves
+// without a token this round.
+__device__ void topk_rank(const RouteArgs& a, int t, bool active, int lane, int w,
+                          int32_t* lds_topk, int32_t* s_ids) {
+    const int Ep = epad(a.E);
+    uint32_t* key = topk_keys(lds_topk) + w * Ep;
+    uint2* slot = topk_slots(lds_topk, a.E) + w * a.K;
+    const bool live = active && !(a.is_padding && a.is_padding[t]);
+    constexpr int kPer = kRankMaxExperts / 64;
+    float sc[kPer];
+    uint32_t kk[kPer];
+    if (live) {
+        const float* row = a.logits + (int64_t)t * a.logits_row_stride;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = lane + 64 * j;
+            sc[j] = 0.0f;
+            kk[j] = 0u;
+            if (e < a.E) {
+                sc[j] = sigmoid32(row[e]);
+                kk[j] = order_key(a.bias ? __fadd_rn(sc[j], a.bias[e]) : sc[j]);
+                key[e] = kk[j];
+            }
+        }
+        if (lane < Ep - a.E) key[a.E + lane] = 0u;   // padding keys: below every real key
+    }
+    __syncthreads();
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = lane + 64 * j;
+            if (e < a.E) {
+                const uint32_t me = kk[j];
+                int rank = 0;
+                for (int i = 0; i < Ep; i += 4) {
+                    const uint4 q = *reinterpret_cast<const uint4*>(key + i);
+                    rank += (q.x > me) | ((q.x == me) & (i < e));
+                    rank += (q.y > me) | ((q.y == me) & (i + 1 < e));
+                    rank += (q.z > me) | ((q.z == me) & (i + 2 < e));
+                    rank += (q.w > me) | ((q.w == me) & (i + 3 < e));
+                }
+                if (rank < a.K) slot[rank] = make_uint2((uint32_t)e, __float_as_uint(sc[j]));
+            }
+        }
+    }
+    __syncthreads();
+    if (active && lane < a.K) {
+        int id = -1;
+        float wt = 0.0f;
+        if (live) {
+            float total = 0.0f;
+            for (int i = 0; i < a.K; ++i) total = __fadd_rn(total, __uint_as_float(slot[i].y));
+            const uint2 mine = slot[lane];
+            id = (int)mine.x;
+            wt = __fmul_rn(__fdiv_rn(__uint_as_float(mine.y), __fadd_rn(total, 1e-15f)), a.route_scale);
+        }
+        emit(a, t, lane, id, wt, s_ids);
+    }
+}
+
+// K rounds of a wave-wide arg-max (any E), one wave, no barrier.
+__device__ void topk_rounds(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
     if (a.is_padding && a.is_padding[t]) {
-        if (lane < a.K) { ids[lane] = -1; wts[lane] = 0.0f; }
+        if (lane < a.K) emit(a, t, lane, -1, 0.0f, s_ids);
         return;
     }
     const float* row = a.logits + (int64_t)t * a.logits_row_stride;
@@ -76,44 +180,118 @@ __device__ void topk_token(const RouteArgs& a, int t, int lane) {
             const float os = __shfl_xor(bs, off);
             if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bs = os; }
         }
-        // bi, bs are now the same on every lane
         if ((bi & 63) == lane) alive &= ~(1u << (bi >> 6));
         if (lane == k) { my_id = bi; my_s = bs; }
         total = __fadd_rn(total, bs);
     }
-    if (lane < a.K) {
-        const float denom = __fadd_rn(total, 1e-15f);
-        ids[lane] = my_id;
-        wts[lane] = __fmul_rn(__fdiv_rn(my_s, denom), a.route_scale);
+    if (lane < a.K)
+        emit(a, t, lane, my_id,
+             __fmul_rn(__fdiv_rn(my_s, __fadd_rn(total, 1e-15f)), a.route_scale), s_ids);
+}
+
+// Top-k of tokens [first, T) with stride `step`, eight per round (every thread
+// of the workgroup takes part in every round: the rank path holds barriers).
+__device__ void topk_tokens(const RouteArgs& a, int first, int step, int32_t* lds_topk,
+                            int32_t* s_ids) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int base = first; base < a.T; base += step) {
+        const int t = base + w;
+        if (a.E <= kRankMaxExperts) topk_rank(a, t, t < a.T, lane, w, lds_topk, s_ids);
+        else if (t < a.T) topk_rounds(a, t, lane, s_ids);
     }
 }
 
-__device__ void permute_block(const RouteArgs& a) {
-    extern __shared__ int32_t lds[];
+__device__ __forceinline__ int local_expert(const RouteArgs& a, int id) {
+    const int loc = id - a.local_offset;
+    return (id >= 0 && loc >= 0 && loc < a.local_num) ? loc : -1;
+}
+
+// Last local expert whose padded range starts at or before `row` (< total rows).
+__device__ __forceinline__ int expert_of_row(const int32_t* offs, int El, int row) {
+    int lo = 0, hi = El - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The permutation metadata from the top-k ids (global or LDS). One workgroup.
+__device__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
     const int El = a.local_num;
     int32_t* cnt = lds;                           // [kRouteWaves][El]
-    int32_t* running = cnt + kRouteWaves * El;    // [El]
+    int32_t* count = cnt + kRouteWaves * El;      // [El]  routes per expert
+    int32_t* running = count + El;                // [El]  next free row of each expert
     int32_t* offs = running + El;                 // [El + 1]
     int32_t* scan = offs + El + 1;                // [kRouteWaves]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int R = a.T * a.K;
+    const int m = a.tile_m;
     int32_t* exp2perm = a.meta + a.L.exp2perm;
     int32_t* perm2tok = a.meta + a.L.perm2tok;
     int32_t* tile_expert = a.meta + a.L.tile_expert;
-    const int m = a.tile_m;
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-    for (int e = tid; e < El; e += kRouteThreads) running[e] = 0;
+    // pass 1: routes per local expert
+    for (int e = tid; e < El; e += kRouteThreads) count[e] = 0;
+    __syncthreads();
+    for (int r = tid; r < R; r += kRouteThreads) {
+        const int e = local_expert(a, ids[r]);
+        if (e >= 0) atomicAdd(&count[e], 1);
+    }
+    __syncthreads();
+    // padded offsets: exclusive scan of ceil(count / m) * m; each thread owns a
+    // contiguous run of experts
+    {
+        const int per = (El + kRouteThreads - 1) / kRouteThreads;
+        const int e0 = tid * per, e1 = min(El, e0 + per);
+        int my_total = 0;
+        for (int x = e0; x < e1; ++x) my_total += (count[x] + m - 1) / m * m;
+        int incl = my_total;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        if (lane == 63) scan[w] = incl;
+        __syncthreads();
+        int wave_base = 0;
+        for (int ww = 0; ww < w; ++ww) wave_base += scan[ww];
+        int acc = wave_base + incl - my_total;
+        for (int x = e0; x < e1; ++x) {
+            offs[x] = acc;
+            running[x] = acc;
+            acc += (count[x] + m - 1) / m * m;
+        }
+        if (tid == kRouteThreads - 1) offs[El] = wave_base + incl;
+    }
+    __syncthreads();
+    const int total_rows = offs[El];
+    const int num_tiles = total_rows / m;
+    for (int x = tid; x <= El; x += kRouteThreads) a.meta[a.L.expert_offsets + x] = offs[x];
+    for (int x = tid; x < El; x += kRouteThreads) a.meta[a.L.expert_counts + x] = count[x];
+    if (tid == 0) {
+        a.meta[a.L.num_tiles] = num_tiles;
+        a.meta[a.L.total_rows] = total_rows;
+    }
+    // tile -> expert (-1 past the last tile); -1 on every padding row (rows of a
+    // tile past its expert's routes, and every row past the last tile)
+    for (int tile = tid; tile < a.L.tiles_max; tile += kRouteThreads)
+        tile_expert[tile] = tile < num_tiles ? expert_of_row(offs, El, tile * m) : -1;
+    for (int row = tid; row < a.L.rows_max; row += kRouteThreads) {
+        bool pad = row >= total_rows;
+        if (!pad) {
+            const int ex = expert_of_row(offs, El, row);
+            pad = row >= offs[ex] + count[ex];
+        }
+        if (pad) perm2tok[row] = -1;
+    }
+    // pass 2: stable rank within the expert, in chunks of one route per thread
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int base = 0; base < R; base += kRouteThreads) {
         for (int i = tid; i < kRouteWaves * El; i += kRouteThreads) cnt[i] = 0;
         __syncthreads();
         const int r = base + tid;
-        int e = -1;
-        if (r < R) {
-            const int id = a.ids[r];
-            const int loc = id - a.local_offset;
-            if (id >= 0 && loc >= 0 && loc < El) e = loc;
-        }
+        const int e = r < R ? local_expert(a, ids[r]) : -1;
         const bool valid = e >= 0;
         uint64_t match = __ballot(valid);
 #pragma unroll
@@ -136,87 +314,107 @@ __device__ void permute_block(const RouteArgs& a) {
             running[x] = acc;
         }
         __syncthreads();
-        if (r < R) exp2perm[r] = valid ? cnt[w * El + e] + rank_in_wave : -1;  // rank for now
-        __syncthreads();
-    }
-    // Padded offsets: exclusive scan of ceil(count / m) * m over the local experts.
-    int my_total = 0;
-    {
-        // each thread owns a contiguous run of experts
-        const int per = (El + kRouteThreads - 1) / kRouteThreads;
-        const int e0 = tid * per, e1 = min(El, e0 + per);
-        for (int x = e0; x < e1; ++x) my_total += (running[x] + m - 1) / m * m;
-        int incl = my_total;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
-        }
-        if (lane == 63) scan[w] = incl;
-        __syncthreads();
-        int wave_base = 0;
-        for (int ww = 0; ww < w; ++ww) wave_base += scan[ww];
-        int acc = wave_base + incl - my_total;
-        for (int x = e0; x < e1; ++x) {
-            offs[x] = acc;
-            acc += (running[x] + m - 1) / m * m;
-        }
-        if (tid == kRouteThreads - 1) offs[El] = wave_base + incl;
-    }
-    __syncthreads();
-    const int total_rows = offs[El];
-    const int num_tiles = total_rows / m;
-    for (int x = tid; x <= El; x += kRouteThreads) a.meta[a.L.expert_offsets + x] = offs[x];
-    for (int x = tid; x < El; x += kRouteThreads) a.meta[a.L.expert_counts + x] = running[x];
-    if (tid == 0) {
-        a.meta[a.L.num_tiles] = num_tiles;
-        a.meta[a.L.total_rows] = total_rows;
-    }
-    // tile -> expert, and -1 on every padding row (rows of a tile past its expert's
-    // routes, and every row past the last tile).
-    for (int tile = tid; tile < a.L.tiles_max; tile += kRouteThreads) {
-        int ex = -1;
-        if (tile < num_tiles) {
-            const int row = tile * m;
-            int lo = 0, hi = El - 1;                 // last expert with offs <= row
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (offs[mid] <= row) lo = mid; else hi = mid - 1;
+        if (r < R) {
+            if (valid) {
+                const int pos = cnt[w * El + e] + rank_in_wave;
+                exp2perm[r] = pos;
+                perm2tok[pos] = r / a.K;
+            } else {
+                exp2perm[r] = -1;
             }
-            ex = lo;
-            // an expert with zero rows shares its offset with the next one
-            while (ex + 1 < El && offs[ex + 1] <= row) ++ex;
         }
-        tile_expert[tile] = ex;
-        const int first_pad = ex >= 0 ? offs[ex] + running[ex] : 0;
-        for (int i = 0; i < m; ++i) {
-            const int row = tile * m + i;
-            if (ex < 0 || row >= first_pad) perm2tok[row] = -1;
-        }
-    }
-    // Scatter: the thread that wrote route r's rank above is this one (r % 512).
-    for (int r = tid; r < R; r += kRouteThreads) {
-        const int rank = exp2perm[r];
-        if (rank < 0) continue;
-        const int e = a.ids[r] - a.local_offset;
-        const int pos = offs[e] + rank;
-        exp2perm[r] = pos;
-        perm2tok[pos] = r / a.K;
+        __syncthreads();   // cnt is cleared for the next chunk
     }
 }
 
-__global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int do_topk,
-                                                              int do_permute) {
-    if (do_topk) {
-        const int lane = threadIdx.x & 63;
-        const int wave = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
-        const int nwaves = gridDim.x * kRouteWaves;
-        for (int t = wave; t < a.T; t += nwaves) topk_token(a, t, lane);
+__global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int mode) {
+    extern __shared__ int32_t lds[];
+    if ((int)blockIdx.x >= a.route_blocks) {       // the fused quantizer's workgroups
+        const int bpr = a.H >> 4;
+        const int64_t blk = (int64_t)(blockIdx.x - a.route_blocks) * kRouteThreads + threadIdx.x;
+        if (blk < (int64_t)a.T * bpr)
+            quantize_block16(a.x, a.x_row_stride, *a.gscale, a.H, (int)(blk / bpr),
+                             (int)(blk % bpr), a.codes, a.sf);
+        return;
     }
-    if (do_permute) {
-        __syncthreads();   // the top-k ids written above are read back below
-        permute_block(a);
+    if (mode == kTopkOnly) {
+        topk_tokens(a, blockIdx.x * kRouteWaves, a.route_blocks * kRouteWaves, lds, nullptr);
+    } else if (mode == kPermuteOnly) {
+        permute_block(a, a.ids, lds);
+    } else {
+        // ids of all routes first, then the region top-k and permutation share
+        int32_t* s_ids = lds;
+        int32_t* work = lds + ((a.T * a.K + 3) & ~3);
+        topk_tokens(a, 0, kRouteWaves, work, s_ids);
+        __syncthreads();
+        permute_block(a, s_ids, work);
     }
+}
+
+static size_t topk_lds_bytes(int E, int K) {
+    if (E > kRankMaxExperts) return 0;
+    return sizeof(int32_t) * ((size_t)kRouteWaves * ((E + 3) & ~3) + (size_t)kRouteWaves * K * 2);
+}
+
+static size_t permute_lds_bytes(int El) {
+    return sizeof(int32_t) * ((size_t)(kRouteWaves + 3) * El + 1 + kRouteWaves);
+}
+
+static int route_launch(const float* logits, int64_t logits_row_stride, const float* expert_bias,
+                        const uint8_t* is_padding, int T, int E, int K, float route_scale,
+                        int tile_m, int local_expert_offset, int local_num_experts,
+                        int32_t* topk_ids, float* topk_weights, int32_t* meta,
+                        const uint16_t* x, int64_t x_row_stride, const float* gscale, int H,
+                        uint8_t* codes, uint8_t* sf, void* stream, const char* name) {
+    if (T < 0) return fail(MOE_EINVAL, "%s: T=%d", name, T);
+    if (E < 1 || E > MOE_MAX_EXPERTS)
+        return fail(MOE_EUNSUPPORTED, "%s: E=%d outside [1, %d]", name, E, MOE_MAX_EXPERTS);
+    if (K < 1 || K > E || K > MOE_MAX_TOPK)
+        return fail(MOE_EUNSUPPORTED, "%s: K=%d outside [1, min(E, %d)]", name, K, MOE_MAX_TOPK);
+    if (local_num_experts < 1 || local_num_experts > MOE_MAX_EXPERTS || local_expert_offset < 0)
+        return fail(MOE_EINVAL, "%s: local experts [%d, +%d) invalid", name, local_expert_offset,
+                    local_num_experts);
+    if (tile_m < 16 || tile_m > 256 || tile_m % 16)
+        return fail(MOE_EUNSUPPORTED, "%s: tile_m=%d must be a multiple of 16 in [16, 256]", name,
+                    tile_m);
+    if (logits_row_stride < E) return fail(MOE_EINVAL, "%s: logits row stride < E", name);
+    if (!meta) return fail(MOE_EINVAL, "%s: meta is NULL", name);
+    if (T > 0 && (!logits || !topk_ids || !topk_weights))
+        return fail(MOE_EINVAL, "%s: NULL pointer", name);
+    if (!aligned16(meta) || (T > 0 && (!aligned16(logits) || !aligned16(topk_ids) ||
+                                        !aligned16(topk_weights))))
+        return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
+    if ((int64_t)T * K > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too many routes", name);
+    RouteArgs a;
+    a.logits = logits; a.logits_row_stride = logits_row_stride; a.bias = expert_bias;
+    a.is_padding = is_padding; a.T = T; a.E = E; a.K = K; a.route_scale = route_scale;
+    a.tile_m = tile_m; a.local_offset = local_expert_offset; a.local_num = local_num_experts;
+    a.ids = topk_ids; a.weights = topk_weights; a.meta = meta;
+    a.L = meta_layout(T, K, local_num_experts, tile_m);
+    a.x = x; a.x_row_stride = x_row_stride; a.gscale = gscale; a.H = H; a.codes = codes; a.sf = sf;
+    const int64_t qblocks = x ? ((int64_t)T * (H / 16) + kRouteThreads - 1) / kRouteThreads : 0;
+    if (qblocks > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too large", name);
+    const size_t topk_lds = topk_lds_bytes(E, K), perm_lds = permute_lds_bytes(local_num_experts);
+    hipStream_t s = (hipStream_t)stream;
+    if (T <= kFusedMaxTokens) {
+        const size_t lds = sizeof(int32_t) * (((size_t)T * K + 3) & ~(size_t)3) +
+                           (topk_lds > perm_lds ? topk_lds : perm_lds);
+        a.route_blocks = 1;
+        hipLaunchKernelGGL(route_kernel, dim3((unsigned)(1 + qblocks)), dim3(kRouteThreads), lds, s,
+                           a, (int)kFused);
+    } else {
+        const int64_t tb = (T + kRouteWaves - 1) / kRouteWaves;
+        a.route_blocks = (int)(tb < 4096 ? tb : 4096);
+        hipLaunchKernelGGL(route_kernel, dim3((unsigned)(a.route_blocks + qblocks)),
+                           dim3(kRouteThreads), topk_lds, s, a, (int)kTopkOnly);
+        int rc = check_launch(name);
+        if (rc) return rc;
+        a.route_blocks = 1;
+        a.x = nullptr;
+        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), perm_lds, s, a,
+                           (int)kPermuteOnly);
+    }
+    return check_launch(name);
 }
 
 }  // namespace moe
@@ -225,42 +423,25 @@ extern "C" int moe_route(const float* logits, int64_t logits_row_stride, const f
                          const uint8_t* is_padding, int T, int E, int K, float route_scale,
                          int tile_m, int local_expert_offset, int local_num_experts,
                          int32_t* topk_ids, float* topk_weights, int32_t* meta, void* stream) {
+    return moe::route_launch(logits, logits_row_stride, expert_bias, is_padding, T, E, K,
+                             route_scale, tile_m, local_expert_offset, local_num_experts, topk_ids,
+                             topk_weights, meta, nullptr, 0, nullptr, 0, nullptr, nullptr, stream,
+                             "moe_route");
+}
+
+extern "C" int moe_route_quant(const float* logits, int64_t logits_row_stride,
+                               const float* expert_bias, const uint8_t* is_padding, int T, int E,
+                               int K, float route_scale, int tile_m, int local_expert_offset,
+                               int local_num_experts, int32_t* topk_ids, float* topk_weights,
+                               int32_t* meta, const uint16_t* x, int64_t x_row_stride,
+                               const float* gscale, int H, uint8_t* codes, uint8_t* sf,
+                               void* stream) {
     using namespace moe;
-    if (T < 0) return fail(MOE_EINVAL, "moe_route: T=%d", T);
-    if (E < 1 || E > MOE_MAX_EXPERTS)
-        return fail(MOE_EUNSUPPORTED, "moe_route: E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
-    if (K < 1 || K > E || K > MOE_MAX_TOPK)
-        return fail(MOE_EUNSUPPORTED, "moe_route: K=%d outside [1, min(E, %d)]", K, MOE_MAX_TOPK);
-    if (local_num_experts < 1 || local_num_experts > MOE_MAX_EXPERTS || local_expert_offset < 0)
-        return fail(MOE_EINVAL, "moe_route: local experts [%d, +%d) invalid", local_expert_offset,
-                    local_num_experts);
-    if (tile_m < 16 || tile_m > 256 || tile_m % 16)
-        return fail(MOE_EUNSUPPORTED, "moe_route: tile_m=%d must be a multiple of 16 in [16, 256]",
-                    tile_m);
-    if (logits_row_stride < E) return fail(MOE_EINVAL, "moe_route: logits row stride < E");
-    if (!meta) return fail(MOE_EINVAL, "moe_route: meta is NULL");
-    if (T > 0 && (!logits || !topk_ids || !topk_weights))
-        return fail(MOE_EINVAL, "moe_route: NULL pointer");
-    if (!aligned16(meta) || (T > 0 && (!aligned16(logits) || !aligned16(topk_ids) ||
-                                        !aligned16(topk_weights))))
-        return fail(MOE_EINVAL, "moe_route: pointers must be 16-byte aligned");
-    if ((int64_t)T * K > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "moe_route: too many routes");
-    RouteArgs a;
-    a.logits = logits; a.logits_row_stride = logits_row_stride; a.bias = expert_bias;
-    a.is_padding = is_padding; a.T = T; a.E = E; a.K = K; a.route_scale = route_scale;
-    a.tile_m = tile_m; a.local_offset = local_expert_offset; a.local_num = local_num_experts;
-    a.ids = topk_ids; a.weights = topk_weights; a.meta = meta;
-    a.L = meta_layout(T, K, local_num_experts, tile_m);
-    const size_t lds = sizeof(int32_t) * ((size_t)(kRouteWaves + 2) * local_num_experts + 1 + kRouteWaves);
-    hipStream_t s = (hipStream_t)stream;
-    if (T <= kRouteWaves) {
-        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, a, 1, 1);
-    } else {
-        const int grid = (int)((T + kRouteWaves - 1) / kRouteWaves < 8192 ? (T + kRouteWaves - 1) / kRouteWaves : 8192);
-        hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(kRouteThreads), 0, s, a, 1, 0);
-        int rc = check_launch("moe_route (top-k)");
-        if (rc) return rc;
-        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, a, 0, 1);
-    }
-    return check_launch("moe_route");
+    const int rc = quant_check(x, x_row_stride, gscale, T, H, codes, sf, "moe_route_quant");
+    if (rc != MOE_OK) return rc;
+    const bool quant = T > 0 && H > 0;
+    return route_launch(logits, logits_row_stride, expert_bias, is_padding, T, E, K, route_scale,
+                        tile_m, local_expert_offset, local_num_experts, topk_ids, topk_weights,
+                        meta, quant ? x : nullptr, x_row_stride, gscale, H, codes, sf, stream,
+                        "moe_route_quant");
 }

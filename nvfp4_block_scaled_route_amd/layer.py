@@ -103,12 +103,19 @@ class Buffers:
 
 def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, weights: N.Weights,
               norm_weight, gain_center: float, eps: float, weight_before_norm: bool,
-              route_scale: float = 1.0, slices: list[N.Weights] | None = None, stream=None) -> None:
-    """route -> quant -> experts (per TP slice) -> finalize, all enqueued on one stream."""
+              route_scale: float = 1.0, slices: list[N.Weights] | None = None, stream=None,
+              fused_route_quant: bool = True) -> None:
+    """route -> quant -> experts (per TP slice) -> finalize, all enqueued on one stream
+    (route and quant in one launch unless fused_route_quant is False)."""
     s = bufs.shape
-    N.moe_route(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
-                bufs.ids, bufs.weights, bufs.meta, stream)
-    N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, stream)
+    if fused_route_quant:
+        N.moe_route_quant(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
+                          bufs.ids, bufs.weights, bufs.meta, x_bf16, gscale, bufs.a_codes,
+                          bufs.a_sf, stream)
+    else:
+        N.moe_route(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
+                    bufs.ids, bufs.weights, bufs.meta, stream)
+        N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, stream)
     parts = slices if slices is not None else [weights]
     I_part = s.I // len(parts)
     for r, w in enumerate(parts):

@@ -18,7 +18,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 
 # Every symbol include/moe_nvfp4.h declares.
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout_get",
-           "moe_route", "nvfp4_quant", "moe_pack_w13", "moe_pack_w2",
+           "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
            "moe_experts_fwd", "moe_finalize")
 
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         "moe_meta_layout_get": (i32, [i32, i32, i32, i32, ctypes.POINTER(MoeMetaLayout)]),
         "moe_route": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp]),
+        "moe_route_quant": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
+                                  vp, i64, vp, i32, vp, vp, vp]),
         "moe_pack_w13": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
         "moe_pack_w2": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
         "moe_experts_fwd": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
@@ -123,6 +125,19 @@ def nvfp4_quant(x, gscale, codes, sf, stream=None) -> None:
     T, H = x.shape
     _check(lib().nvfp4_quant(_ptr(x), x.stride(0), _ptr(gscale), T, H, _ptr(codes), _ptr(sf),
                              _stream(stream)), "nvfp4_quant")
+
+
+def moe_route_quant(logits, expert_bias, is_padding, K, route_scale, tile_m, local_expert_offset,
+                    local_num_experts, topk_ids, topk_weights, meta, x, gscale, codes, sf,
+                    stream=None) -> None:
+    T, E = logits.shape
+    H = x.shape[1]
+    _check(lib().moe_route_quant(_ptr(logits), logits.stride(0), _ptr(expert_bias),
+                                 _ptr(is_padding), T, E, K, float(route_scale), tile_m,
+                                 local_expert_offset, local_num_experts, _ptr(topk_ids),
+                                 _ptr(topk_weights), _ptr(meta), _ptr(x), x.stride(0),
+                                 _ptr(gscale), H, _ptr(codes), _ptr(sf), _stream(stream)),
+           "moe_route_quant")
 
 
 def moe_pack_w13(codes, sf, E, I, H, out_codes, out_sf, stream=None) -> None:

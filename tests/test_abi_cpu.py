@@ -61,6 +61,10 @@ def test_invalid_sizes_are_refused():
         (L.moe_route, (None, 4, None, None, 4, 8, 2, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EINVAL),  # stride < E
         (L.nvfp4_quant, (None, 24, None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
         (L.nvfp4_quant, (None, 32, None, 4, 32, None, None, None), N.MOE_EINVAL),         # NULL
+        (L.moe_route_quant, (None, 8, None, None, 4, 8, 2, f(1.0), 16, 0, 8, None, None, None,
+                             None, 24, None, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
+        (L.moe_route_quant, (None, 8, None, None, 4, 8, 9, f(1.0), 16, 0, 8, None, None, None,
+                             None, 32, None, 32, None, None, None), N.MOE_EINVAL),         # NULL x
         (L.moe_pack_w13, (None, None, 2, 24, 64, None, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_pack_w2, (None, None, 2, 64, 96, None, None, None), N.MOE_EUNSUPPORTED),
         (L.moe_pack_w2, (None, None, 2, 48, 64, None, None, None), N.MOE_EUNSUPPORTED),   # H % 32

@@ -194,6 +194,44 @@ def test_route_zero_tokens():
     assert np.all(m[L.expert_offsets:L.expert_offsets + 65] == 0)
 
 
+@pytest.mark.parametrize("T,E,K,m", [(5, 256, 8, 16), (20, 512, 6, 32), (32, 128, 8, 16),
+                                     (16, 3, 3, 16), (33, 200, 7, 16)])
+def test_route_tied_keys_both_paths(T, E, K, m):
+    """Many equal keys: the rank count (E <= 256) and the arg-max rounds (E > 256)
+    must both take ties to the lower index, in one workgroup (T <= 32) and in
+    the top-k grid (T > 32)."""
+    rng = np.random.default_rng(T * 7 + E)
+    logits = rng.choice(np.array([-3, -0.5, 0, 0.25, 1, 4], np.float32), (T, E))
+    bias = rng.choice(np.array([0.0, -0.0, 0.125], np.float32), E)
+    pad = rng.random(T) < 0.15
+    _check_route(logits, bias, K, m, padding=pad)
+
+
+@pytest.mark.parametrize("T,H,E,K", [(8, 2048, 64, 8), (300, 256, 128, 8), (1, 64, 8, 2),
+                                     (40, 4096, 300, 4)])
+def test_route_quant_equals_separate_calls(T, H, E, K):
+    rng = np.random.default_rng(T + H)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = W.to_bf16_bits((rng.standard_normal((T, H)) * 3).astype(np.float32))
+    gscale = np.array([0.5], np.float32)
+    pad = rng.random(T) < 0.2
+    ids0, w0, meta0, L = _gpu_route(logits, None, K, 16, padding=pad)
+    codes0, sf0 = _gpu_quant(x, float(gscale[0]))
+    ids = torch.full((T, K), 12345, dtype=torch.int32, device=DEV)
+    w = torch.full((T, K), 7.0, dtype=torch.float32, device=DEV)
+    meta = torch.full((L.total_ints + 64,), -777, dtype=torch.int32, device=DEV)
+    codes = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
+    sf = torch.empty((T, H // 16), dtype=torch.uint8, device=DEV)
+    say(f"moe_route_quant T={T} H={H} E={E} K={K}")
+    N.moe_route_quant(dev(logits), None, dev(pad.astype(np.uint8)), K, 1.0, 16, 0, E, ids, w,
+                      meta, dev(x), dev(gscale), codes, sf)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ids), ids0)
+    assert np.array_equal(host(w).view(np.uint32), w0.view(np.uint32))
+    assert np.array_equal(host(meta), meta0)
+    assert np.array_equal(host(codes), codes0) and np.array_equal(host(sf), sf0)
+
+
 # ------------------------------------------------------------------ weight converter
 @pytest.mark.parametrize("E,H,I", [(3, 256, 128), (4, 512, 256), (2, 2048, 768), (1, 64, 64)])
 def test_pack_bit_exact(E, H, I):
@@ -218,8 +256,19 @@ def test_pack_bit_exact(E, H, I):
 @pytest.mark.parametrize("wbn,npart,use_norm", [(1, 1, True), (0, 1, True), (1, 8, True),
                                                 (1, 1, False), (0, 3, False)])
 def test_finalize_against_oracle(wbn, npart, use_norm):
-    rng = np.random.default_rng(7 + npart)
-    T, K, H, R = 37, 8, 4096, 400
+    _finalize_case(wbn, npart, use_norm, 37, 8, 4096)
+
+
+@pytest.mark.parametrize("K,H,npart", [(20, 16384, 1), (32, 2048, 1), (3, 64, 2), (9, 8200, 1)])
+def test_finalize_batches_and_widths(K, H, npart):
+    """More than one batch of 8 routes, two chunks per thread (H > 8192), a
+    single-wave workgroup (H = 64), a width that leaves the last wave partial."""
+    _finalize_case(1, npart, True, 5, K, H)
+
+
+def _finalize_case(wbn, npart, use_norm, T, K, H):
+    rng = np.random.default_rng(7 + npart + K + H)
+    R = 400
     parts = [F.f32_to_bf16((rng.standard_normal((R, H)) * rng.uniform(0.1, 50)).astype(np.float32))
              for _ in range(npart)]
     e2p = rng.integers(-1, R, (T, K)).astype(np.int32)
