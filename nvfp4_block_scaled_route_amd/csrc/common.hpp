@@ -179,6 +179,50 @@ __device__ __forceinline__ half2v splat_lo(half2v v) { half2v r = {v[0], v[0]}; 
 __device__ __forceinline__ half2v splat_hi(half2v v) { half2v r = {v[1], v[1]}; return r; }
 
 // ------------------------------------------------------------------ wave reductions
+// Cross-lane moves by DPP (no LDS traffic, no wait counter). Controls of the
+// gfx9 encoding: quad_perm, row_shr:n, row_mirror, row_half_mirror,
+// row_bcast:15, row_bcast:31.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int ctrl, int row_mask = 0xF, int bank_mask = 0xF, bool bound_ctrl = true>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, ctrl, row_mask, bank_mask, bound_ctrl);
+}
+template <int ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes in a fixed order (every lane of a 16-lane row forms the
+// same row sum: pairs within quads, quads, halves, then the four rows in
+// order), so the result is deterministic. Uniform result.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = __fadd_rn(v, dpp_f<kDppQuadXor1>(v));
+    v = __fadd_rn(v, dpp_f<kDppQuadXor2>(v));
+    v = __fadd_rn(v, dpp_f<kDppRowHalfMirror>(v));
+    v = __fadd_rn(v, dpp_f<kDppRowMirror>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return __fadd_rn(__fadd_rn(r0, r1), __fadd_rn(r2, r3));
+}
+
+// Inclusive prefix sum over the 64 lanes (integers: exact in any order).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v += dpp_i<kDppRowShr1>(v);
+    v += dpp_i<kDppRowShr2>(v);
+    v += dpp_i<kDppRowShr4>(v);
+    v += dpp_i<kDppRowShr8>(v);
+    v += dpp_i<kDppRowBcast15, 0xA>(v);     // rows 1, 3 += last lane of rows 0, 2
+    v += dpp_i<kDppRowBcast31, 0xC>(v);     // rows 2, 3 += lane 31
+    return v;
+}
+
 __device__ __forceinline__ float wave_max16(float v) {      // max over 16-lane rows
     v = fmaxf(v, __shfl_xor(v, 8));
     v = fmaxf(v, __shfl_xor(v, 4));

@@ -138,19 +138,17 @@ struct RowTile {
 __device__ __forceinline__ RowTile row_tile(const ExpArgs& a, int sub, int n) {
     RowTile r;
     const int per_tile = a.tile_m >> 4;
-    const int t = sub / per_tile;
-    r.e = -1;
-    r.row0 = t * a.tile_m + (sub - t * per_tile) * 16;
-    r.tok = -1;
-    r.vmask = 0;
-    if (t >= a.L.tiles_max) return r;
-    const int e = a.meta[a.L.tile_expert + t];
-    if (e < 0 || e >= a.E_local) return r;
+    const int t = (int)((uint32_t)sub / (uint32_t)per_tile);
+    // Both metadata loads go out before any decision: the tile index is clamped
+    // so that they stay in bounds for units past the last tile.
+    const int tc = min(t, (int)a.L.tiles_max - 1);
+    r.row0 = tc * a.tile_m + (sub - t * per_tile) * 16;
+    const int e = a.meta[a.L.tile_expert + tc];
     int tok = a.meta[a.L.perm2tok + r.row0 + n];
     if (tok >= a.T) tok = -1;
     r.tok = tok;
     r.vmask = (uint32_t)(__ballot(tok >= 0) & 0xFFFFull);
-    r.e = r.vmask ? e : -1;
+    r.e = (t < a.L.tiles_max && e >= 0 && e < a.E_local && r.vmask) ? e : -1;
     return r;
 }
 
@@ -158,10 +156,9 @@ __device__ __forceinline__ RowTile row_tile(const ExpArgs& a, int sub, int n) {
 template <int D>
 __global__ void __launch_bounds__(kThreads) gemm1_kernel(ExpArgs a) {
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-    const int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n1 = a.I >> 4;
-    const int sub = (int)(unit / n1), j = (int)(unit - (int64_t)sub * n1);
+    const uint32_t unit = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n1 = a.I >> 4;
+    const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
     const RowTile rt = row_tile(a, sub, n);
     if (rt.e < 0) return;
     const int e = rt.e;
@@ -201,10 +198,9 @@ __global__ void __launch_bounds__(kThreads) gemm1_kernel(ExpArgs a) {
 template <int D>
 __global__ void __launch_bounds__(kThreads) gemm2_kernel(ExpArgs a) {
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-    const int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock +
-                         __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n2 = a.H >> 5;
-    const int sub = (int)(unit / n2), c = (int)(unit - (int64_t)sub * n2);
+    const uint32_t unit = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n2 = a.H >> 5;
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
     const RowTile rt = row_tile(a, sub, n);
     if (rt.e < 0) return;
     const int e = rt.e;
@@ -303,7 +299,7 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
     const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
     const int64_t grid1 = (units1 + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t grid2 = (units2 + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (grid1 > 0x7FFFFFFF || grid2 > 0x7FFFFFFF)
+    if (units1 > 0x7FFFFFFF || units2 > 0x7FFFFFFF)   // unit indices are 32-bit in the kernels
         return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many work units");
     hipStream_t s = (hipStream_t)stream;
     launch_gemm1_kernel(pipeline_depth((int)kt1), dim3((unsigned)grid1), s, args);

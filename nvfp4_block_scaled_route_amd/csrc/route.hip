@@ -8,15 +8,18 @@
 // Top-k, one 64-wide wave per token. Selection keys are totally ordered by
 // (key descending, expert index ascending), so every expert's place in the
 // ranking is unique: for E <= 256 each lane counts, against the wave's keys in
-// LDS, the experts that beat its own, and the experts with rank < K land in
-// slot `rank` -- the K choices in key order with no serial rounds. Larger E
+// LDS (one 64-bit comparison per key), the experts that beat its own, and the
+// experts with rank < K land in slot `rank` -- the K choices in key order with
+// no serial rounds. Larger E
 // takes K rounds of a wave-wide arg-max. The renormalizing sum then runs over
 // the K slots in order.
-// Permutation, one workgroup: routes per expert are counted with LDS atomics,
-// the padded offsets scanned, and a second pass gives every route its rank
-// among the earlier routes of its expert (ballot matching over the expert
-// index bits within a wave, a scan across waves: a stable counting sort, no
-// ordering atomics, deterministic) and scatters it at once.
+// Permutation: routes per expert are counted, the padded offsets scanned, and
+// a second pass gives every route its rank among the earlier routes of its
+// expert (ballot matching over the expert index bits within a wave: a stable
+// counting sort, no ordering atomics, deterministic) and scatters it at once.
+// Up to 512 routes one wave does it, chunk by chunk, with no workgroup
+// barrier; beyond, one workgroup (LDS atomics for the counts, a scan across
+// its waves for the ranks).
 // Small batches run top-k and the permutation in one workgroup, the top-k ids
 // staying in LDS; larger ones take a top-k grid, then the permutation.
 // moe_route_quant appends the quantizer's workgroups to the first launch: they
@@ -68,10 +71,11 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 
 __device__ __forceinline__ int epad(int E) { return (E + 3) & ~3; }
 
-// LDS of the top-k: per wave Epad keys, then per wave K (expert, score) slots.
-__device__ __forceinline__ uint32_t* topk_keys(int32_t* base) { return reinterpret_cast<uint32_t*>(base); }
+// LDS of the top-k: per wave Epad 64-bit composite keys, then per wave K
+// (expert, score) slots.
+__device__ __forceinline__ uint64_t* topk_keys(int32_t* base) { return reinterpret_cast<uint64_t*>(base); }
 __device__ __forceinline__ uint2* topk_slots(int32_t* base, int E) {
-    return reinterpret_cast<uint2*>(base + kRouteWaves * epad(E));
+    return reinterpret_cast<uint2*>(base + 2 * kRouteWaves * epad(E));
 }
 
 // Writes token t's ids and weights (and its ids into s_ids when given).
@@ -84,16 +88,19 @@ __device__ __forceinline__ void emit(const RouteArgs& a, int t, int lane, int id
 
 // Rank-count top-k of token t by wave w (E <= kRankMaxExperts). Called by every
 // thread of the workgroup (it holds two barriers); `active` is false for waves
-// without a token this round.
+// without a token this round. An expert's composite key is its ordered key in
+// the high word and the complement of its index in the low word, so that one
+// 64-bit comparison decides (key desc, index asc); its rank is the number of
+// larger composites.
 __device__ void topk_rank(const RouteArgs& a, int t, bool active, int lane, int w,
                           int32_t* lds_topk, int32_t* s_ids) {
     const int Ep = epad(a.E);
-    uint32_t* key = topk_keys(lds_topk) + w * Ep;
+    uint64_t* key = topk_keys(lds_topk) + w * Ep;
     uint2* slot = topk_slots(lds_topk, a.E) + w * a.K;
     const bool live = active && !(a.is_padding && a.is_padding[t]);
     constexpr int kPer = kRankMaxExperts / 64;
     float sc[kPer];
-    uint32_t kk[kPer];
+    uint64_t kk[kPer];
     if (live) {
         const float* row = a.logits + (int64_t)t * a.logits_row_stride;
 #pragma unroll
@@ -103,7 +110,8 @@ __device__ void topk_rank(const RouteArgs& a, int t, bool active, int lane, int 
             kk[j] = 0u;
             if (e < a.E) {
                 sc[j] = sigmoid32(row[e]);
-                kk[j] = order_key(a.bias ? __fadd_rn(sc[j], a.bias[e]) : sc[j]);
+                const uint32_t ok = order_key(a.bias ? __fadd_rn(sc[j], a.bias[e]) : sc[j]);
+                kk[j] = ((uint64_t)ok << 32) | (uint32_t)~(uint32_t)e;
                 key[e] = kk[j];
             }
         }
@@ -115,31 +123,31 @@ __device__ void topk_rank(const RouteArgs& a, int t, bool active, int lane, int 
         for (int j = 0; j < kPer; ++j) {
             const int e = lane + 64 * j;
             if (e < a.E) {
-                const uint32_t me = kk[j];
+                const uint64_t me = kk[j];
                 int rank = 0;
-                for (int i = 0; i < Ep; i += 4) {
-                    const uint4 q = *reinterpret_cast<const uint4*>(key + i);
-                    rank += (q.x > me) | ((q.x == me) & (i < e));
-                    rank += (q.y > me) | ((q.y == me) & (i + 1 < e));
-                    rank += (q.z > me) | ((q.z == me) & (i + 2 < e));
-                    rank += (q.w > me) | ((q.w == me) & (i + 3 < e));
+#pragma unroll 4
+                for (int i = 0; i < Ep; i += 2) {
+                    const ulonglong2 q = *reinterpret_cast<const ulonglong2*>(key + i);
+                    rank += (int)(q.x > me) + (int)(q.y > me);
                 }
                 if (rank < a.K) slot[rank] = make_uint2((uint32_t)e, __float_as_uint(sc[j]));
             }
         }
     }
     __syncthreads();
-    if (active && lane < a.K) {
+    if (active) {
         int id = -1;
         float wt = 0.0f;
         if (live) {
+            const uint2 mine = slot[lane < a.K ? lane : 0];
+            // the renormalizing sum over k in order, from the K lanes' scores
             float total = 0.0f;
-            for (int i = 0; i < a.K; ++i) total = __fadd_rn(total, __uint_as_float(slot[i].y));
-            const uint2 mine = slot[lane];
+            for (int k = 0; k < a.K; ++k)
+                total = __fadd_rn(total, __int_as_float(__builtin_amdgcn_readlane((int)mine.y, k)));
             id = (int)mine.x;
             wt = __fmul_rn(__fdiv_rn(__uint_as_float(mine.y), __fadd_rn(total, 1e-15f)), a.route_scale);
         }
-        emit(a, t, lane, id, wt, s_ids);
+        if (lane < a.K) emit(a, t, lane, id, wt, s_ids);
     }
 }
 
@@ -206,14 +214,94 @@ __device__ __forceinline__ int local_expert(const RouteArgs& a, int id) {
     return (id >= 0 && loc >= 0 && loc < a.local_num) ? loc : -1;
 }
 
-// Last local expert whose padded range starts at or before `row` (< total rows).
-__device__ __forceinline__ int expert_of_row(const int32_t* offs, int El, int row) {
-    int lo = 0, hi = El - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offs[mid] <= row) lo = mid; else hi = mid - 1;
+// Lanes of the wave whose route goes to the same local expert (e < 0: none).
+__device__ __forceinline__ uint64_t same_expert_lanes(int e) {
+    uint64_t match = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+        const bool mine = (e >> bit) & 1;
+        const uint64_t b = __ballot(mine);
+        match &= mine ? b : ~b;
     }
-    return lo;
+    return match;
+}
+
+// LDS writes of this wave are seen by its later LDS reads (a wave's LDS
+// operations complete in order); this keeps the compiler from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The permutation metadata by one wave, with no workgroup barrier: routes in
+// chunks of 64 (one per lane), experts in runs of ceil(El / 64) per lane.
+constexpr int kWaveMaxRoutes = 512;
+
+__device__ void permute_wave(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
+    const int El = a.local_num;
+    int32_t* count = lds;                          // [El]
+    int32_t* offs = count + El;                    // [El + 1]
+    int32_t* running = offs + El + 1;              // [El]
+    const int lane = threadIdx.x & 63;
+    const int R = a.T * a.K;
+    const int m = a.tile_m;
+    int32_t* exp2perm = a.meta + a.L.exp2perm;
+    int32_t* perm2tok = a.meta + a.L.perm2tok;
+    int32_t* tile_expert = a.meta + a.L.tile_expert;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+    for (int x = lane; x < El; x += 64) count[x] = 0;
+    wave_lds_sync();
+    for (int base = 0; base < R; base += 64) {
+        const int r = base + lane;
+        const int e = r < R ? local_expert(a, ids[r]) : -1;
+        const uint64_t match = same_expert_lanes(e);
+        if (e >= 0 && (match & lt_mask) == 0) count[e] += __popcll(match);   // one lane per expert
+        wave_lds_sync();
+    }
+    // padded offsets
+    const int per = (El + 63) >> 6;
+    const int x0 = lane * per, x1 = min(El, x0 + per);
+    int mine = 0;
+    for (int x = x0; x < x1; ++x) mine += (count[x] + m - 1) / m * m;
+    const int incl = wave_inclusive_scan(mine);
+    const int total_rows = __builtin_amdgcn_readlane(incl, 63);
+    int acc = incl - mine;
+    for (int x = x0; x < x1; ++x) {
+        offs[x] = acc;
+        running[x] = acc;
+        acc += (count[x] + m - 1) / m * m;
+    }
+    if (lane == 0) offs[El] = total_rows;
+    wave_lds_sync();
+    const int num_tiles = total_rows / m;
+    for (int x = lane; x <= El; x += 64) a.meta[a.L.expert_offsets + x] = offs[x];
+    for (int x = lane; x < El; x += 64) a.meta[a.L.expert_counts + x] = count[x];
+    if (lane == 0) {
+        a.meta[a.L.num_tiles] = num_tiles;
+        a.meta[a.L.total_rows] = total_rows;
+    }
+    for (int x = lane; x < El; x += 64) {
+        for (int tile = offs[x] / m; tile < offs[x + 1] / m; ++tile) tile_expert[tile] = x;
+        for (int row = offs[x] + count[x]; row < offs[x + 1]; ++row) perm2tok[row] = -1;
+    }
+    for (int tile = num_tiles + lane; tile < a.L.tiles_max; tile += 64) tile_expert[tile] = -1;
+    for (int row = total_rows + lane; row < a.L.rows_max; row += 64) perm2tok[row] = -1;
+    // stable ranks, chunk by chunk, scattered at once
+    for (int base = 0; base < R; base += 64) {
+        const int r = base + lane;
+        const int e = r < R ? local_expert(a, ids[r]) : -1;
+        const uint64_t match = same_expert_lanes(e);
+        const int pos = e >= 0 ? running[e] + __popcll(match & lt_mask) : -1;
+        wave_lds_sync();
+        if (e >= 0 && (match & lt_mask) == 0) running[e] += __popcll(match);
+        wave_lds_sync();
+        if (r < R) {
+            exp2perm[r] = pos;
+            if (pos >= 0) perm2tok[pos] = r / a.K;
+        }
+    }
 }
 
 // The permutation metadata from the top-k ids (global or LDS). One workgroup.
@@ -246,12 +334,7 @@ __device__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* l
         const int e0 = tid * per, e1 = min(El, e0 + per);
         int my_total = 0;
         for (int x = e0; x < e1; ++x) my_total += (count[x] + m - 1) / m * m;
-        int incl = my_total;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
-        }
+        const int incl = wave_inclusive_scan(my_total);
         if (lane == 63) scan[w] = incl;
         __syncthreads();
         int wave_base = 0;
@@ -273,18 +356,14 @@ __device__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* l
         a.meta[a.L.num_tiles] = num_tiles;
         a.meta[a.L.total_rows] = total_rows;
     }
-    // tile -> expert (-1 past the last tile); -1 on every padding row (rows of a
-    // tile past its expert's routes, and every row past the last tile)
-    for (int tile = tid; tile < a.L.tiles_max; tile += kRouteThreads)
-        tile_expert[tile] = tile < num_tiles ? expert_of_row(offs, El, tile * m) : -1;
-    for (int row = tid; row < a.L.rows_max; row += kRouteThreads) {
-        bool pad = row >= total_rows;
-        if (!pad) {
-            const int ex = expert_of_row(offs, El, row);
-            pad = row >= offs[ex] + count[ex];
-        }
-        if (pad) perm2tok[row] = -1;
+    // tile -> expert and -1 on the padding rows of each expert's range (the
+    // expert's own thread), then -1 past the last tile
+    for (int x = tid; x < El; x += kRouteThreads) {
+        for (int tile = offs[x] / m; tile < offs[x + 1] / m; ++tile) tile_expert[tile] = x;
+        for (int row = offs[x] + count[x]; row < offs[x + 1]; ++row) perm2tok[row] = -1;
     }
+    for (int tile = num_tiles + tid; tile < a.L.tiles_max; tile += kRouteThreads) tile_expert[tile] = -1;
+    for (int row = total_rows + tid; row < a.L.rows_max; row += kRouteThreads) perm2tok[row] = -1;
     // pass 2: stable rank within the expert, in chunks of one route per thread
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int base = 0; base < R; base += kRouteThreads) {
@@ -293,13 +372,7 @@ __device__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* l
         const int r = base + tid;
         const int e = r < R ? local_expert(a, ids[r]) : -1;
         const bool valid = e >= 0;
-        uint64_t match = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 10; ++bit) {
-            const bool mine = (e >> bit) & 1;
-            const uint64_t b = __ballot(mine);
-            match &= mine ? b : ~b;
-        }
+        const uint64_t match = same_expert_lanes(e);
         const int rank_in_wave = __popcll(match & lt_mask);
         if (valid && rank_in_wave == 0) cnt[w * El + e] = __popcll(match);
         __syncthreads();
@@ -340,20 +413,22 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int m
     if (mode == kTopkOnly) {
         topk_tokens(a, blockIdx.x * kRouteWaves, a.route_blocks * kRouteWaves, lds, nullptr);
     } else if (mode == kPermuteOnly) {
-        permute_block(a, a.ids, lds);
+        if (a.T * a.K > kWaveMaxRoutes) permute_block(a, a.ids, lds);
+        else if (threadIdx.x < 64) permute_wave(a, a.ids, lds);
     } else {
         // ids of all routes first, then the region top-k and permutation share
         int32_t* s_ids = lds;
         int32_t* work = lds + ((a.T * a.K + 3) & ~3);
         topk_tokens(a, 0, kRouteWaves, work, s_ids);
         __syncthreads();
-        permute_block(a, s_ids, work);
+        if (a.T * a.K > kWaveMaxRoutes) permute_block(a, s_ids, work);
+        else if (threadIdx.x < 64) permute_wave(a, s_ids, work);
     }
 }
 
 static size_t topk_lds_bytes(int E, int K) {
     if (E > kRankMaxExperts) return 0;
-    return sizeof(int32_t) * ((size_t)kRouteWaves * ((E + 3) & ~3) + (size_t)kRouteWaves * K * 2);
+    return sizeof(int32_t) * ((size_t)2 * kRouteWaves * ((E + 3) & ~3) + (size_t)kRouteWaves * K * 2);
 }
 
 static size_t permute_lds_bytes(int El) {
