@@ -40,6 +40,24 @@ def parse():
 
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per expert step from the committed PMC summary
+    (profiles/experts_<workload>_traffic.json), or None when there is none or
+    when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"experts_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return float(rec["traffic_bytes"]) if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def algorithmic_bytes(wl, counts) -> dict:
@@ -169,7 +187,8 @@ def main():
                    "tp": wl.tp, "tile_m": wl.tile_m, "weight_copies": copies},
         "roofline": {"bound": "hbm", "kernel": "moe_experts_fwd (gemm1_kernel: GEMM1+SwiGLU+requant, gemm2_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                      "experts_touched": ab["touched"], "kernel_ms": k_ms},
     }
