@@ -32,26 +32,12 @@
 // metadata entry, which is -1 for every tile past the routed ones, so those
 // waves exit at once. The expert kernels never read expert counts: a 16-row
 // tile's padding rows have token -1 and are neither read nor written.
-#include "common.hpp"
+#include "experts.hpp"
 
 namespace moe {
 
-struct ExpArgs {
-    const uint8_t* a_codes;
-    const uint8_t* a_sf;
-    const int32_t* meta;
-    moe_meta_layout L;
-    moe_nvfp4_weights w;
-    int T, E_local, H, I, tile_m;
-    uint8_t* inter_codes;
-    uint8_t* inter_sf;
-    uint16_t* rows;
-    int64_t rows_stride;
-};
-
 constexpr int kThreads = 256;              // 4 independent waves per workgroup
 constexpr int kWavesPerBlock = kThreads / 64;
-constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;   // per pair and k-tile
 
 __device__ __forceinline__ floatx4 mfma16(const half8& a, const half8& b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -302,6 +288,12 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
     if (units1 > 0x7FFFFFFF || units2 > 0x7FFFFFFF)   // unit indices are 32-bit in the kernels
         return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many work units");
     hipStream_t s = (hipStream_t)stream;
+    // Many routes per expert (on average a quarter of a 128-row block or more):
+    // the GEMMs are MFMA-bound and take the LDS-tiled kernels.
+    if (tiled_shape_ok(H, I, tile_m) && (int64_t)T * K >= (int64_t)32 * E_local) {
+        launch_tiled(args, s);
+        return check_launch("moe_experts_fwd (tiled)");
+    }
     launch_gemm1_kernel(pipeline_depth((int)kt1), dim3((unsigned)grid1), s, args);
     int rc = check_launch("moe_experts_fwd (GEMM1)");
     if (rc) return rc;

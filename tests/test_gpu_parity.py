@@ -323,6 +323,23 @@ def test_layer_parity_full_oracle(inputs, name):
     _compare_layer(res, ref, name)
 
 
+@pytest.mark.parametrize("T,H,I,E,K,m", [(256, 512, 256, 4, 2, 128), (200, 256, 512, 6, 3, 256),
+                                         (96, 1024, 256, 3, 2, 128)])
+def test_layer_parity_tiled_path(T, H, I, E, K, m):
+    """Many routes per expert: the LDS-tiled MFMA kernels (every 128-row block
+    of one expert, padding rows in every expert's last block), whole layer
+    against the oracle."""
+    from oracle.layer import intermediate_amax
+    wl = W.Workload(f"tiled_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E, K=K, tile_m=m, seed=3)
+    probe = W.make_inputs(wl, a2_gscale=1.0)
+    a2 = float(np.float32(2688.0 / intermediate_amax(probe)))
+    inp = W.make_inputs(wl, a2_gscale=a2)
+    assert T * K >= 32 * E                      # the tiled path's dispatch condition
+    res = run_layer(inp)
+    ref = o_layer(inp)
+    _compare_layer(res, ref, wl.name)
+
+
 @pytest.mark.parametrize("tile_m", [32, 64, 256])
 def test_layer_parity_other_tiles(inputs, tile_m):
     inp = inputs("decode_b8")
