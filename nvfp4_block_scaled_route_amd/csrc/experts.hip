@@ -289,8 +289,8 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
         return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many work units");
     hipStream_t s = (hipStream_t)stream;
     // Many routes per expert (on average a quarter of a 128-row block or more):
-    // the GEMMs are MFMA-bound and take the LDS-tiled kernels.
-    if (tiled_shape_ok(H, I, tile_m) && (int64_t)T * K >= (int64_t)32 * E_local) {
+    // the GEMMs are MFMA-bound and take the register-tiled kernels.
+    if (tiled_shape_ok(T, H, I, tile_m) && (int64_t)T * K >= (int64_t)32 * E_local) {
         launch_tiled(args, s);
         return check_launch("moe_experts_fwd (tiled)");
     }

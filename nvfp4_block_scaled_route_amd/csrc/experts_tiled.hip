@@ -1,278 +1,515 @@
-// The expert GEMMs for many routes per expert (prefill): LDS-tiled MFMA.
+// The expert GEMMs for many routes per expert (prefill): register-tiled MFMA.
 //   the runner page, "MuseSparkTrtLlmNvFp4Experts.apply_routed"; the
 //   flashinfer_ops page, "routed_experts_from_metadata" -- same arithmetic as
 //   the streaming kernels in experts.hip (GEMM1 + SwiGLU + requant, GEMM2).
 //
 // With hundreds of routes per expert the GEMMs are bound by the matrix cores,
-// not by the weight stream, and every operand element must serve many MFMAs.
-// A workgroup computes a 128 x 128 output block (128 permuted rows of one
-// expert x 128 weight rows = 4 row pairs) over K in 64-wide k-tiles:
-//   * four waves, 2 x 2, each compute 64 x 64 with v_mfma_f32_32x32x16_f16;
-//   * the weight operand B goes through LDS: the 256 threads load one k-tile
-//     of it as NVFP4 (16 code bytes + the scale word each), decode it once to
-//     exact f16 and store it (double buffered, rows padded to 144 bytes), and
-//     every wave reads its fragments from there;
-//   * the activation operand A goes straight to registers: each wave gathers
-//     its own 64 rows in MFMA lane order (a lane's 32 elements of a k-tile are
-//     two whole NVFP4 blocks of its row: the MFMA K index is permuted on both
-//     operands to make it so) and decodes them itself, so A costs no LDS
-//     traffic and no LDS latency sits before the MFMAs;
-//   * the raw loads run 4 k-tiles ahead in registers, so HBM latency is hidden
-//     behind 4 k-tiles of MFMA work; one barrier per k-tile.
-// Blocks are mapped so that consecutive row blocks with the same column block
-// -- usually rows of one expert, sharing its weights -- run on the same XCD
-// (workgroups are dealt to the 8 XCDs round robin) and meet in its L2.
-// GEMM1's epilogue (SwiGLU, 16-wide amax, e4m3 scale, codes) and GEMM2's
-// (bf16 rows) work from the MFMA accumulators; rows without a route are
-// neither read from global memory as routes nor written.
+// not by the weight stream. gfx950 has no MFMA for 16-element blocks under e4m3
+// scales, so both operands are decoded to exact f16 (one VALU instruction per
+// element) and multiplied with v_mfma_f32_32x32x16_f16. The decode is the cost
+// to amortize: every decoded element must feed as many MFMAs as possible.
+//
+// A workgroup takes one 128-row block of one expert and 4 column blocks of 128;
+// each of its 4 waves computes one 128 x 128 output block over K in 64-wide
+// k-tiles with 4 x 4 accumulators (the 256 accumulators fill the AGPR file: one
+// wave per SIMD):
+//   * the MFMA K index is permuted on both operands so that over the 4 K-steps
+//     of a k-tile a lane (r, h) of a 32 x 32 x 16 MFMA holds two whole NVFP4
+//     blocks of its row (column), blocks 2h and 2h + 1, each under one scale;
+//     a decoded A fragment then feeds 4 MFMAs and a decoded B fragment 4:
+//     4 VALU instructions per 32-cycle MFMA, which run beside the matrix pipe;
+//   * the weights (B) go straight from global memory to registers in MFMA lane
+//     order (whole pair tiles of the converted layout: full cache lines), two
+//     k-tiles ahead;
+//   * the activation rows (A) are shared by the 4 waves: the workgroup copies 4
+//     k-tiles of its 128 rows at a time (128 bytes of codes per row: whole cache
+//     lines) with direct global-to-LDS loads into a double-buffered LDS stage,
+//     one barrier per stage, and each wave reads its fragments from there. A
+//     row's 16-byte chunks are stored XOR-swizzled by the row's low 3 bits, so
+//     the fragment reads of 8 consecutive rows hit 8 different bank groups.
+//     (Gathered straight into registers, every A load touched 32 cache lines
+//     for 32 bytes each, and the weight stream evicted them before the next
+//     k-tile could use the rest.)
+//   * row tiles with no route are skipped (an expert's rows are padded to the
+//     block size): a block runs with 1 to 4 row tiles.
+// Workgroups are mapped to the routed row blocks only (their count is read from
+// the routing metadata), split into 8 equal contiguous chunks, one per XCD
+// (workgroups are dealt to the 8 XCDs round robin), row block major: the
+// column groups of a row block, and the row blocks of one expert, run on the
+// same XCD at about the same time and share the A rows and the weights in its L2.
+//
+// GEMM1's columns are arranged so that a lane holds the gate and the up value of
+// the same intermediate in two accumulators (column tiles 2t and 2t + 1 take the
+// gate and the up halves of the same two pairs), so SwiGLU is lane-local; the
+// 16-wide amax and the packing of the codes use DPP moves within 16-lane rows.
+// GEMM2 writes bf16 rows. Rows without a route are not written.
 #include "experts.hpp"
 
 namespace moe {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTM = 128, kTN = 128, kTK = 64;
-constexpr int kLdsRow = kTK + 8;            // halves per LDS row
-constexpr int kTiledThreads = 256;
-constexpr int kAhead = 4;                   // k-tiles loaded ahead in registers
+constexpr int kCT = 4;                      // 32-column MFMA tiles per wave
+constexpr int kBlockRows = 128;             // rows per block (4 row tiles of 32)
+constexpr int kWaves = 4;                   // waves (column blocks) per workgroup
+constexpr int kStage = 4;                   // k-tiles per A stage in LDS
+constexpr int kAhead = 2;                   // weight k-tiles loaded ahead in registers
 constexpr int kXcds = 8;
+constexpr int kARowBytes = 32 * kStage;     // codes of one row in a stage
+constexpr int kASfBytes = 4 * kStage;       // block scales of one row in a stage
 
-// One thread's raw operands of one k-tile: its A rows (each lane holds 32 of
-// K = 64: blocks 2h and 2h + 1 of its row, h = lane / 32) and one B slot
-// (block q of row n of both halves of a pair). Scales are loaded as aligned
-// 32-bit words (in bounds: the 4 block scales of a row's k-tile; the scales of
-// an even/odd slot pair) and the thread's 16 bits are shifted out where they
-// are used: a 16-bit load would be widened with a mask that the compiler
-// hoists to the top of the loop, where it makes every wave wait for all loads
-// in flight.
-struct TileRegs {
-    uint4 a[2];       // A, row tiles 0 and 1: 32 elements each (2 blocks)
-    uint32_t asf[2];  // the rows' 4 block scales of the k-tile
-    uint4 b;          // B slot
-    uint32_t bsf;     // scales of slots 2 (slot / 2), 2 (slot / 2) + 1
+// LDS: two A stages (codes, swizzled; block scales)
+struct ALds {
+    uint8_t codes[2][kBlockRows * kARowBytes];
+    uint8_t sf[2][kBlockRows * kASfBytes];
 };
 
-struct TilePtrs {
-    const uint8_t* ac[2];   // k-tile c at +32 c
-    const uint8_t* as[2];   // +4 c
-    const uint8_t* bc;      // +1024 c
-    const uint8_t* bs;      // +128 c
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+    // raw buffer (stride 0) with no range limit; gfx9 data-format word
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// One lane's raw weight operands of one k-tile: blocks 2h and 2h + 1 of each
+// column tile's column (8 bytes each, 256 bytes apart in the pair tile) and the
+// u32 words holding their scales. In GEMM1 column tiles 2t and 2t + 1 are the
+// two halves of the same pairs, whose scale bytes share words: kSW word pairs.
+template <int MODE>
+struct BRaw {
+    static constexpr int kSW = MODE == 1 ? kCT / 2 : kCT;
+    static constexpr int kLoads = 2 * kCT + 2 * kSW;
+    uint2 b[kCT][2];
+    uint32_t bsf[kSW][2];
 };
 
-// The six loads of a k-tile always issue in this order and by themselves
+// One lane's raw activation operands of one k-tile: the 32 codes (blocks 2h,
+// 2h + 1) of each row tile's row and the row's 4 block scales of the k-tile.
+template <int RT>
+struct ARaw {
+    uint4 a[RT];
+    uint32_t asf[RT];
+};
+
+struct BSrc {
+    __amdgpu_buffer_rsrc_t b, bs;   // k-tile c at + 1024 c, + 128 c
+    uint32_t b_off, bs_off;         // per lane
+    int b_step, bs_step;            // from one pair to the next
+};
+
+// The weight loads of a k-tile always issue in this order and by themselves
 // (prologue and loop alike), so that every use waits only for the loads issued
 // before it: vmcnt drains in issue order.
-__device__ __forceinline__ void tile_load(TileRegs& r, const TilePtrs& p, int c) {
+template <int MODE>
+__device__ __forceinline__ void b_load(BRaw<MODE>& r, const BSrc& p, int c) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int j = 0; j < kCT; ++j) {
+        // GEMM1: tile j = 2t + g is half g of pairs 2t + lane / 16;
+        // GEMM2: tile j is pair j
+        const int so = c * kSlotBytes + (MODE == 1 ? (j >> 1) * 2 : j) * p.b_step;
+        const int o = (int)p.b_off + (MODE == 1 ? (j & 1) * 8 : 0);
         __builtin_amdgcn_sched_barrier(0);
-        r.a[i] = *reinterpret_cast<const uint4*>(p.ac[i] + c * 32);
+        const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(p.b, o, so, 0);
         __builtin_amdgcn_sched_barrier(0);
-        r.asf[i] = *reinterpret_cast<const uint32_t*>(p.as[i] + c * 4);
+        const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(p.b, o + 256, so, 0);
+        r.b[j][0] = make_uint2(v0[0], v0[1]);
+        r.b[j][1] = make_uint2(v1[0], v1[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < BRaw<MODE>::kSW; ++t) {
+        const int so = c * kSlotSfBytes + t * (MODE == 1 ? 2 : 1) * p.bs_step;
+        __builtin_amdgcn_sched_barrier(0);
+        r.bsf[t][0] = __builtin_amdgcn_raw_buffer_load_b32(p.bs, (int)p.bs_off, so, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        r.bsf[t][1] = __builtin_amdgcn_raw_buffer_load_b32(p.bs, (int)p.bs_off + 32, so, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    r.b = *reinterpret_cast<const uint4*>(p.bc + (int64_t)c * kSlotBytes);
-    __builtin_amdgcn_sched_barrier(0);
-    r.bsf = *reinterpret_cast<const uint32_t*>(p.bs + (int64_t)c * kSlotSfBytes);
-    __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void store_half8(_Float16* dst, const half8& v) {
-    *reinterpret_cast<half8*>(dst) = v;
+// The workgroup's copy of A stage g into LDS buffer g & 1. Codes: wave w's
+// load q covers rows 32q + 8w + [0, 8) (1 KB, lane l at byte 16 l): lane l
+// fetches chunk (l % 8) ^ (row % 8) of row 32q + 8w + l / 8. Scales: waves 0
+// and 1, lane l fetches the 16 scale bytes of row 64w + l.
+//
+// The copies are written as inline assembly on purpose: the compiler treats
+// its own direct-to-LDS loads as LDS writes of unknown extent and waits for
+// all of them (vmcnt(0), the weight prefetch included) before every LDS read,
+// which would serialize the stage pipeline. Here the stage's own vmcnt wait
+// and barrier order the copies against the reads. M0 holds the LDS address.
+struct ASrc {
+    u32x4 a, as;                    // buffer descriptors
+    uint32_t a_off[4];              // per lane and load q: row start + chunk
+    uint32_t as_off;                // per lane: row start (waves 0, 1)
+};
+
+__device__ __forceinline__ u32x4 buffer_desc(const void* base) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    // raw buffer (stride 0) with no range limit; gfx9 data-format word
+    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
 }
 
-// Decode one thread's B slot of a k-tile into LDS. The MFMA's K index is
-// permuted on both operands: lane (h, r) of a K = 16 step s takes elements
-// 32h + 8s + [0, 8) of the k-tile (the A lane's own two blocks), so element j of
-// block q lives at LDS column 32 (q % 2) + 16 (j / 8) + 8 (q / 2) + j % 8.
-__device__ __forceinline__ void store_b(const TileRegs& r, _Float16 (*Bs)[kLdsRow], int bp, int slot) {
-    const half2v sb = e4m3x2_to_f16(r.bsf >> (16 * (slot & 1)));
-    const half2v sb0 = splat_lo(sb), sb1 = splat_hi(sb);
-    const int q = slot >> 4, n = slot & 15;
-    const int col = 32 * (q & 1) + 8 * (q >> 1);
-    _Float16* b0 = &Bs[bp * 32 + n][col];
-    _Float16* b1 = &Bs[bp * 32 + 16 + n][col];
-    store_half8(b0, nvfp4x8_to_f16(r.b.x, sb0));
-    store_half8(b0 + 16, nvfp4x8_to_f16(r.b.y, sb0));
-    store_half8(b1, nvfp4x8_to_f16(r.b.z, sb1));
-    store_half8(b1 + 16, nvfp4x8_to_f16(r.b.w, sb1));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// The wave's 64 x 64 block over one k-tile: A decoded from the lane's own
-// registers, B fragments from LDS, 4 steps of K = 16, 2 x 2 MFMA tiles.
-__device__ __forceinline__ void tile_mfma(const TileRegs& r, const _Float16 (*Bs)[kLdsRow], int wn,
-                                          int lane, floatx16 acc[2][2]) {
-    const int rr = lane & 31, h = lane >> 5;
-    half8 bf[4][2];
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+__device__ __forceinline__ void a_stage_load(ALds& lds, const ASrc& p, int wave, int g) {
+    const int buf = g & 1;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int q = 0; q < 4; ++q)
+        lds_copy16(p.a, __builtin_amdgcn_readfirstlane(lds_addr(&lds.codes[buf][(32 * q + 8 * wave) * kARowBytes])),
+                   p.a_off[q], (uint32_t)(g * kARowBytes));
+    if (wave < 2)
+        lds_copy16(p.as, __builtin_amdgcn_readfirstlane(lds_addr(&lds.sf[buf][64 * wave * kASfBytes])), p.as_off,
+                   (uint32_t)(g * kASfBytes));
+}
+
+// A fragments of k-tile c of a stage: lane (nn, h) of row tile i reads the 16
+// bytes of chunk 2c + h of row 32 i + nn (swizzled), and its 4 block scales.
+template <int RT>
+__device__ __forceinline__ void a_read(ARaw<RT>& r, const ALds& lds, int buf, int c, int nn, int h) {
+    const int pos = ((2 * c + h) ^ (nn & 7)) * 16;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bf[s][j] = *reinterpret_cast<const half8*>(&Bs[wn * 64 + j * 32 + rr][s * 16 + 8 * h]);
-    half2v sa[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const half2v sc = e4m3x2_to_f16(r.asf[i] >> (16 * h));
-        sa[i][0] = splat_lo(sc);
-        sa[i][1] = splat_hi(sc);
+    for (int i = 0; i < RT; ++i) {
+        r.a[i] = *reinterpret_cast<const uint4*>(&lds.codes[buf][(32 * i + nn) * kARowBytes + pos]);
+        r.asf[i] = *reinterpret_cast<const uint32_t*>(&lds.sf[buf][(32 * i + nn) * kASfBytes + 4 * c]);
     }
+}
+
+// The MFMAs of one k-tile. K-step s takes, in lane (r, h), the elements
+// 32 h + 8 s + [0, 8) of the k-tile: u32 word s of the lane's 16 code bytes,
+// under the scale of block 2h + s / 2. The fragments of step s + 1 are decoded
+// while the MFMAs of step s run: one MFMA, then 4 or 5 VALU instructions.
+template <int RT>
+struct Frags {
+    half8 a[RT], b[kCT];
+};
+
+template <int MODE, int RT>
+__device__ __forceinline__ void decode_step(const ARaw<RT>& ar, const BRaw<MODE>& br, const half2v (&sa)[RT],
+                                            const half2v (&sb)[kCT], int s, Frags<RT>& f) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const uint32_t w = s == 0 ? ar.a[i].x : s == 1 ? ar.a[i].y : s == 2 ? ar.a[i].z : ar.a[i].w;
+        f.a[i] = nvfp4x8_to_f16(w, s < 2 ? splat_lo(sa[i]) : splat_hi(sa[i]));
+    }
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) {
+        const uint32_t w = s == 0 ? br.b[j][0].x : s == 1 ? br.b[j][0].y : s == 2 ? br.b[j][1].x : br.b[j][1].y;
+        f.b[j] = nvfp4x8_to_f16(w, s < 2 ? splat_lo(sb[j]) : splat_hi(sb[j]));
+    }
+}
+
+template <int MODE, int RT>
+__device__ __forceinline__ void tile_mfma(const ARaw<RT>& ar, const BRaw<MODE>& br, int h,
+                                          const uint32_t (&sel)[2], floatx16 (&acc)[RT][kCT]) {
+    half2v sa[RT], sb[kCT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) sa[i] = e4m3x2_to_f16(ar.asf[i] >> (16 * h));
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) {
+        const int t = MODE == 1 ? j >> 1 : j;
+        sb[j] = e4m3x2_to_f16(__builtin_amdgcn_perm(br.bsf[t][1], br.bsf[t][0], sel[MODE == 1 ? j & 1 : 0]));
+    }
+    Frags<RT> f[2];
+    decode_step(ar, br, sa, sb, 0, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        half8 af[2];
+        if (s < 3) decode_step(ar, br, sa, sb, s + 1, f[(s + 1) & 1]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t w = s == 0 ? r.a[i].x : s == 1 ? r.a[i].y : s == 2 ? r.a[i].z : r.a[i].w;
-            af[i] = nvfp4x8_to_f16(w, sa[i][s >> 1]);
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int j = 0; j < kCT; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[s & 1].a[i], f[s & 1].b[j], acc[i][j], 0, 0, 0);
+        if (s < 3) {
+#pragma unroll
+            for (int k = 0; k < RT * kCT; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 8 * (RT + kCT) / (RT * kCT) + 1, 0);   // VALU
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// s_waitcnt immediate (gfx9 encoding): at most n vector-memory loads in
+// flight, the other counters unconstrained
+__host__ __device__ constexpr int vmcnt_at_most(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// max over 16-lane rows by DPP (exact in any order)
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return v;
+}
+
+// lane i of each 16-lane row receives lane i + n (0 past the row's end)
+template <int n>
+__device__ __forceinline__ uint32_t row_shl(uint32_t v) {
+    return (uint32_t)dpp_i<0x100 + n>((int)v);
+}
+
+// lane i of each 16-lane row receives lane x of the row
+template <int x>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + x, 0xF, 0xF, false));
+}
+
+// GEMM1 epilogue of one gate tile and its up tile: rows m0 + [0, 32), lane l
+// holds intermediate col0 + l % 32 of rows m0 + 8(x/4) + 4(l/32) + x%4 in
+// element x. The 16 intermediates of a block sit in one 16-lane row, so the
+// amax is a row max; the block scale of element x is computed by lane x of the
+// row (one scale per lane, then broadcast back), and the codes are packed 8 to
+// a word by shifting within the row.
+__device__ __forceinline__ void swiglu_quant_tile(const floatx16& gacc, const floatx16& uacc, float ga, float uc,
+                                                  int lane, uint32_t vrow, const ExpArgs& a, int m0, int col0) {
+    const int n = lane & 15, h = lane >> 5;
+    const int col = col0 + (lane & 31);
+    float hv[16];
+    float amax_t = 0.0f;        // lane n: amax of element n's block
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+    for (int x = 0; x < 16; ++x) {
+        const float g = gacc[x] * ga;
+        const float u = uacc[x] * uc;
+        hv[x] = g / (1.0f + expf(-g)) * u;
+        const float am = row16_max(__builtin_fabsf(hv[x]));
+        amax_t = n == x ? am : amax_t;
+    }
+    const BlockScale bs = nvfp4_block_scale(amax_t, 1.0f);
+    {   // lane n writes the scale byte of element n's row
+        const int64_t row = m0 + 8 * (n >> 2) + 4 * h + (n & 3);
+        if ((vrow >> n) & 1u) a.inter_sf[row * (a.I >> 4) + (col >> 4)] = (uint8_t)bs.byte;
+    }
+#define MOE_CODE(x)                                                                        \
+    {                                                                                      \
+        const float r = row_bcast<x>(bs.r);                                                \
+        uint32_t b = r == 0.0f ? 0u : e2m1_encode(__fmul_rn(hv[x], r));                     \
+        b |= row_shl<1>(b) << 4;                                                           \
+        b |= row_shl<2>(b) << 8;                                                           \
+        b |= row_shl<4>(b) << 16;                                                          \
+        const int64_t row = m0 + 8 * (x >> 2) + 4 * h + (x & 3);                          \
+        if (((vrow >> x) & 1u) && (n & 7) == 0)                                            \
+            *reinterpret_cast<uint32_t*>(a.inter_codes + row * (a.I >> 1) + (col >> 1)) = b; \
+    }
+    MOE_CODE(0) MOE_CODE(1) MOE_CODE(2) MOE_CODE(3) MOE_CODE(4) MOE_CODE(5) MOE_CODE(6) MOE_CODE(7)
+    MOE_CODE(8) MOE_CODE(9) MOE_CODE(10) MOE_CODE(11) MOE_CODE(12) MOE_CODE(13) MOE_CODE(14) MOE_CODE(15)
+#undef MOE_CODE
+}
+
+// GEMM2 epilogue of one tile: bf16 rows m0 + [0, 32), columns col0 + [0, 32).
+__device__ __forceinline__ void bf16_tile(const floatx16& acc, float alpha, int lane, uint32_t vrow,
+                                          const ExpArgs& a, int m0, int col0) {
+    const int h = lane >> 5;
+    uint16_t* out = a.rows + (int64_t)m0 * a.rows_stride + col0 + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[s][j], acc[i][j], 0, 0, 0);
+    for (int x = 0; x < 16; ++x) {
+        const int m = 8 * (x >> 2) + 4 * h + (x & 3);
+        if ((vrow >> x) & 1u) out[(int64_t)m * a.rows_stride] = (uint16_t)f32_to_bf16(acc[x] * alpha);
+    }
+}
+
+// One wave's block: rows [row0, row0 + 32 RT) of expert e, column block cb
+// (computed but not stored when store is false: a column group past the end).
+// vrows[i]: bit x is set when the row this lane holds in element x of row tile
+// i's accumulators has a route.
+template <int MODE, int RT>
+__device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASrc& ap, int e, int row0, int cb,
+                                          bool store, int wave, int lane, const uint32_t (&vrows)[4]) {
+    const int h = lane >> 5, nn = lane & 31, n = lane & 15, hh = (lane >> 4) & 1;
+    const int K = MODE == 1 ? a.H : a.I;
+    const int NS = K / (64 * kStage);
+
+    BSrc p;
+    if (MODE == 1) {
+        const int pair0 = cb * kCT;                                 // 4 pairs: 64 intermediates
+        p.b = buffer_rsrc(a.w.w13 + e * a.w.w13_expert_stride_bytes + pair0 * a.w.w13_pair_stride_bytes);
+        p.bs = buffer_rsrc(a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + pair0 * a.w.w13_sf_pair_stride_bytes);
+        p.b_step = (int)a.w.w13_pair_stride_bytes;
+        p.bs_step = (int)a.w.w13_sf_pair_stride_bytes;
+        // column nn of tile 2t + g: pair 2t + nn / 16, half g, row n
+        p.b_off = hh * (uint32_t)p.b_step + (uint32_t)(2 * h * 16 + n) * 16;
+        p.bs_off = hh * (uint32_t)p.bs_step + 64 * h + 4 * (n >> 1);
+    } else {
+        const int pair0 = cb * kCT;                                 // 4 pairs: 128 output columns
+        p.b = buffer_rsrc(a.w.w2 + e * a.w.w2_expert_stride_bytes + pair0 * a.w.w2_pair_stride_bytes);
+        p.bs = buffer_rsrc(a.w.w2_sf + e * a.w.w2_sf_expert_stride_bytes + pair0 * a.w.w2_sf_pair_stride_bytes);
+        p.b_step = (int)a.w.w2_pair_stride_bytes;
+        p.bs_step = (int)a.w.w2_sf_pair_stride_bytes;
+        // column nn of tile j: pair j, half nn / 16, row n
+        p.b_off = (uint32_t)((2 * h * 16 + n) * 2 + hh) * 8;
+        p.bs_off = 64 * h + 4 * (n >> 1);
+    }
+    // byte selectors of the two block scales (block 2h from the first word,
+    // 2h + 1 from the second): for half g = 0, 1 (GEMM1), the lane's half (GEMM2)
+    uint32_t sel[2];
+    {
+        const uint32_t b0 = MODE == 1 ? 2 * (n & 1) : 2 * (n & 1) + hh;
+        sel[0] = 0x0c0c0000u | ((4 + b0) << 8) | b0;
+        sel[1] = sel[0] + 0x0101u;
+    }
+
+    floatx16 acc[RT][kCT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < kCT; ++j)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.0f;
+
+    // prologue: A stage 0, weights for k-tiles 0 .. kAhead - 1
+    a_stage_load(lds, ap, wave, 0);
+    BRaw<MODE> ring[kAhead];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) b_load(ring[d], p, d);
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAhead * BRaw<MODE>::kLoads));
+    __syncthreads();
+
+    // stage g (buffer g % 2): A stage g + 1 is copied into the other buffer
+    // (read by nobody since the last barrier; in the last stage a harmless copy
+    // of the last stage); k-tiles 4g .. 4g + 3 run, the weights of k-tile
+    // c + kAhead load into ring slot c % kAhead (past the end: the last k-tile
+    // again, unused); then every wave's copies have landed (vmcnt: only the
+    // weight loads issued after them may still be in flight) and a barrier
+    // publishes them.
+    const int KT = NS * kStage;
+    for (int g = 0; g < NS; ++g) {
+        const int buf = g & 1;
+        a_stage_load(lds, ap, wave, min(g + 1, NS - 1));
+        ARaw<RT> ar[2];
+        a_read(ar[0], lds, buf, 0, nn, h);
+#pragma unroll
+        for (int c = 0; c < kStage; ++c) {
+            if (c + 1 < kStage) a_read(ar[(c + 1) & 1], lds, buf, c + 1, nn, h);
+            tile_mfma(ar[c & 1], ring[c % kAhead], h, sel, acc);
+            b_load(ring[c % kAhead], p, min(kStage * g + c + kAhead, KT - 1));
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAhead * BRaw<MODE>::kLoads));
+        __syncthreads();
+    }
+
+    if (!store) return;
+    // epilogue, one 32 x 32 tile (GEMM1: a gate tile and its up tile) at a time
+    if (MODE == 1) {
+        const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
+#define MOE_EPI1(i, t)                                                                          \
+    if (RT > i) swiglu_quant_tile(acc[RT > i ? i : 0][2 * t], acc[RT > i ? i : 0][2 * t + 1], ga, uc, lane, \
+                                  vrows[i], a, row0 + 32 * i, 64 * cb + 32 * t)
+        MOE_EPI1(0, 0); MOE_EPI1(0, 1); MOE_EPI1(1, 0); MOE_EPI1(1, 1);
+        MOE_EPI1(2, 0); MOE_EPI1(2, 1); MOE_EPI1(3, 0); MOE_EPI1(3, 1);
+#undef MOE_EPI1
+    } else {
+        const float alpha = a.w.g2_alphas[e];
+#define MOE_EPI2(i, j) \
+    if (RT > i) bf16_tile(acc[RT > i ? i : 0][j], alpha, lane, vrows[i], a, row0 + 32 * i, 128 * cb + 32 * j)
+        MOE_EPI2(0, 0); MOE_EPI2(0, 1); MOE_EPI2(0, 2); MOE_EPI2(0, 3);
+        MOE_EPI2(1, 0); MOE_EPI2(1, 1); MOE_EPI2(1, 2); MOE_EPI2(1, 3);
+        MOE_EPI2(2, 0); MOE_EPI2(2, 1); MOE_EPI2(2, 2); MOE_EPI2(2, 3);
+        MOE_EPI2(3, 0); MOE_EPI2(3, 1); MOE_EPI2(3, 2); MOE_EPI2(3, 3);
+#undef MOE_EPI2
     }
 }
 
 template <int MODE>   // 1: GEMM1 + SwiGLU + requant, 2: GEMM2
-__global__ void __launch_bounds__(kTiledThreads) tiled_kernel(ExpArgs a, int nx, int ny) {
-    // the two LDS buffers are separate objects, so that the stores of the next
-    // k-tile provably do not alias the fragment reads of this one
-    __shared__ _Float16 Bs0[kTN][kLdsRow], Bs1[kTN][kLdsRow];
-    __shared__ int s_valid[kTM];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+__global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, int ncb) {
+    __shared__ ALds lds;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // XCD-aware block order: consecutive ids run on one XCD
-    const int per_xcd = (int)gridDim.x / kXcds;
-    const int id = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-    if (id >= nx * ny) return;
-    const int bx = id % nx, by = id / nx;
-    const int row0 = bx * kTM;
+    // work items: (routed row block, column group), row block major, in 8
+    // equal contiguous chunks, chunk x on XCD x
+    const int items = a.meta[a.L.num_tiles] * (a.tile_m / kBlockRows) * ncg;
+    const int per_xcd = (items + kXcds - 1) / kXcds;
+    const int slot = (int)(blockIdx.x / kXcds);
+    if (slot >= per_xcd) return;
+    const int item = (int)(blockIdx.x % kXcds) * per_xcd + slot;
+    if (item >= items) return;
+    const int bx = item / ncg, cg = item % ncg;
+    const int row0 = bx * kBlockRows;
     const int e = a.meta[a.L.tile_expert + row0 / a.tile_m];
-    if (e < 0 || e >= a.E_local) return;
+    if (e < 0 || e >= a.E_local) return;                     // uniform over the workgroup
+    int cb = cg * kWaves + wave;
+    const bool store = cb < ncb;
+    cb = min(cb, ncb - 1);
 
-    const int K = MODE == 1 ? a.H : a.I;
-    const int KT = K >> 6;
-    const int h = lane >> 5, rr = lane & 31;
-    const int bp = tid >> 6, slot = tid & 63;
-    const int pair = by * 4 + bp;
-    TilePtrs p;
+    const int nn = lane & 31, h = lane >> 5;
+    // the rows this lane holds in the accumulators: element x of row tile i is
+    // row 32 i + 8(x/4) + 4h + x%4
+    uint32_t vrows[4];
+    int rt = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = wm * 64 + i * 32 + rr;       // this lane's A row of row tile i
-        int tok = a.meta[a.L.perm2tok + row0 + m];
-        if (tok >= a.T) tok = -1;
-        if (wn == 0 && h == 0) s_valid[m] = tok >= 0;
+    for (int i = 0; i < 4; ++i) {
+        const int t = a.meta[a.L.perm2tok + row0 + 32 * i + nn];
+        const uint32_t m = (uint32_t)__ballot(t >= 0 && t < a.T);   // bit r: row 32 i + r
+        if (m != 0u) rt = i + 1;
+        uint32_t v = 0;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) v |= ((m >> (8 * (x >> 2) + 4 * h + (x & 3))) & 1u) << x;
+        vrows[i] = v;
+    }
+
+    // the A stage copies of this lane (rows without a route copy token row 0)
+    ASrc ap;
+    {
+        const int l8 = lane >> 3, c16 = lane & 7;
         if (MODE == 1) {
-            const int64_t t = tok >= 0 ? tok : 0;   // rows without a route read a stand-in row
-            p.ac[i] = a.a_codes + t * (a.H >> 1) + h * 16;
-            p.as[i] = a.a_sf + t * (a.H >> 4);
+            ap.a = buffer_desc(a.a_codes);
+            ap.as = buffer_desc(a.a_sf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 32 * q + 8 * wave + l8;
+                int t = a.meta[a.L.perm2tok + row0 + r];
+                t = (t >= 0 && t < a.T) ? t : 0;
+                ap.a_off[q] = (uint32_t)t * (uint32_t)(a.H >> 1) + ((c16 ^ (r & 7)) * 16);
+            }
+            int t = a.meta[a.L.perm2tok + row0 + ((64 * wave + lane) & (kBlockRows - 1))];
+            t = (t >= 0 && t < a.T) ? t : 0;
+            ap.as_off = (uint32_t)t * (uint32_t)(a.H >> 4);
         } else {
-            const int64_t row = row0 + m;
-            p.ac[i] = a.inter_codes + row * (a.I >> 1) + h * 16;
-            p.as[i] = a.inter_sf + row * (a.I >> 4);
-        }
-    }
-    if (MODE == 1) {
-        p.bc = a.w.w13 + e * a.w.w13_expert_stride_bytes + pair * a.w.w13_pair_stride_bytes + slot * 16;
-        p.bs = a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + pair * a.w.w13_sf_pair_stride_bytes + (slot >> 1) * 4;
-    } else {
-        p.bc = a.w.w2 + e * a.w.w2_expert_stride_bytes + pair * a.w.w2_pair_stride_bytes + slot * 16;
-        p.bs = a.w.w2_sf + e * a.w.w2_sf_expert_stride_bytes + pair * a.w.w2_sf_pair_stride_bytes + (slot >> 1) * 4;
-    }
-
-    floatx16 acc[2][2];
+            ap.a = buffer_desc(a.inter_codes + (int64_t)row0 * (a.I >> 1));
+            ap.as = buffer_desc(a.inter_sf + (int64_t)row0 * (a.I >> 4));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.0f;
-
-    // ring slot k % kAhead holds k-tile k; k-tile 0's B is decoded into buffer 0
-    TileRegs ring[kAhead];
-#pragma unroll
-    for (int d = 0; d < kAhead; ++d) tile_load(ring[d], p, d);
-    store_b(ring[0], Bs0, bp, slot);
-    __syncthreads();
-
-    // iteration c: MFMAs of k-tile c (A from ring slot c, B from buffer c & 1),
-    // B of k-tile c + 1 into the other buffer, ring slot c reloaded with k-tile
-    // c + kAhead. Branch-free, one scheduling region per k-tile: past the end
-    // the ring reloads the last k-tile (in bounds, unused) and the last
-    // iteration decodes into the buffer nobody reads again. KT % kAhead == 0.
-    for (int c0 = 0; c0 < KT; c0 += kAhead) {
-#pragma unroll
-        for (int d = 0; d < kAhead; ++d) {
-            const int c = c0 + d;
-            _Float16 (*Bcur)[kLdsRow] = (d & 1) ? Bs1 : Bs0;     // kAhead is even
-            _Float16 (*Bnxt)[kLdsRow] = (d & 1) ? Bs0 : Bs1;
-            tile_mfma(ring[d], Bcur, wn, lane, acc);
-            store_b(ring[(d + 1) % kAhead], Bnxt, bp, slot);
-            tile_load(ring[d], p, min(c + kAhead, KT - 1));
-            __syncthreads();
-        }
-    }
-
-    // epilogue: lane l of a 32 x 32 tile holds column l % 32, rows 8(x/4) + 4(l/32) + x%4
-    const int n = lane & 31;
-    if (MODE == 1) {
-        const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int pr = by * 4 + wn * 2 + j;          // pair = intermediates [16 pr, 16 pr + 16)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const int m = wm * 64 + i * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-                    const float g = acc[i][j][x] * ga;                       // gate: lanes n < 16
-                    const float u = __shfl_xor(acc[i][j][x], 16) * uc;       // up from lane n + 16
-                    const float hv = g / (1.0f + expf(-g)) * u;
-                    const float amax = wave_max16(__builtin_fabsf(hv));
-                    const BlockScale bsc = nvfp4_block_scale(amax, 1.0f);
-                    const uint32_t code = nvfp4_code(hv, bsc);
-                    uint32_t b = code | (__shfl_xor(code, 1) << 4);
-                    b = b | (__shfl_xor(b, 2) << 8);
-                    b = b | (__shfl_xor(b, 4) << 16);
-                    if (n < 16 && s_valid[m]) {
-                        const int64_t row = row0 + m;
-                        if ((n & 7) == 0)
-                            *reinterpret_cast<uint32_t*>(a.inter_codes + row * (a.I >> 1) + pr * 8 + (n >> 1)) = b;
-                        if (n == 0) a.inter_sf[row * (a.I >> 4) + pr] = (uint8_t)bsc.byte;
-                    }
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int r = 32 * q + 8 * wave + l8;
+                ap.a_off[q] = (uint32_t)r * (uint32_t)(a.I >> 1) + ((c16 ^ (r & 7)) * 16);
             }
+            ap.as_off = (uint32_t)((64 * wave + lane) & (kBlockRows - 1)) * (uint32_t)(a.I >> 4);
         }
-    } else {
-        const float alpha = a.w.g2_alphas[e];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = (by * 4 + wn * 2 + j) * 32 + n;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    const int m = wm * 64 + i * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-                    if (s_valid[m])
-                        a.rows[(int64_t)(row0 + m) * a.rows_stride + col] =
-                            (uint16_t)f32_to_bf16(acc[i][j][x] * alpha);
-                }
-            }
-        }
+    }
+
+    switch (rt) {
+        case 1: run_block<MODE, 1>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
+        case 2: run_block<MODE, 2>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
+        case 3: run_block<MODE, 3>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
+        case 4: run_block<MODE, 4>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
+        default: break;
     }
 }
 
-bool tiled_shape_ok(int H, int I, int tile_m) {
-    return tile_m % kTM == 0 && H % 256 == 0 && I % 256 == 0;
+bool tiled_shape_ok(int T, int H, int I, int tile_m) {
+    // whole row blocks; K = H and K = I in whole A stages (4 k-tiles); 32-bit
+    // per-lane offsets into the activation codes
+    return tile_m % kBlockRows == 0 && H % (64 * kStage) == 0 && I % (64 * kStage) == 0 &&
+           (int64_t)T * (H / 2) < ((int64_t)1 << 31);
 }
 
 void launch_tiled(const ExpArgs& a, hipStream_t s) {
-    const int nx = (int)(a.L.rows_max / kTM);
-    const int ny1 = 2 * a.I / kTN, ny2 = a.H / kTN;
-    auto grid = [](int blocks) { return dim3((unsigned)((blocks + kXcds - 1) / kXcds * kXcds)); };
-    hipLaunchKernelGGL(tiled_kernel<1>, grid(nx * ny1), dim3(kTiledThreads), 0, s, a, nx, ny1);
-    hipLaunchKernelGGL(tiled_kernel<2>, grid(nx * ny2), dim3(kTiledThreads), 0, s, a, nx, ny2);
+    // grids cover every row block that routing can fill; the kernels take the
+    // routed ones from the metadata
+    const int nx = (int)(a.L.rows_max / kBlockRows);
+    const int ncb1 = a.I / 64, ncb2 = a.H / 128;
+    const int ncg1 = (ncb1 + kWaves - 1) / kWaves, ncg2 = (ncb2 + kWaves - 1) / kWaves;
+    auto grid = [](int64_t items) { return dim3((unsigned)((items + kXcds - 1) / kXcds * kXcds)); };
+    hipLaunchKernelGGL(tiled_kernel<1>, grid((int64_t)nx * ncg1), dim3(64 * kWaves), 0, s, a, ncg1, ncb1);
+    hipLaunchKernelGGL(tiled_kernel<2>, grid((int64_t)nx * ncg2), dim3(64 * kWaves), 0, s, a, ncg2, ncb2);
 }
 
 }  // namespace moe

@@ -324,11 +324,12 @@ def test_layer_parity_full_oracle(inputs, name):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(256, 512, 256, 4, 2, 128), (200, 256, 512, 6, 3, 256),
-                                         (96, 1024, 256, 3, 2, 128)])
+                                         (96, 1024, 256, 3, 2, 128), (128, 768, 256, 2, 2, 128)])
 def test_layer_parity_tiled_path(T, H, I, E, K, m):
-    """Many routes per expert: the LDS-tiled MFMA kernels (every 128-row block
-    of one expert, padding rows in every expert's last block), whole layer
-    against the oracle."""
+    """Many routes per expert: the register-tiled MFMA kernels (every 128-row
+    block of one expert, padding rows in every expert's last block, 1 to 4
+    routed row tiles per block, column groups that do not fill a workgroup),
+    whole layer against the oracle."""
     from oracle.layer import intermediate_amax
     wl = W.Workload(f"tiled_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E, K=K, tile_m=m, seed=3)
     probe = W.make_inputs(wl, a2_gscale=1.0)
