@@ -88,6 +88,28 @@ __device__ __forceinline__ uint32_t nvfp4_code(float x, const BlockScale& bs) {
     return bs.r == 0.0f ? 0u : e2m1_encode(__fmul_rn(x, bs.r));
 }
 
+// The same for 8 consecutive elements, packed (element 0 in the low nibble).
+// The hardware pack conversion at scale 1 (no scaling) rounds to nearest, ties
+// to the even code, saturates at 6 and keeps the sign: it gives e2m1_encode's
+// code for every non-NaN f32 (checked over all 2^32 patterns on gfx950).
+// kNan: NaN products take code 0 as in e2m1_encode; without it the caller
+// guarantees that there are none.
+template <bool kNan>
+__device__ __forceinline__ uint32_t nvfp4_codes8(const float* v, const BlockScale& bs) {
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        p[k] = __fmul_rn(v[k], bs.r);
+        if (kNan) p[k] = p[k] == p[k] ? p[k] : 0.0f;
+    }
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[0], p[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[2], p[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[4], p[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[6], p[7], 1.0f, 3);
+    return bs.r == 0.0f ? 0u : w;
+}
+
 // ------------------------------------------------------------------ sigmoid
 // s(l) = 1 / (1 + exp(-l)). exp by Cody and Waite's range reduction
 // x = n ln2 + r, with ln2 split so that n * ln2_hi is exact, and the degree-7
@@ -142,11 +164,7 @@ __device__ __forceinline__ void quantize_block16(const uint16_t* __restrict__ x,
         amax = fmaxf(amax, fmaxf(__builtin_fabsf(v[2 * i]), __builtin_fabsf(v[2 * i + 1])));
     }
     const BlockScale bs = nvfp4_block_scale(amax, gscale);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= nvfp4_code(v[i], bs) << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= nvfp4_code(v[8 + i], bs) << (4 * i);
+    const uint32_t lo = nvfp4_codes8<true>(v, bs), hi = nvfp4_codes8<true>(v + 8, bs);
     *reinterpret_cast<uint2*>(codes + (int64_t)t * (H >> 1) + b * 8) = make_uint2(lo, hi);
     sf[(int64_t)t * (H >> 4) + b] = (uint8_t)bs.byte;
 }
@@ -221,6 +239,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     v += dpp_i<kDppRowBcast15, 0xA>(v);     // rows 1, 3 += last lane of rows 0, 2
     v += dpp_i<kDppRowBcast31, 0xC>(v);     // rows 2, 3 += lane 31
     return v;
+}
+
+// LDS writes of this wave are seen by its later LDS reads (a wave's LDS
+// operations complete in order); this keeps the compiler from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ float wave_max16(float v) {      // max over 16-lane rows

@@ -40,9 +40,11 @@
 //
 // GEMM1's columns are arranged so that a lane holds the gate and the up value of
 // the same intermediate in two accumulators (column tiles 2t and 2t + 1 take the
-// gate and the up halves of the same two pairs), so SwiGLU is lane-local; the
-// 16-wide amax and the packing of the codes use DPP moves within 16-lane rows.
-// GEMM2 writes bf16 rows. Rows without a route are not written.
+// gate and the up halves of the same two pairs), so SwiGLU is lane-local. The
+// epilogues then transpose each 32 x 32 tile through LDS so that a lane holds
+// one whole 16-wide block of one row: the requantization (amax, e4m3 scale,
+// codes) and the bf16 packing are lane-local and the stores are 8 or 32
+// contiguous bytes. Rows without a route are not written.
 #include "experts.hpp"
 
 namespace moe {
@@ -60,10 +62,19 @@ constexpr int kXcds = 8;
 constexpr int kARowBytes = 32 * kStage;     // codes of one row in a stage
 constexpr int kASfBytes = 4 * kStage;       // block scales of one row in a stage
 
+// s_waitcnt immediates (gfx9 encoding): at most n vector-memory loads in
+// flight, the other counters unconstrained; and-ed with lgkmcnt_zero(): no
+// LDS reads in flight either
+__host__ __device__ constexpr int vmcnt_at_most(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+__host__ __device__ constexpr int lgkmcnt_zero() { return ~(15 << 8); }
+
 // LDS: two A stages (codes, swizzled; block scales)
 struct ALds {
     uint8_t codes[2][kBlockRows * kARowBytes];
     uint8_t sf[2][kBlockRows * kASfBytes];
+    float slab[4][32 * 36];     // per wave: the epilogue's tile transpose (32 rows of 36)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
@@ -96,6 +107,28 @@ struct BSrc {
     uint32_t b_off, bs_off;         // per lane
     int b_step, bs_step;            // from one pair to the next
 };
+
+// The weight loads of a k-tile, in a fixed order (vmcnt drains in issue
+// order); b_load_nb leaves their placement among the MFMAs to the region's
+// schedule.
+template <int MODE>
+__device__ __forceinline__ void b_load_nb(BRaw<MODE>& r, const BSrc& p, int c) {
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) {
+        const int so = c * kSlotBytes + (MODE == 1 ? (j >> 1) * 2 : j) * p.b_step;
+        const int o = (int)p.b_off + (MODE == 1 ? (j & 1) * 8 : 0);
+        const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(p.b, o, so, 0);
+        const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(p.b, o + 256, so, 0);
+        r.b[j][0] = make_uint2(v0[0], v0[1]);
+        r.b[j][1] = make_uint2(v1[0], v1[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < BRaw<MODE>::kSW; ++t) {
+        const int so = c * kSlotSfBytes + t * (MODE == 1 ? 2 : 1) * p.bs_step;
+        r.bsf[t][0] = __builtin_amdgcn_raw_buffer_load_b32(p.bs, (int)p.bs_off, so, 0);
+        r.bsf[t][1] = __builtin_amdgcn_raw_buffer_load_b32(p.bs, (int)p.bs_off + 32, so, 0);
+    }
+}
 
 // The weight loads of a k-tile always issue in this order and by themselves
 // (prologue and loop alike), so that every use waits only for the loads issued
@@ -204,10 +237,10 @@ __device__ __forceinline__ void decode_step(const ARaw<RT>& ar, const BRaw<MODE>
     }
 }
 
+// The block scales of one k-tile as f16 pairs (block 2h, block 2h + 1).
 template <int MODE, int RT>
-__device__ __forceinline__ void tile_mfma(const ARaw<RT>& ar, const BRaw<MODE>& br, int h,
-                                          const uint32_t (&sel)[2], floatx16 (&acc)[RT][kCT]) {
-    half2v sa[RT], sb[kCT];
+__device__ __forceinline__ void tile_scales(const ARaw<RT>& ar, const BRaw<MODE>& br, int h,
+                                            const uint32_t (&sel)[2], half2v (&sa)[RT], half2v (&sb)[kCT]) {
 #pragma unroll
     for (int i = 0; i < RT; ++i) sa[i] = e4m3x2_to_f16(ar.asf[i] >> (16 * h));
 #pragma unroll
@@ -215,115 +248,129 @@ __device__ __forceinline__ void tile_mfma(const ARaw<RT>& ar, const BRaw<MODE>& 
         const int t = MODE == 1 ? j >> 1 : j;
         sb[j] = e4m3x2_to_f16(__builtin_amdgcn_perm(br.bsf[t][1], br.bsf[t][0], sel[MODE == 1 ? j & 1 : 0]));
     }
-    Frags<RT> f[2];
-    decode_step(ar, br, sa, sb, 0, f[0]);
+}
+
+// Keeps the decode of a step's fragments in the region where it is written:
+// without it the compiler sinks the VALU work next to its first use, into the
+// following region, where it no longer overlaps the MFMAs.
+template <int RT>
+__device__ __forceinline__ void pin(Frags<RT>& f) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) asm volatile("" : "+v"(f.a[i]));
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) asm volatile("" : "+v"(f.b[j]));
+}
+
+template <int RT>
+__device__ __forceinline__ void step_mfma(const Frags<RT>& f, floatx16 (&acc)[RT][kCT]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < kCT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling of one step region: each MFMA followed by its share of the VALU
+// decode work (and of the memory instructions, nmem of them in the region).
+template <int RT>
+__device__ __forceinline__ void interleave(int nmem) {
+    constexpr int kM = RT * kCT;
+    constexpr int kV = (8 * (RT + kCT) + 2 * (RT + kCT) + kM - 1) / kM;   // decode + scale work, rounded up
+#pragma unroll
+    for (int k = 0; k < kM; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);     // VALU
+        if (k < nmem) __builtin_amdgcn_sched_group_barrier(0x020 | 0x100, 1, 0);   // VMEM or DS read
+    }
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// The epilogues transpose each 32 x 32 tile through a private LDS slab of the
+// wave (rows padded to 36 floats: the 16-byte reads of 8 consecutive rows fall
+// in 8 different bank groups), so that lane L then holds the 16 consecutive
+// columns 16 (L % 2) + [0, 16) of row L / 2: one whole NVFP4 block (GEMM1) or
+// 32 contiguous bytes of a bf16 row (GEMM2), with all arithmetic lane-local.
+constexpr int kSlabStride = 36;
+
+// lane l holds column l % 32 of rows 8(x/4) + 4(l/32) + x%4 in element x
+__device__ __forceinline__ void slab_store(float* slab, const float (&v)[16], int lane) {
+    const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if (s < 3) decode_step(ar, br, sa, sb, s + 1, f[(s + 1) & 1]);
+    for (int x = 0; x < 16; ++x) slab[(8 * (x >> 2) + 4 * h + (x & 3)) * kSlabStride + n] = v[x];
+}
+
+__device__ __forceinline__ void slab_load_row16(const float* slab, float (&v)[16], int lane) {
+    const float4* src = reinterpret_cast<const float4*>(slab + (lane >> 1) * kSlabStride + 16 * (lane & 1));
 #pragma unroll
-        for (int i = 0; i < RT; ++i)
-#pragma unroll
-            for (int j = 0; j < kCT; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[s & 1].a[i], f[s & 1].b[j], acc[i][j], 0, 0, 0);
-        if (s < 3) {
-#pragma unroll
-            for (int k = 0; k < RT * kCT; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 8 * (RT + kCT) / (RT * kCT) + 1, 0);   // VALU
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 4; ++q) {
+        const float4 t = src[q];
+        v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
     }
 }
 
-// s_waitcnt immediate (gfx9 encoding): at most n vector-memory loads in
-// flight, the other counters unconstrained
-__host__ __device__ constexpr int vmcnt_at_most(int n) {
-    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-
-// max over 16-lane rows by DPP (exact in any order)
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
-    v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
-    v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp_f<kDppRowMirror>(v));
-    return v;
-}
-
-// lane i of each 16-lane row receives lane i + n (0 past the row's end)
-template <int n>
-__device__ __forceinline__ uint32_t row_shl(uint32_t v) {
-    return (uint32_t)dpp_i<0x100 + n>((int)v);
-}
-
-// lane i of each 16-lane row receives lane x of the row
-template <int x>
-__device__ __forceinline__ float row_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + x, 0xF, 0xF, false));
-}
-
-// GEMM1 epilogue of one gate tile and its up tile: rows m0 + [0, 32), lane l
-// holds intermediate col0 + l % 32 of rows m0 + 8(x/4) + 4(l/32) + x%4 in
-// element x. The 16 intermediates of a block sit in one 16-lane row, so the
-// amax is a row max; the block scale of element x is computed by lane x of the
-// row (one scale per lane, then broadcast back), and the codes are packed 8 to
-// a word by shifting within the row.
+// GEMM1 epilogue of one gate tile and its up tile (rows m0 + [0, 32),
+// intermediates col0 + [0, 32)): SwiGLU lane-local in the MFMA layout, then
+// per lane one block: amax, e4m3 scale, 16 codes, 8 code bytes and the scale
+// byte stored when its row has a route (bit r of vmask).
 __device__ __forceinline__ void swiglu_quant_tile(const floatx16& gacc, const floatx16& uacc, float ga, float uc,
-                                                  int lane, uint32_t vrow, const ExpArgs& a, int m0, int col0) {
-    const int n = lane & 15, h = lane >> 5;
-    const int col = col0 + (lane & 31);
+                                                  int lane, uint32_t vmask, const ExpArgs& a, int m0, int col0,
+                                                  float* slab) {
     float hv[16];
-    float amax_t = 0.0f;        // lane n: amax of element n's block
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
         const float g = gacc[x] * ga;
         const float u = uacc[x] * uc;
         hv[x] = g / (1.0f + expf(-g)) * u;
-        const float am = row16_max(__builtin_fabsf(hv[x]));
-        amax_t = n == x ? am : amax_t;
     }
-    const BlockScale bs = nvfp4_block_scale(amax_t, 1.0f);
-    {   // lane n writes the scale byte of element n's row
-        const int64_t row = m0 + 8 * (n >> 2) + 4 * h + (n & 3);
-        if ((vrow >> n) & 1u) a.inter_sf[row * (a.I >> 4) + (col >> 4)] = (uint8_t)bs.byte;
+    wave_lds_sync();            // the previous tile's reads are done
+    slab_store(slab, hv, lane);
+    wave_lds_sync();
+    float v[16];
+    slab_load_row16(slab, v, lane);
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, __builtin_fabsf(v[k]));
+    const BlockScale bs = nvfp4_block_scale(amax, 1.0f);
+    // finite values: products of finite accumulators
+    const uint32_t w0 = nvfp4_codes8<false>(v, bs), w1 = nvfp4_codes8<false>(v + 8, bs);
+    const int r = lane >> 1;
+    if ((vmask >> r) & 1u) {
+        const int64_t row = m0 + r;
+        const int col = col0 + 16 * (lane & 1);
+        *reinterpret_cast<uint2*>(a.inter_codes + row * (a.I >> 1) + (col >> 1)) = make_uint2(w0, w1);
+        a.inter_sf[row * (a.I >> 4) + (col >> 4)] = (uint8_t)bs.byte;
     }
-#define MOE_CODE(x)                                                                        \
-    {                                                                                      \
-        const float r = row_bcast<x>(bs.r);                                                \
-        uint32_t b = r == 0.0f ? 0u : e2m1_encode(__fmul_rn(hv[x], r));                     \
-        b |= row_shl<1>(b) << 4;                                                           \
-        b |= row_shl<2>(b) << 8;                                                           \
-        b |= row_shl<4>(b) << 16;                                                          \
-        const int64_t row = m0 + 8 * (x >> 2) + 4 * h + (x & 3);                          \
-        if (((vrow >> x) & 1u) && (n & 7) == 0)                                            \
-            *reinterpret_cast<uint32_t*>(a.inter_codes + row * (a.I >> 1) + (col >> 1)) = b; \
-    }
-    MOE_CODE(0) MOE_CODE(1) MOE_CODE(2) MOE_CODE(3) MOE_CODE(4) MOE_CODE(5) MOE_CODE(6) MOE_CODE(7)
-    MOE_CODE(8) MOE_CODE(9) MOE_CODE(10) MOE_CODE(11) MOE_CODE(12) MOE_CODE(13) MOE_CODE(14) MOE_CODE(15)
-#undef MOE_CODE
 }
 
-// GEMM2 epilogue of one tile: bf16 rows m0 + [0, 32), columns col0 + [0, 32).
-__device__ __forceinline__ void bf16_tile(const floatx16& acc, float alpha, int lane, uint32_t vrow,
-                                          const ExpArgs& a, int m0, int col0) {
-    const int h = lane >> 5;
-    uint16_t* out = a.rows + (int64_t)m0 * a.rows_stride + col0 + (lane & 31);
+// GEMM2 epilogue of one tile: bf16 rows m0 + [0, 32), columns col0 + [0, 32);
+// lane L stores 32 contiguous bytes of row L / 2.
+__device__ __forceinline__ void bf16_tile(const floatx16& acc, float alpha, int lane, uint32_t vmask,
+                                          const ExpArgs& a, int m0, int col0, float* slab) {
+    float o[16];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-        const int m = 8 * (x >> 2) + 4 * h + (x & 3);
-        if ((vrow >> x) & 1u) out[(int64_t)m * a.rows_stride] = (uint16_t)f32_to_bf16(acc[x] * alpha);
+    for (int x = 0; x < 16; ++x) o[x] = acc[x] * alpha;
+    wave_lds_sync();
+    slab_store(slab, o, lane);
+    wave_lds_sync();
+    float v[16];
+    slab_load_row16(slab, v, lane);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
+    const int r = lane >> 1;
+    if ((vmask >> r) & 1u) {
+        uint4* dst = reinterpret_cast<uint4*>(a.rows + (int64_t)(m0 + r) * a.rows_stride + col0 + 16 * (lane & 1));
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
 }
 
 // One wave's block: rows [row0, row0 + 32 RT) of expert e, column block cb
 // (computed but not stored when store is false: a column group past the end).
-// vrows[i]: bit x is set when the row this lane holds in element x of row tile
-// i's accumulators has a route.
+// vmask[i]: bit r is set when row 32 i + r of the block has a route.
 template <int MODE, int RT>
 __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASrc& ap, int e, int row0, int cb,
-                                          bool store, int wave, int lane, const uint32_t (&vrows)[4]) {
+                                          bool store, int wave, int lane, const uint32_t (&vmask)[4]) {
     const int h = lane >> 5, nn = lane & 31, n = lane & 15, hh = (lane >> 4) & 1;
     const int K = MODE == 1 ? a.H : a.I;
     const int NS = K / (64 * kStage);
@@ -365,35 +412,79 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
 #pragma unroll
             for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.0f;
 
-    // prologue: A stage 0, weights for k-tiles 0 .. kAhead - 1
-    a_stage_load(lds, ap, wave, 0);
-    BRaw<MODE> ring[kAhead];
-#pragma unroll
-    for (int d = 0; d < kAhead; ++d) b_load(ring[d], p, d);
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAhead * BRaw<MODE>::kLoads));
-    __syncthreads();
-
-    // stage g (buffer g % 2): A stage g + 1 is copied into the other buffer
-    // (read by nobody since the last barrier; in the last stage a harmless copy
-    // of the last stage); k-tiles 4g .. 4g + 3 run, the weights of k-tile
-    // c + kAhead load into ring slot c % kAhead (past the end: the last k-tile
-    // again, unused); then every wave's copies have landed (vmcnt: only the
-    // weight loads issued after them may still be in flight) and a barrier
-    // publishes them.
+    // Software pipeline over k-tiles c (A stage g = c / 4, buffer g % 2; ring
+    // slot c % 2 for the weights, c % 2 for the A fragments' raw data). Each
+    // k-tile is 4 step regions of RT x 4 MFMAs; while the MFMAs of step s run,
+    // the fragments of step s + 1 are decoded, and in the last region those of
+    // step 0 of k-tile c + 1, while the weights and A data of k-tile c + 2 load
+    // into the slots that k-tile c has finished with. A barrier in k-tile
+    // 4g + 2 publishes A stage g + 1 (copied since the barrier before) and
+    // frees buffer g % 2 for stage g + 2: every read of stage g was issued by
+    // then (the A data of k-tile c is read during k-tile c - 2).
     const int KT = NS * kStage;
-    for (int g = 0; g < NS; ++g) {
-        const int buf = g & 1;
-        a_stage_load(lds, ap, wave, min(g + 1, NS - 1));
-        ARaw<RT> ar[2];
-        a_read(ar[0], lds, buf, 0, nn, h);
+    static_assert(kAhead == 2, "ring slots c % 2");
+    // weight loads issued between one stage copy and the barrier that waits for it
+    constexpr int kAfterCopy = 4 * BRaw<MODE>::kLoads < 63 ? 4 * BRaw<MODE>::kLoads : 63;
+
+    a_stage_load(lds, ap, wave, 0);
+    a_stage_load(lds, ap, wave, min(1, NS - 1));
+    BRaw<MODE> ring[2];
+    b_load(ring[0], p, 0);
+    b_load(ring[1], p, min(1, KT - 1));
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    __syncthreads();
+    ARaw<RT> ar[2];
+    a_read(ar[0], lds, 0, 0, nn, h);
+    a_read(ar[1], lds, 0, min(1, KT - 1) % kStage, nn, h);
+    half2v sa[RT], sb[kCT];
+    Frags<RT> f[2];
+    tile_scales(ar[0], ring[0], h, sel, sa, sb);
+    decode_step(ar[0], ring[0], sa, sb, 0, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int c0 = 0; c0 < KT; c0 += kStage) {
+        const int g = c0 / kStage;
 #pragma unroll
-        for (int c = 0; c < kStage; ++c) {
-            if (c + 1 < kStage) a_read(ar[(c + 1) & 1], lds, buf, c + 1, nn, h);
-            tile_mfma(ar[c & 1], ring[c % kAhead], h, sel, acc);
-            b_load(ring[c % kAhead], p, min(kStage * g + c + kAhead, KT - 1));
+        for (int cc = 0; cc < kStage; ++cc) {
+            const int c = c0 + cc;
+            const int d = cc & 1;                      // c % 2
+            // step 0, 1, 2: decode the next step of this k-tile
+            decode_step(ar[d], ring[d], sa, sb, 1, f[1]);
+            step_mfma(f[0], acc);
+            pin(f[1]);
+            interleave<RT>(0);
+            decode_step(ar[d], ring[d], sa, sb, 2, f[0]);
+            step_mfma(f[1], acc);
+            pin(f[0]);
+            interleave<RT>(0);
+            if (cc == 2) {
+                // every wave: its reads of stage g done, its copy of stage g + 1 landed
+                __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAfterCopy) & lgkmcnt_zero());
+                __syncthreads();
+                if (g + 2 < NS) a_stage_load(lds, ap, wave, g + 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            decode_step(ar[d], ring[d], sa, sb, 3, f[1]);
+            step_mfma(f[0], acc);
+            pin(f[1]);
+            interleave<RT>(0);
+            // step 3: k-tile c + 1 step 0 decoded; k-tile c + 2 loads into slot d
+            {
+                const int cn = min(c + 2, KT - 1);
+                half2v sa1[RT], sb1[kCT];
+                tile_scales(ar[d ^ 1], ring[d ^ 1], h, sel, sa1, sb1);
+                decode_step(ar[d ^ 1], ring[d ^ 1], sa1, sb1, 0, f[0]);
+                b_load_nb(ring[d], p, cn);
+                a_read(ar[d], lds, (cn / kStage) & 1, cn % kStage, nn, h);
+                step_mfma(f[1], acc);
+                pin(f[0]);
+                interleave<RT>(BRaw<MODE>::kLoads + 2 * RT);
+#pragma unroll
+                for (int i = 0; i < RT; ++i) sa[i] = sa1[i];
+#pragma unroll
+                for (int j = 0; j < kCT; ++j) sb[j] = sb1[j];
+            }
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAhead * BRaw<MODE>::kLoads));
-        __syncthreads();
     }
 
     if (!store) return;
@@ -402,14 +493,15 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
         const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
 #define MOE_EPI1(i, t)                                                                          \
     if (RT > i) swiglu_quant_tile(acc[RT > i ? i : 0][2 * t], acc[RT > i ? i : 0][2 * t + 1], ga, uc, lane, \
-                                  vrows[i], a, row0 + 32 * i, 64 * cb + 32 * t)
+                                  vmask[i], a, row0 + 32 * i, 64 * cb + 32 * t, lds.slab[wave])
         MOE_EPI1(0, 0); MOE_EPI1(0, 1); MOE_EPI1(1, 0); MOE_EPI1(1, 1);
         MOE_EPI1(2, 0); MOE_EPI1(2, 1); MOE_EPI1(3, 0); MOE_EPI1(3, 1);
 #undef MOE_EPI1
     } else {
         const float alpha = a.w.g2_alphas[e];
 #define MOE_EPI2(i, j) \
-    if (RT > i) bf16_tile(acc[RT > i ? i : 0][j], alpha, lane, vrows[i], a, row0 + 32 * i, 128 * cb + 32 * j)
+    if (RT > i) bf16_tile(acc[RT > i ? i : 0][j], alpha, lane, vmask[i], a, row0 + 32 * i, 128 * cb + 32 * j, \
+                          lds.slab[wave])
         MOE_EPI2(0, 0); MOE_EPI2(0, 1); MOE_EPI2(0, 2); MOE_EPI2(0, 3);
         MOE_EPI2(1, 0); MOE_EPI2(1, 1); MOE_EPI2(1, 2); MOE_EPI2(1, 3);
         MOE_EPI2(2, 0); MOE_EPI2(2, 1); MOE_EPI2(2, 2); MOE_EPI2(2, 3);
@@ -441,19 +533,14 @@ __global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, 
     cb = min(cb, ncb - 1);
 
     const int nn = lane & 31, h = lane >> 5;
-    // the rows this lane holds in the accumulators: element x of row tile i is
-    // row 32 i + 8(x/4) + 4h + x%4
-    uint32_t vrows[4];
+    // bit r of vmask[i]: row 32 i + r of the block has a route
+    uint32_t vmask[4];
     int rt = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = a.meta[a.L.perm2tok + row0 + 32 * i + nn];
-        const uint32_t m = (uint32_t)__ballot(t >= 0 && t < a.T);   // bit r: row 32 i + r
-        if (m != 0u) rt = i + 1;
-        uint32_t v = 0;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) v |= ((m >> (8 * (x >> 2) + 4 * h + (x & 3))) & 1u) << x;
-        vrows[i] = v;
+        vmask[i] = (uint32_t)__ballot(t >= 0 && t < a.T);
+        if (vmask[i] != 0u) rt = i + 1;
     }
 
     // the A stage copies of this lane (rows without a route copy token row 0)
@@ -486,10 +573,10 @@ __global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, 
     }
 
     switch (rt) {
-        case 1: run_block<MODE, 1>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
-        case 2: run_block<MODE, 2>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
-        case 3: run_block<MODE, 3>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
-        case 4: run_block<MODE, 4>(a, lds, ap, e, row0, cb, store, wave, lane, vrows); break;
+        case 1: run_block<MODE, 1>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 2: run_block<MODE, 2>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 3: run_block<MODE, 3>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 4: run_block<MODE, 4>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
         default: break;
     }
 }

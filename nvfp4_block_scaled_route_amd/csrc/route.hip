@@ -226,13 +226,6 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e) {
     return match;
 }
 
-// LDS writes of this wave are seen by its later LDS reads (a wave's LDS
-// operations complete in order); this keeps the compiler from moving them.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The permutation metadata by one wave, with no workgroup barrier: routes in
 // chunks of 64 (one per lane), experts in runs of ceil(El / 64) per lane.
