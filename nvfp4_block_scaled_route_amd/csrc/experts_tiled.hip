@@ -25,8 +25,10 @@
 //     k-tiles of its 128 rows at a time (128 bytes of codes per row: whole cache
 //     lines) with direct global-to-LDS loads into a double-buffered LDS stage,
 //     one barrier per stage, and each wave reads its fragments from there. A
-//     row's 16-byte chunks are stored XOR-swizzled by the row's low 3 bits, so
-//     the fragment reads of 8 consecutive rows hit 8 different bank groups.
+//     row's 16-byte chunks are stored XOR-swizzled (chunk_swizzle), so that
+//     the 16-byte fragment reads of 16 consecutive rows -- one LDS cycle on
+//     gfx950, 64 banks -- hit 16 different bank groups (measured: the
+//     3-bit XOR alone left 4 conflict cycles per read).
 //     (Gathered straight into registers, every A load touched 32 cache lines
 //     for 32 bytes each, and the weight stream evicted them before the next
 //     k-tile could use the rest.)
@@ -70,6 +72,11 @@ __host__ __device__ constexpr int vmcnt_at_most(int n) {
 }
 __host__ __device__ constexpr int lgkmcnt_zero() { return ~(15 << 8); }
 
+// The LDS position (16-byte unit within its 128-byte row) of chunk k of row r:
+// rows r and r + 1 fall in different halves of the 64 banks, so the 8
+// positions of the rows r % 2 == const must differ over 16 consecutive rows.
+__device__ __forceinline__ int chunk_swizzle(int k, int r) { return k ^ (r & 7) ^ ((r >> 3) & 1); }
+
 // LDS: two A stages (codes, swizzled; block scales)
 struct ALds {
     uint8_t codes[2][kBlockRows * kARowBytes];
@@ -108,25 +115,29 @@ struct BSrc {
     int b_step, bs_step;            // from one pair to the next
 };
 
-// The weight loads of a k-tile, in a fixed order (vmcnt drains in issue
-// order); b_load_nb leaves their placement among the MFMAs to the region's
-// schedule.
+// The weight loads of a k-tile in three parts, each issued as soon as the
+// slot's previous contents are consumed (vmcnt drains in issue order, so a
+// wait for one part never waits for a part issued later): the scale words
+// (consumed by k-tile c - 1's last region), blocks 2h (words 0, 1: consumed
+// by step 1) and blocks 2h + 1 (words 2, 3: consumed by step 3).
 template <int MODE>
-__device__ __forceinline__ void b_load_nb(BRaw<MODE>& r, const BSrc& p, int c) {
-#pragma unroll
-    for (int j = 0; j < kCT; ++j) {
-        const int so = c * kSlotBytes + (MODE == 1 ? (j >> 1) * 2 : j) * p.b_step;
-        const int o = (int)p.b_off + (MODE == 1 ? (j & 1) * 8 : 0);
-        const u32x2 v0 = __builtin_amdgcn_raw_buffer_load_b64(p.b, o, so, 0);
-        const u32x2 v1 = __builtin_amdgcn_raw_buffer_load_b64(p.b, o + 256, so, 0);
-        r.b[j][0] = make_uint2(v0[0], v0[1]);
-        r.b[j][1] = make_uint2(v1[0], v1[1]);
-    }
+__device__ __forceinline__ void b_load_sf(BRaw<MODE>& r, const BSrc& p, int c) {
 #pragma unroll
     for (int t = 0; t < BRaw<MODE>::kSW; ++t) {
         const int so = c * kSlotSfBytes + t * (MODE == 1 ? 2 : 1) * p.bs_step;
         r.bsf[t][0] = __builtin_amdgcn_raw_buffer_load_b32(p.bs, (int)p.bs_off, so, 0);
         r.bsf[t][1] = __builtin_amdgcn_raw_buffer_load_b32(p.bs, (int)p.bs_off + 32, so, 0);
+    }
+}
+
+template <int MODE, int PART>
+__device__ __forceinline__ void b_load_half(BRaw<MODE>& r, const BSrc& p, int c) {
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) {
+        const int so = c * kSlotBytes + (MODE == 1 ? (j >> 1) * 2 : j) * p.b_step;
+        const int o = (int)p.b_off + (MODE == 1 ? (j & 1) * 8 : 0) + 256 * PART;
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(p.b, o, so, 0);
+        r.b[j][PART] = make_uint2(v[0], v[1]);
     }
 }
 
@@ -161,7 +172,8 @@ __device__ __forceinline__ void b_load(BRaw<MODE>& r, const BSrc& p, int c) {
 
 // The workgroup's copy of A stage g into LDS buffer g & 1. Codes: wave w's
 // load q covers rows 32q + 8w + [0, 8) (1 KB, lane l at byte 16 l): lane l
-// fetches chunk (l % 8) ^ (row % 8) of row 32q + 8w + l / 8. Scales: waves 0
+// fetches the chunk of row 32q + 8w + l / 8 whose swizzled position is l % 8
+// (the swizzle is an involution). Scales: waves 0
 // and 1, lane l fetches the 16 scale bytes of row 64w + l.
 //
 // The copies are written as inline assembly on purpose: the compiler treats
@@ -205,7 +217,7 @@ __device__ __forceinline__ void a_stage_load(ALds& lds, const ASrc& p, int wave,
 // bytes of chunk 2c + h of row 32 i + nn (swizzled), and its 4 block scales.
 template <int RT>
 __device__ __forceinline__ void a_read(ARaw<RT>& r, const ALds& lds, int buf, int c, int nn, int h) {
-    const int pos = ((2 * c + h) ^ (nn & 7)) * 16;
+    const int pos = chunk_swizzle(2 * c + h, nn) * 16;       // rows 32 i + nn: same low bits
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         r.a[i] = *reinterpret_cast<const uint4*>(&lds.codes[buf][(32 * i + nn) * kARowBytes + pos]);
@@ -308,6 +320,15 @@ __device__ __forceinline__ void slab_load_row16(const float* slab, float (&v)[16
     }
 }
 
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (each about
+// 1 ulp): a third of the instructions of the correctly rounded expf and
+// division, which dominate this epilogue. Saturates correctly: e^-g overflows
+// to inf for g < -88 (silu -> -0) and underflows to 0 for large g (silu -> g).
+__device__ __forceinline__ float silu_fast(float g) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // GEMM1 epilogue of one gate tile and its up tile (rows m0 + [0, 32),
 // intermediates col0 + [0, 32)): SwiGLU lane-local in the MFMA layout, then
 // per lane one block: amax, e4m3 scale, 16 codes, 8 code bytes and the scale
@@ -320,7 +341,7 @@ __device__ __forceinline__ void swiglu_quant_tile(const floatx16& gacc, const fl
     for (int x = 0; x < 16; ++x) {
         const float g = gacc[x] * ga;
         const float u = uacc[x] * uc;
-        hv[x] = g / (1.0f + expf(-g)) * u;
+        hv[x] = silu_fast(g) * u;
     }
     wave_lds_sync();            // the previous tile's reads are done
     slab_store(slab, hv, lane);
@@ -418,12 +439,15 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
     // the fragments of step s + 1 are decoded, and in the last region those of
     // step 0 of k-tile c + 1, while the weights and A data of k-tile c + 2 load
     // into the slots that k-tile c has finished with. A barrier in k-tile
-    // 4g + 2 publishes A stage g + 1 (copied since the barrier before) and
-    // frees buffer g % 2 for stage g + 2: every read of stage g was issued by
-    // then (the A data of k-tile c is read during k-tile c - 2).
+    // 4g + 2 publishes A stage g + 1 (copied during k-tile 4g - 2) and frees
+    // buffer g % 2 for stage g + 2: every read of stage g was issued by then
+    // (the A data of k-tile c is read during k-tile c - 2). Past the end the
+    // copies repeat the last stage into the free buffer.
     const int KT = NS * kStage;
     static_assert(kAhead == 2, "ring slots c % 2");
-    // weight loads issued between one stage copy and the barrier that waits for it
+    // weight loads issued between one stage copy (k-tile 4g - 2, step 3) and
+    // the barrier that waits for it (k-tile 4g + 2, after step 1): 4 k-tiles'
+    // worth
     constexpr int kAfterCopy = 4 * BRaw<MODE>::kLoads < 63 ? 4 * BRaw<MODE>::kLoads : 63;
 
     a_stage_load(lds, ap, wave, 0);
@@ -448,37 +472,45 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
         for (int cc = 0; cc < kStage; ++cc) {
             const int c = c0 + cc;
             const int d = cc & 1;                      // c % 2
-            // step 0, 1, 2: decode the next step of this k-tile
+            const int cn = min(c + 2, KT - 1);
+            // step 0, 1, 2: decode the next step of this k-tile; the weight
+            // scales, then blocks 2h, of k-tile c + 2 load into slot d
             decode_step(ar[d], ring[d], sa, sb, 1, f[1]);
+            b_load_sf(ring[d], p, cn);
             step_mfma(f[0], acc);
             pin(f[1]);
-            interleave<RT>(0);
+            interleave<RT>(2 * BRaw<MODE>::kSW);
             decode_step(ar[d], ring[d], sa, sb, 2, f[0]);
+            b_load_half<MODE, 0>(ring[d], p, cn);
             step_mfma(f[1], acc);
             pin(f[0]);
-            interleave<RT>(0);
+            interleave<RT>(kCT);
             if (cc == 2) {
                 // every wave: its reads of stage g done, its copy of stage g + 1 landed
                 __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAfterCopy) & lgkmcnt_zero());
                 __syncthreads();
-                if (g + 2 < NS) a_stage_load(lds, ap, wave, g + 2);
                 __builtin_amdgcn_sched_barrier(0);
             }
             decode_step(ar[d], ring[d], sa, sb, 3, f[1]);
             step_mfma(f[0], acc);
             pin(f[1]);
             interleave<RT>(0);
-            // step 3: k-tile c + 1 step 0 decoded; k-tile c + 2 loads into slot d
+            // step 3: k-tile c + 1 step 0 decoded; blocks 2h + 1 of k-tile c + 2
+            // load into slot d, its A data into A slot d
             {
-                const int cn = min(c + 2, KT - 1);
                 half2v sa1[RT], sb1[kCT];
                 tile_scales(ar[d ^ 1], ring[d ^ 1], h, sel, sa1, sb1);
                 decode_step(ar[d ^ 1], ring[d ^ 1], sa1, sb1, 0, f[0]);
-                b_load_nb(ring[d], p, cn);
+                // the copy of A stage g + 2 (into buffer g % 2, free since the
+                // barrier) issues with the weight loads it will be waited for
+                // with: vmcnt drains in order, so a copy issued earlier would
+                // hold up the next wait for the weights by a full memory latency
+                if (cc == 2) a_stage_load(lds, ap, wave, min(g + 2, NS - 1));
+                b_load_half<MODE, 1>(ring[d], p, cn);
                 a_read(ar[d], lds, (cn / kStage) & 1, cn % kStage, nn, h);
                 step_mfma(f[1], acc);
                 pin(f[0]);
-                interleave<RT>(BRaw<MODE>::kLoads + 2 * RT);
+                interleave<RT>(kCT + 2 * RT);
 #pragma unroll
                 for (int i = 0; i < RT; ++i) sa[i] = sa1[i];
 #pragma unroll
@@ -555,7 +587,7 @@ __global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, 
                 const int r = 32 * q + 8 * wave + l8;
                 int t = a.meta[a.L.perm2tok + row0 + r];
                 t = (t >= 0 && t < a.T) ? t : 0;
-                ap.a_off[q] = (uint32_t)t * (uint32_t)(a.H >> 1) + ((c16 ^ (r & 7)) * 16);
+                ap.a_off[q] = (uint32_t)t * (uint32_t)(a.H >> 1) + chunk_swizzle(c16, r) * 16;
             }
             int t = a.meta[a.L.perm2tok + row0 + ((64 * wave + lane) & (kBlockRows - 1))];
             t = (t >= 0 && t < a.T) ? t : 0;
@@ -566,7 +598,7 @@ __global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, 
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = 32 * q + 8 * wave + l8;
-                ap.a_off[q] = (uint32_t)r * (uint32_t)(a.I >> 1) + ((c16 ^ (r & 7)) * 16);
+                ap.a_off[q] = (uint32_t)r * (uint32_t)(a.I >> 1) + chunk_swizzle(c16, r) * 16;
             }
             ap.as_off = (uint32_t)((64 * wave + lane) & (kBlockRows - 1)) * (uint32_t)(a.I >> 4);
         }
