@@ -145,6 +145,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {   // nearest even
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two finite values -> packed bf16 (a in the low half) with the hardware pack
+// conversion: the same bits as f32_to_bf16 for every non-NaN f32 (checked over
+// all 2^32 patterns on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_pack(float a, float b) {
+    const floatx2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // ------------------------------------------------------------------ NVFP4 quantizer block
 // One 16-value block (row t, block b) of a bf16 matrix -> 8 code bytes and its
 // e4m3 scale byte, in nvfp4_quant's layout (row-major codes and scales).

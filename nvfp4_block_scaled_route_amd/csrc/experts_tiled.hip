@@ -81,7 +81,7 @@ __device__ __forceinline__ int chunk_swizzle(int k, int r) { return k ^ (r & 7) 
 struct ALds {
     uint8_t codes[2][kBlockRows * kARowBytes];
     uint8_t sf[2][kBlockRows * kASfBytes];
-    float slab[4][32 * 36];     // per wave: the epilogue's tile transpose (32 rows of 36)
+    float slab[4][2][32 * 36];  // per wave, two: the epilogue's tile transposes (32 rows of 36)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
@@ -304,6 +304,12 @@ __device__ __forceinline__ void interleave(int nmem) {
 // 32 contiguous bytes of a bf16 row (GEMM2), with all arithmetic lane-local.
 constexpr int kSlabStride = 36;
 
+// A wave's LDS instructions execute in order, so its later reads see its
+// earlier writes (those of other lanes included) without a wait; this only
+// keeps the compiler from reordering them. The two slabs of a wave alternate
+// between tiles, so a tile's writes never meet the previous tile's reads.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
 // lane l holds column l % 32 of rows 8(x/4) + 4(l/32) + x%4 in element x
 __device__ __forceinline__ void slab_store(float* slab, const float (&v)[16], int lane) {
     const int n = lane & 31, h = lane >> 5;
@@ -343,9 +349,8 @@ __device__ __forceinline__ void swiglu_quant_tile(const floatx16& gacc, const fl
         const float u = uacc[x] * uc;
         hv[x] = silu_fast(g) * u;
     }
-    wave_lds_sync();            // the previous tile's reads are done
     slab_store(slab, hv, lane);
-    wave_lds_sync();
+    lds_order();
     float v[16];
     slab_load_row16(slab, v, lane);
     float amax = 0.0f;
@@ -370,14 +375,13 @@ __device__ __forceinline__ void bf16_tile(const floatx16& acc, float alpha, int 
     float o[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) o[x] = acc[x] * alpha;
-    wave_lds_sync();
     slab_store(slab, o, lane);
-    wave_lds_sync();
+    lds_order();
     float v[16];
     slab_load_row16(slab, v, lane);
     uint32_t w[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
+    for (int k = 0; k < 8; ++k) w[k] = bf16x2_pack(v[2 * k], v[2 * k + 1]);   // finite sums
     const int r = lane >> 1;
     if ((vmask >> r) & 1u) {
         uint4* dst = reinterpret_cast<uint4*>(a.rows + (int64_t)(m0 + r) * a.rows_stride + col0 + 16 * (lane & 1));
@@ -525,7 +529,7 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
         const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
 #define MOE_EPI1(i, t)                                                                          \
     if (RT > i) swiglu_quant_tile(acc[RT > i ? i : 0][2 * t], acc[RT > i ? i : 0][2 * t + 1], ga, uc, lane, \
-                                  vmask[i], a, row0 + 32 * i, 64 * cb + 32 * t, lds.slab[wave])
+                                  vmask[i], a, row0 + 32 * i, 64 * cb + 32 * t, lds.slab[wave][t])
         MOE_EPI1(0, 0); MOE_EPI1(0, 1); MOE_EPI1(1, 0); MOE_EPI1(1, 1);
         MOE_EPI1(2, 0); MOE_EPI1(2, 1); MOE_EPI1(3, 0); MOE_EPI1(3, 1);
 #undef MOE_EPI1
@@ -533,7 +537,7 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
         const float alpha = a.w.g2_alphas[e];
 #define MOE_EPI2(i, j) \
     if (RT > i) bf16_tile(acc[RT > i ? i : 0][j], alpha, lane, vmask[i], a, row0 + 32 * i, 128 * cb + 32 * j, \
-                          lds.slab[wave])
+                          lds.slab[wave][j & 1])
         MOE_EPI2(0, 0); MOE_EPI2(0, 1); MOE_EPI2(0, 2); MOE_EPI2(0, 3);
         MOE_EPI2(1, 0); MOE_EPI2(1, 1); MOE_EPI2(1, 2); MOE_EPI2(1, 3);
         MOE_EPI2(2, 0); MOE_EPI2(2, 1); MOE_EPI2(2, 2); MOE_EPI2(2, 3);
