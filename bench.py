@@ -7,11 +7,13 @@ that the 256 MB Infinity Cache cannot hold them between uses, so weight bytes
 come from HBM (the cold-cache timing the flashinfer_ops page's tuning
 configuration asks for). Inputs are resident in HBM before timing starts.
 
-Prints one JSON line. ``roofline`` is the dominant kernel (the experts step)
-against HBM bandwidth: algorithmic bytes per launch (codes + e4m3 scales of the
+Prints one JSON line. ``roofline`` is the dominant kernel (the experts step),
+timed with HIP events on its own stream. With few routes per expert (decode)
+it is bound by HBM: algorithmic bytes per launch (codes + e4m3 scales of the
 experts that have a route, the NVFP4 input read once, the NVFP4 intermediate
-written and re-read, the GEMM2 rows written) over its average duration measured
-with HIP events on its own stream. ``cpu_baseline`` is the CPU oracle timed on a bounded
+written and re-read, the GEMM2 rows written) over its average duration. With
+many (prefill, the register-tiled kernels) it is bound by the matrix cores:
+the routed rows' GEMM FLOPs over the duration, against the f16 MFMA peak. ``cpu_baseline`` is the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload decode_b8]
@@ -40,6 +42,7 @@ def parse():
 
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense f16 matrix peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -58,6 +61,21 @@ def measured_traffic(workload: str):
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
     return float(rec["traffic_bytes"]) if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def mfma_bound(wl) -> bool:
+    """Whether moe_experts_fwd takes the register-tiled MFMA kernels (many routes
+    per expert; the library's dispatch rule): then the step is bound by the
+    matrix cores and its roofline is f16 MFMA throughput."""
+    I_part = wl.I // wl.tp
+    return (wl.tile_m % 128 == 0 and wl.H % 256 == 0 and I_part % 256 == 0
+            and wl.T * (wl.H // 2) < 2 ** 31 and wl.T * wl.K >= 32 * wl.E)
+
+
+def algorithmic_flops(wl, counts) -> float:
+    """Matrix FLOPs of the routed rows: GEMM1 (2I x H) and GEMM2 (H x I) per route."""
+    routes = int(counts.sum())
+    return 2.0 * routes * (2 * wl.I * wl.H + wl.H * wl.I)
 
 
 def algorithmic_bytes(wl, counts) -> dict:
@@ -185,13 +203,25 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
                    "tp": wl.tp, "tile_m": wl.tile_m, "weight_copies": copies},
-        "roofline": {"bound": "hbm", "kernel": "moe_experts_fwd (gemm1_kernel: GEMM1+SwiGLU+requant, gemm2_kernel)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
-                     "experts_touched": ab["touched"], "kernel_ms": k_ms},
     }
+    if mfma_bound(wl):
+        flops = algorithmic_flops(wl, counts)
+        tflops = flops / (k_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "moe_experts_fwd (tiled_kernel<1>: GEMM1+SwiGLU+requant, "
+                                                      "tiled_kernel<2>: GEMM2)",
+                           "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
+                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                           "algorithmic_flops": flops, "algorithmic_bytes": ab["total"], "hbm_gbs": achieved,
+                           "kernel_ms": k_ms}
+    else:
+        out["roofline"] = {"bound": "hbm", "kernel": "moe_experts_fwd (gemm1_kernel: GEMM1+SwiGLU+requant, "
+                                                     "gemm2_kernel)",
+                           "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
+                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                           "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
+                           "experts_touched": ab["touched"], "kernel_ms": k_ms}
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
