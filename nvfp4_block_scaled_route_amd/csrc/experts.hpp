@@ -21,9 +21,9 @@ struct ExpArgs {
 
 constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;   // converted layout: per pair and k-tile
 
-// The tiled path: 128-row blocks of one expert (tile_m % 128 == 0), k-tiles in
-// pairs and whole column blocks (H % 128 == 0, I % 128 == 0), activation code
-// offsets below 2^31 bytes.
+// The tiled path: 128-row blocks of one expert (tile_m % 128 == 0), K in whole
+// 4-k-tile stages (H % 256 == 0, I % 256 == 0), activation code offsets below
+// 2^31 bytes.
 bool tiled_shape_ok(int T, int H, int I, int tile_m);
 void launch_tiled(const ExpArgs& a, hipStream_t s);
 
