@@ -32,6 +32,13 @@
 // metadata entry, which is -1 for every tile past the routed ones, so those
 // waves exit at once. The expert kernels never read expert counts: a 16-row
 // tile's padding rows have token -1 and are neither read nor written.
+//
+// Where the shape allows, a workgroup's four waves take four units of one tile
+// and share one copy of the tile's 16 activation rows in LDS, brought in by
+// direct-to-LDS loads issued ahead of the weight pipeline: a wave's k-tile then
+// requests only its 16-byte weight slot and 2 scale bytes from memory, not 16
+// rows x (8 code bytes + 1 scale byte) spread over 32 cache lines, which leaves
+// a CU's memory requests to the weights.
 #include "experts.hpp"
 
 namespace moe {
@@ -62,9 +69,13 @@ struct Streams {
     const uint8_t* as;
 };
 
-__device__ __forceinline__ void load_stage(Stage& st, const Streams& p, int c) {
+__device__ __forceinline__ void load_w(Stage& st, const Streams& p, int c) {
     st.w = *reinterpret_cast<const uint4*>(p.wc + (int64_t)c * kSlotBytes);
     st.wsf = *reinterpret_cast<const uint16_t*>(p.ws + (int64_t)c * kSlotSfBytes);
+}
+
+__device__ __forceinline__ void load_stage(Stage& st, const Streams& p, int c) {
+    load_w(st, p, c);
     st.a = *reinterpret_cast<const uint2*>(p.ac + c * 32);
     st.asf = p.as[c * 4];
 }
@@ -138,26 +149,10 @@ __device__ __forceinline__ RowTile row_tile(const ExpArgs& a, int sub, int n) {
     return r;
 }
 
-// ---------------------------------------------------------------- GEMM1 + SwiGLU + requant
-template <int D>
-__global__ void __launch_bounds__(kThreads) gemm1_kernel(ExpArgs a) {
-    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-    const uint32_t unit = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t n1 = a.I >> 4;
-    const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
-    const RowTile rt = row_tile(a, sub, n);
-    if (rt.e < 0) return;
-    const int e = rt.e;
-    Streams p;
-    p.wc = a.w.w13 + e * a.w.w13_expert_stride_bytes + j * a.w.w13_pair_stride_bytes + lane * 16;
-    p.ws = a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + j * a.w.w13_sf_pair_stride_bytes + lane * 2;
-    const int64_t tok = rt.tok >= 0 ? rt.tok : 0;
-    p.ac = a.a_codes + tok * (a.H >> 1) + q * 8;
-    p.as = a.a_sf + tok * (a.H >> 4) + q;
-    floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
-    stream_unit<D>(p, a.H >> 6, acc_g, acc_u);
-
-    // lane (q, n) holds rows 4q + i of intermediate 16j + n
+// ---------------------------------------------------------------- epilogues
+// GEMM1: lane (q, n) holds rows 4q + i of intermediate 16j + n.
+__device__ __forceinline__ void gemm1_epilogue(const ExpArgs& a, const RowTile& rt, int e, int j, int n, int q,
+                                               const floatx4& acc_g, const floatx4& acc_u) {
     const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -180,7 +175,44 @@ __global__ void __launch_bounds__(kThreads) gemm1_kernel(ExpArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- GEMM2
+// GEMM2: lane (q, n) holds rows 4q + i of output columns 32c + n and 32c + 16 + n.
+__device__ __forceinline__ void gemm2_epilogue(const ExpArgs& a, const RowTile& rt, int e, int c, int n, int q,
+                                               const floatx4& acc0, const floatx4& acc1) {
+    const float alpha = a.w.g2_alphas[e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;
+        if ((rt.vmask >> m) & 1u) {
+            uint16_t* out = a.rows + (int64_t)(rt.row0 + m) * a.rows_stride + c * 32 + n;
+            out[0] = (uint16_t)f32_to_bf16(acc0[i] * alpha);
+            out[16] = (uint16_t)f32_to_bf16(acc1[i] * alpha);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- one unit per wave
+// Activation rows read by every wave from global memory: the kernels for the
+// shapes the workgroup kernels below do not take.
+template <int D>
+__global__ void __launch_bounds__(kThreads) gemm1_kernel(ExpArgs a) {
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const uint32_t unit = blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n1 = a.I >> 4;
+    const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
+    const RowTile rt = row_tile(a, sub, n);
+    if (rt.e < 0) return;
+    const int e = rt.e;
+    Streams p;
+    p.wc = a.w.w13 + e * a.w.w13_expert_stride_bytes + j * a.w.w13_pair_stride_bytes + lane * 16;
+    p.ws = a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + j * a.w.w13_sf_pair_stride_bytes + lane * 2;
+    const int64_t tok = rt.tok >= 0 ? rt.tok : 0;
+    p.ac = a.a_codes + tok * (a.H >> 1) + q * 8;
+    p.as = a.a_sf + tok * (a.H >> 4) + q;
+    floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
+    stream_unit<D>(p, a.H >> 6, acc_g, acc_u);
+    gemm1_epilogue(a, rt, e, j, n, q, acc_g, acc_u);
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) gemm2_kernel(ExpArgs a) {
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
@@ -198,18 +230,139 @@ __global__ void __launch_bounds__(kThreads) gemm2_kernel(ExpArgs a) {
     p.as = a.inter_sf + row * (a.I >> 4) + q;
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     stream_unit<D>(p, a.I >> 6, acc0, acc1);
+    gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+}
 
-    // lane (q, n) holds rows 4q + i of output columns 32c + n and 32c + 16 + n
-    const float alpha = a.w.g2_alphas[e];
+// ---------------------------------------------------------------- four units per workgroup
+// The tile's 16 activation rows (K values each: K/2 code bytes, K/16 scale
+// bytes) in LDS as 16-byte chunks, chunk-major: code chunk k of row r at
+// 16 (16 k + r), scale chunk k of row r at 16 (K/2 + 16 k + r). A k-tile's
+// reads (row n, 8 code bytes at 32c + 8q and scale byte 4c + q for lane
+// (q, n)) then fall on distinct banks.
+__host__ __device__ constexpr int tile_lds_bytes(int K) { return 8 * K + K; }
+
+// Issue the copy of the tile: chunk x of each region goes to LDS unit x, so
+// one direct-to-LDS load moves 64 consecutive units, lane l taking row l % 16
+// (a lane of a 16-row MFMA tile, whose row base `cbase`/`sbase` it holds).
+// The four waves take every fourth load.
+__device__ __forceinline__ void copy_tile(uint8_t* lds, int K, int wave, int lane, u32x4 crsrc, uint32_t cbase,
+                                          u32x4 srsrc, uint32_t sbase) {
+    const int code_chunks = K >> 1, sf_chunks = K >> 4;   // 16 rows x (K/32) and 16 rows x (K/256)
+    const uint32_t l0 = lds_addr(lds);
+    const uint32_t k = (uint32_t)(lane >> 4);
+    for (int x0 = wave * 64; x0 < code_chunks; x0 += kThreads)
+        lds_copy16(crsrc, __builtin_amdgcn_readfirstlane(l0 + x0 * 16), cbase + ((x0 >> 4) + k) * 16, 0);
+    for (int x0 = wave * 64; x0 < sf_chunks; x0 += kThreads)
+        if (x0 + lane < sf_chunks)
+            lds_copy16(srsrc, __builtin_amdgcn_readfirstlane(l0 + (code_chunks + x0) * 16),
+                       sbase + ((x0 >> 4) + k) * 16, 0);
+}
+
+// A wave's loads of the copy issued by copy_tile: wait for those with all D
+// weight k-tiles (2 loads each) requested after them still in flight, then
+// for the other waves' copies.
+template <int D>
+__device__ __forceinline__ void copy_wait() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(2 * D));
+    __syncthreads();
+}
+
+// Only the weights go through the D-deep register pipeline; the activation
+// of k-tile c comes from the LDS copy (lc, ls: the lane's row and position
+// in the chunk-major layout), read one k-tile ahead. As in stream_unit, the
+// steady-state loop has no branches, so the compiler's waits count the
+// pipeline exactly.
+__device__ __forceinline__ void lds_act(uint2& a, uint32_t& s, const uint8_t* lc, const uint8_t* ls, int c) {
+    a = *reinterpret_cast<const uint2*>(lc + c * 512);   // code chunk 2c + q/2 of the lane's row
+    s = ls[(c >> 2) * 256 + (c & 3) * 4];                  // byte 4c + q: scale chunk c/4
+}
+
+template <int D>
+__device__ __forceinline__ void stream_lds(const Streams& p, const uint8_t* lc, const uint8_t* ls, int KT,
+                                           floatx4& acc0, floatx4& acc1) {
+    Stage st[D];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;
-        if ((rt.vmask >> m) & 1u) {
-            uint16_t* out = a.rows + (int64_t)(rt.row0 + m) * a.rows_stride + c * 32 + n;
-            out[0] = (uint16_t)f32_to_bf16(acc0[i] * alpha);
-            out[16] = (uint16_t)f32_to_bf16(acc1[i] * alpha);
+    for (int d = 0; d < D; ++d) {
+        load_w(st[d], p, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    copy_wait<D>();
+    uint2 na;
+    uint32_t ns;
+    lds_act(na, ns, lc, ls, 0);
+    int c0 = 0;
+    for (; c0 + D < KT; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            st[d].a = na;
+            st[d].asf = ns;
+            lds_act(na, ns, lc, ls, c0 + d + 1);
+            use_stage(st[d], acc0, acc1);
+            load_w(st[d], p, c0 + D + d);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        st[d].a = na;
+        st[d].asf = ns;
+        if (d + 1 < D) lds_act(na, ns, lc, ls, c0 + d + 1);
+        use_stage(st[d], acc0, acc1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// GEMM1 units 4b .. 4b + 3: intermediate pairs of one tile (I/16 % 4 == 0).
+// The 16 activation rows are gathered by token; a padding row reads token 0's
+// row, which only feeds an output row that is never written.
+template <int D>
+__global__ void __launch_bounds__(kThreads) gemm1_wg_kernel(ExpArgs a) {
+    extern __shared__ __align__(16) uint8_t tile_lds[];
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n1 = a.I >> 4;
+    const uint32_t unit = blockIdx.x * kWavesPerBlock + wave;
+    const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
+    const RowTile rt = row_tile(a, sub, n);   // one tile for the whole workgroup
+    if (rt.e < 0) return;
+    const int e = rt.e;
+    const uint32_t tok = rt.tok >= 0 ? (uint32_t)rt.tok : 0u;
+    copy_tile(tile_lds, a.H, wave, lane, buffer_desc(a.a_codes), tok * (uint32_t)(a.H >> 1), buffer_desc(a.a_sf),
+              tok * (uint32_t)(a.H >> 4));
+    Streams p;
+    p.wc = a.w.w13 + e * a.w.w13_expert_stride_bytes + j * a.w.w13_pair_stride_bytes + lane * 16;
+    p.ws = a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + j * a.w.w13_sf_pair_stride_bytes + lane * 2;
+    const uint8_t* lc = tile_lds + ((q >> 1) * 16 + n) * 16 + (q & 1) * 8;
+    const uint8_t* ls = tile_lds + (a.H >> 1) * 16 + n * 16 + q;
+    floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
+    stream_lds<D>(p, lc, ls, a.H >> 6, acc_g, acc_u);
+    gemm1_epilogue(a, rt, e, j, n, q, acc_g, acc_u);
+}
+
+// GEMM2 units 4b .. 4b + 3: output pairs of one tile (H/32 % 4 == 0); the
+// tile's 16 intermediate rows are consecutive.
+template <int D>
+__global__ void __launch_bounds__(kThreads) gemm2_wg_kernel(ExpArgs a) {
+    extern __shared__ __align__(16) uint8_t tile_lds[];
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n2 = a.H >> 5;
+    const uint32_t unit = blockIdx.x * kWavesPerBlock + wave;
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
+    const RowTile rt = row_tile(a, sub, n);   // one tile for the whole workgroup
+    if (rt.e < 0) return;
+    const int e = rt.e;
+    const uint32_t row = (uint32_t)(rt.row0 + n);
+    copy_tile(tile_lds, a.I, wave, lane, buffer_desc(a.inter_codes), row * (uint32_t)(a.I >> 1),
+              buffer_desc(a.inter_sf), row * (uint32_t)(a.I >> 4));
+    Streams p;
+    p.wc = a.w.w2 + e * a.w.w2_expert_stride_bytes + c * a.w.w2_pair_stride_bytes + lane * 16;
+    p.ws = a.w.w2_sf + e * a.w.w2_sf_expert_stride_bytes + c * a.w.w2_sf_pair_stride_bytes + lane * 2;
+    const uint8_t* lc = tile_lds + ((q >> 1) * 16 + n) * 16 + (q & 1) * 8;
+    const uint8_t* ls = tile_lds + (a.I >> 1) * 16 + n * 16 + q;
+    floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    stream_lds<D>(p, lc, ls, a.I >> 6, acc0, acc1);
+    gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
 }
 
 // ---------------------------------------------------------------- launch
@@ -220,19 +373,24 @@ static int pipeline_depth(int kt) {
     return 1;
 }
 
-#define MOE_LAUNCH_DEPTHS(kernel)                                                         \
-    static void launch_##kernel(int d, dim3 grid, hipStream_t s, const ExpArgs& a) {      \
-        switch (d) {                                                                      \
-            case 8: hipLaunchKernelGGL(kernel<8>, grid, dim3(kThreads), 0, s, a); break; \
-            case 6: hipLaunchKernelGGL(kernel<6>, grid, dim3(kThreads), 0, s, a); break; \
-            case 4: hipLaunchKernelGGL(kernel<4>, grid, dim3(kThreads), 0, s, a); break; \
-            case 3: hipLaunchKernelGGL(kernel<3>, grid, dim3(kThreads), 0, s, a); break; \
-            case 2: hipLaunchKernelGGL(kernel<2>, grid, dim3(kThreads), 0, s, a); break; \
-            default: hipLaunchKernelGGL(kernel<1>, grid, dim3(kThreads), 0, s, a); break; \
-        }                                                                                 \
+// The workgroup kernels' LDS: at most 40 KB keeps 4 workgroups on a CU.
+constexpr int kMaxTileLds = 40 * 1024;
+
+#define MOE_LAUNCH_DEPTHS(kernel)                                                                  \
+    static void launch_##kernel(int d, dim3 grid, unsigned lds, hipStream_t s, const ExpArgs& a) { \
+        switch (d) {                                                                               \
+            case 8: hipLaunchKernelGGL(kernel<8>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 6: hipLaunchKernelGGL(kernel<6>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 4: hipLaunchKernelGGL(kernel<4>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 3: hipLaunchKernelGGL(kernel<3>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 2: hipLaunchKernelGGL(kernel<2>, grid, dim3(kThreads), lds, s, a); break;        \
+            default: hipLaunchKernelGGL(kernel<1>, grid, dim3(kThreads), lds, s, a); break;       \
+        }                                                                                          \
     }
 MOE_LAUNCH_DEPTHS(gemm1_kernel)
 MOE_LAUNCH_DEPTHS(gemm2_kernel)
+MOE_LAUNCH_DEPTHS(gemm1_wg_kernel)
+MOE_LAUNCH_DEPTHS(gemm2_wg_kernel)
 #undef MOE_LAUNCH_DEPTHS
 
 }  // namespace moe
@@ -294,9 +452,19 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
         launch_tiled(args, s);
         return check_launch("moe_experts_fwd (tiled)");
     }
-    launch_gemm1_kernel(pipeline_depth((int)kt1), dim3((unsigned)grid1), s, args);
+    // Workgroups of four units sharing one LDS copy of their tile's activation
+    // where the shape allows: whole 16-byte scale chunks (K % 256 == 0), at
+    // most 40 KB of LDS, GEMM2's four output pairs in one tile (H % 128 == 0),
+    // 32-bit row offsets into the activation.
+    const int d1 = pipeline_depth((int)kt1), d2 = pipeline_depth((int)kt2);
+    const bool wg1 = H % 256 == 0 && tile_lds_bytes(H) <= kMaxTileLds && (int64_t)T * (H / 2) < (1ll << 31);
+    const bool wg2 = I % 256 == 0 && H % 128 == 0 && tile_lds_bytes(I) <= kMaxTileLds &&
+                     args.L.rows_max * (I / 2) < (1ll << 31);
+    if (wg1) launch_gemm1_wg_kernel(d1, dim3((unsigned)grid1), (unsigned)tile_lds_bytes(H), s, args);
+    else launch_gemm1_kernel(d1, dim3((unsigned)grid1), 0, s, args);
     int rc = check_launch("moe_experts_fwd (GEMM1)");
     if (rc) return rc;
-    launch_gemm2_kernel(pipeline_depth((int)kt2), dim3((unsigned)grid2), s, args);
+    if (wg2) launch_gemm2_wg_kernel(d2, dim3((unsigned)grid2), (unsigned)tile_lds_bytes(I), s, args);
+    else launch_gemm2_kernel(d2, dim3((unsigned)grid2), 0, s, args);
     return check_launch("moe_experts_fwd (GEMM2)");
 }

@@ -21,6 +21,34 @@ struct ExpArgs {
 
 constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;   // converted layout: per pair and k-tile
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediates (gfx9 encoding): at most n vector-memory loads in
+// flight, the other counters unconstrained; and-ed with lgkmcnt_zero(): no
+// LDS reads in flight either
+__host__ __device__ constexpr int vmcnt_at_most(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+__host__ __device__ constexpr int lgkmcnt_zero() { return ~(15 << 8); }
+
+__device__ __forceinline__ u32x4 buffer_desc(const void* base) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    // raw buffer (stride 0) with no range limit; gfx9 data-format word
+    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS load: lane l's 16 bytes at base + voff + soff land at LDS
+// address lds + 16 l. The compiler does not see it: a wait for it is the
+// caller's (vmcnt, which it shares with the loads issued around it).
+__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
 // The tiled path: 128-row blocks of one expert (tile_m % 128 == 0), K in whole
 // 4-k-tile stages (H % 256 == 0, I % 256 == 0), activation code offsets below
 // 2^31 bytes.

@@ -52,7 +52,6 @@
 namespace moe {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kCT = 4;                      // 32-column MFMA tiles per wave
@@ -64,13 +63,6 @@ constexpr int kXcds = 8;
 constexpr int kARowBytes = 32 * kStage;     // codes of one row in a stage
 constexpr int kASfBytes = 4 * kStage;       // block scales of one row in a stage
 
-// s_waitcnt immediates (gfx9 encoding): at most n vector-memory loads in
-// flight, the other counters unconstrained; and-ed with lgkmcnt_zero(): no
-// LDS reads in flight either
-__host__ __device__ constexpr int vmcnt_at_most(int n) {
-    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-__host__ __device__ constexpr int lgkmcnt_zero() { return ~(15 << 8); }
 
 // The LDS position (16-byte unit within its 128-byte row) of chunk k of row r:
 // rows r and r + 1 fall in different halves of the 64 banks, so the 8
@@ -187,20 +179,6 @@ struct ASrc {
     uint32_t as_off;                // per lane: row start (waves 0, 1)
 };
 
-__device__ __forceinline__ u32x4 buffer_desc(const void* base) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    // raw buffer (stride 0) with no range limit; gfx9 data-format word
-    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
 
 __device__ __forceinline__ void a_stage_load(ALds& lds, const ASrc& p, int wave, int g) {
     const int buf = g & 1;

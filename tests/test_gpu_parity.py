@@ -341,6 +341,23 @@ def test_layer_parity_tiled_path(T, H, I, E, K, m):
     _compare_layer(res, ref, wl.name)
 
 
+@pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 16),
+                                         (7, 512, 768, 16, 4, 32), (3, 1024, 512, 4, 2, 16)])
+def test_layer_parity_streaming_kernel_choices(T, H, I, E, K, m):
+    """Few routes per expert, shapes that take each expert kernel: GEMM1 on the
+    one-wave kernel (H % 256 != 0) or on the workgroup kernel with the LDS copy
+    of the activation, GEMM2 likewise (I % 256 and H % 128), pipeline depths
+    5 (H/64), 3, 6 (I/64 = 12) and 8."""
+    from oracle.layer import intermediate_amax
+    wl = W.Workload(f"stream_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E, K=K, tile_m=m, seed=5)
+    probe = W.make_inputs(wl, a2_gscale=1.0)
+    a2 = float(np.float32(2688.0 / intermediate_amax(probe)))
+    inp = W.make_inputs(wl, a2_gscale=a2)
+    res = run_layer(inp)
+    ref = o_layer(inp)
+    _compare_layer(res, ref, wl.name)
+
+
 @pytest.mark.parametrize("tile_m", [32, 64, 256])
 def test_layer_parity_other_tiles(inputs, tile_m):
     inp = inputs("decode_b8")
@@ -425,6 +442,33 @@ def test_expert_tp_slices(inputs):
     ref = layer_sampled(inp, tokens)
     got = F.bf16_to_f64(sliced["out"][tokens])
     assert rel_l2(got, F.bf16_to_f64(ref["out"])) < TOL
+
+
+@pytest.mark.parametrize("name,tile_m", [("decode_b8", 16), ("decode_b8", 64), ("tiny", 16)])
+def test_experts_repeated_calls_on_one_metadata(inputs, name, tile_m):
+    """moe_experts_fwd called again and again on one routing (as a graph replay
+    or the expert TP slices do), its intermediate and rows cleared in between:
+    identical rows every time (decode_b8: the workgroup kernels with the LDS
+    copy of the activation for both GEMMs; tiny: GEMM2 on the one-wave kernel,
+    I/16 = 8 scale bytes per row)."""
+    inp = inputs(name)
+    wl = inp.wl
+    w = upload_weights(inp)
+    first = run_layer(inp, weights=w, tile_m=tile_m)
+    shape = LY.LayerShape(wl.T, wl.H, wl.I, wl.E, wl.K, tile_m)
+    bufs = LY.Buffers(shape, DEV)
+    LY.run_layer(bufs, dev(inp.x_bf16), dev(inp.a1_gscale), dev(inp.logits), None, None, w,
+                 dev(inp.norm_weight_bf16), wl.gain_center, wl.eps, bool(wl.weight_before_norm))
+    valid = first["perm2tok"] >= 0
+    say(f"repeated moe_experts_fwd {name} tile_m={tile_m}")
+    for it in range(6):
+        bufs.rows.fill_(0)
+        bufs.inter_codes.fill_(0)
+        bufs.inter_sf.fill_(0)
+        N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, w, wl.T, wl.K, wl.E, wl.H, wl.I,
+                          tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[0], None)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(bufs.rows)[0][valid], first["rows"][0][valid]), it
 
 
 def test_layer_leaves_padding_rows_untouched_and_is_deterministic(inputs):
