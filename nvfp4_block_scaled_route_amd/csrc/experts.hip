@@ -373,6 +373,11 @@ static int pipeline_depth(int kt) {
     return 1;
 }
 
+// Deepest pipelines of the workgroup kernels, as measured on the decode
+// shapes: GEMM1 gains nothing past 8 k-tiles (16 was slower), GEMM2 (12 k-tiles
+// at I = 768) a little from holding all of them.
+constexpr int kWgDepth1 = 8, kWgDepth2 = 16;
+
 // The workgroup kernels' LDS: at most 40 KB keeps 4 workgroups on a CU.
 constexpr int kMaxTileLds = 40 * 1024;
 
@@ -389,9 +394,33 @@ constexpr int kMaxTileLds = 40 * 1024;
     }
 MOE_LAUNCH_DEPTHS(gemm1_kernel)
 MOE_LAUNCH_DEPTHS(gemm2_kernel)
-MOE_LAUNCH_DEPTHS(gemm1_wg_kernel)
-MOE_LAUNCH_DEPTHS(gemm2_wg_kernel)
 #undef MOE_LAUNCH_DEPTHS
+
+// The workgroup kernels hold only weights in their pipeline (5 registers a
+// k-tile), so they go deeper.
+static int wg_depth(int kt, int cap) {
+    const int depths[] = {16, 12, 8, 6, 4, 3, 2, 1};
+    for (int d : depths)
+        if (d <= cap && kt % d == 0) return d;
+    return 1;
+}
+
+#define MOE_LAUNCH_WG(kernel)                                                                      \
+    static void launch_##kernel(int d, dim3 grid, unsigned lds, hipStream_t s, const ExpArgs& a) { \
+        switch (d) {                                                                               \
+            case 16: hipLaunchKernelGGL(kernel<16>, grid, dim3(kThreads), lds, s, a); break;      \
+            case 12: hipLaunchKernelGGL(kernel<12>, grid, dim3(kThreads), lds, s, a); break;      \
+            case 8: hipLaunchKernelGGL(kernel<8>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 6: hipLaunchKernelGGL(kernel<6>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 4: hipLaunchKernelGGL(kernel<4>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 3: hipLaunchKernelGGL(kernel<3>, grid, dim3(kThreads), lds, s, a); break;        \
+            case 2: hipLaunchKernelGGL(kernel<2>, grid, dim3(kThreads), lds, s, a); break;        \
+            default: hipLaunchKernelGGL(kernel<1>, grid, dim3(kThreads), lds, s, a); break;       \
+        }                                                                                          \
+    }
+MOE_LAUNCH_WG(gemm1_wg_kernel)
+MOE_LAUNCH_WG(gemm2_wg_kernel)
+#undef MOE_LAUNCH_WG
 
 }  // namespace moe
 
@@ -460,11 +489,11 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
     const bool wg1 = H % 256 == 0 && tile_lds_bytes(H) <= kMaxTileLds && (int64_t)T * (H / 2) < (1ll << 31);
     const bool wg2 = I % 256 == 0 && H % 128 == 0 && tile_lds_bytes(I) <= kMaxTileLds &&
                      args.L.rows_max * (I / 2) < (1ll << 31);
-    if (wg1) launch_gemm1_wg_kernel(d1, dim3((unsigned)grid1), (unsigned)tile_lds_bytes(H), s, args);
+    if (wg1) launch_gemm1_wg_kernel(wg_depth((int)kt1, kWgDepth1), dim3((unsigned)grid1), (unsigned)tile_lds_bytes(H), s, args);
     else launch_gemm1_kernel(d1, dim3((unsigned)grid1), 0, s, args);
     int rc = check_launch("moe_experts_fwd (GEMM1)");
     if (rc) return rc;
-    if (wg2) launch_gemm2_wg_kernel(d2, dim3((unsigned)grid2), (unsigned)tile_lds_bytes(I), s, args);
+    if (wg2) launch_gemm2_wg_kernel(wg_depth((int)kt2, kWgDepth2), dim3((unsigned)grid2), (unsigned)tile_lds_bytes(I), s, args);
     else launch_gemm2_kernel(d2, dim3((unsigned)grid2), 0, s, args);
     return check_launch("moe_experts_fwd (GEMM2)");
 }
