@@ -215,8 +215,8 @@ def main():
                            "algorithmic_flops": flops, "algorithmic_bytes": ab["total"], "hbm_gbs": achieved,
                            "kernel_ms": k_ms}
     else:
-        out["roofline"] = {"bound": "hbm", "kernel": "moe_experts_fwd (gemm1_wg_kernel: GEMM1+SwiGLU+requant, "
-                                                     "gemm2_wg_kernel)",
+        out["roofline"] = {"bound": "hbm", "kernel": "moe_experts_fwd (experts_fused_kernel: GEMM1+SwiGLU+requant "
+                                                     "and GEMM2 in one launch)",
                            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",

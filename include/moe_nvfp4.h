@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 2
+#define MOE_NVFP4_ABI_VERSION 3
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -78,6 +78,15 @@ int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
  *   perm2tok        [rows_max]   token of each permuted row; -1 for padding rows
  *                                and for every row >= total_rows
  *   tile_expert     [rows_max/m] local expert of each tile; -1 beyond num_tiles
+ *   sync_status     [1]          0; moe_experts_fwd sets 1 if one of its waits
+ *                                gave up (its results are then not valid)
+ *   sub_sync        [256*subs_max] (subs_max = rows_max/16): two counters per
+ *                                16-row tile s, at 256*s and 256*s + 1 (1 KB
+ *                                apart, so that the polls on different tiles
+ *                                spread over memory channels), set to 0 by
+ *                                moe_route; moe_experts_fwd's one-launch form
+ *                                uses them and leaves them at 0 again. The
+ *                                other words are not used.
  * Order (the counting-sort reading of the flashinfer_ops page's metadata,
  * "FlashInferOps.slot"): experts ascending, routes of one expert in ascending
  * t*K+k, each expert's rows padded to a multiple of m. */
@@ -92,6 +101,9 @@ typedef struct moe_meta_layout {
     int64_t total_ints; /* buffer length in int32 */
     int64_t rows_max;
     int64_t tiles_max;
+    int64_t sync_status;
+    int64_t sub_sync;
+    int64_t subs_max;
 } moe_meta_layout;
 
 int moe_meta_layout_get(int T, int K, int E_local, int tile_m, moe_meta_layout* out);
@@ -228,14 +240,23 @@ typedef struct moe_nvfp4_weights {
  * not written.
  *   a_codes, a_sf  device [T, H/2], [T, H/16]: the NVFP4 input, row-major, as
  *                  nvfp4_quant writes it
- *   meta           moe_route's metadata for the same T, K, E_local, tile_m
+ *   meta           moe_route's metadata for the same T, K, E_local, tile_m (in/out:
+ *                  the sync words, see below)
  *   w              converted experts (host struct; pointers in it are device)
  *   inter_codes, inter_sf  device [rows_max, I/2], [rows_max, I/16] out: the
  *                  requantized intermediate, row-major (GEMM2's input)
  *   rows           device bf16 [rows_max, rows_stride] out, rows_stride >= H
- * Two launches on `stream` (GEMM1 with the SwiGLU/requant epilogue, then GEMM2).
+ * Launches on `stream`: with few routes per expert and H % 256 == 0,
+ * I % 256 == 0, 9*H and 9*I <= 40960, one launch in which each 16-row tile's
+ * GEMM2 workgroups fetch their weights at once and wait, on the tile's
+ * counters in meta's sub_sync, for its GEMM1 workgroups to publish the
+ * intermediate; otherwise two (GEMM1 with the SwiGLU/requant epilogue, then
+ * GEMM2). The counters must be 0 on entry (moe_route leaves them so, and every
+ * call returns them to 0), so calls that share one meta buffer must not run
+ * concurrently. Every wait is bounded: a wait that gives up sets
+ * meta[sync_status] to 1.
  * H % 64 == 0, I % 64 == 0, H and I <= MOE_MAX_HIDDEN, tile_m % 16 == 0. */
-int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const int32_t* meta,
+int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
                     const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
                     int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
                     int64_t rows_stride, void* stream);

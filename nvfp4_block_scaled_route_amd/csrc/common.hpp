@@ -18,6 +18,10 @@ int quant_check(const uint16_t* x, int64_t x_row_stride, const float* gscale, in
 int check_launch(const char* what);                // MOE_ELAUNCH on a pending launch error
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m);
+// int32 words between the sync counters of consecutive 16-row tiles in the
+// metadata (1 KB): tiles' counters on distinct cache lines and memory channels,
+// so that the polls of many workgroups do not all queue on one channel.
+constexpr int kSubSyncStride = 256;
 
 // ------------------------------------------------------------------ codecs
 // e2m1: nearest value of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,

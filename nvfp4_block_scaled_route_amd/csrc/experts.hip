@@ -150,7 +150,19 @@ __device__ __forceinline__ RowTile row_tile(const ExpArgs& a, int sub, int n) {
 }
 
 // ---------------------------------------------------------------- epilogues
-// GEMM1: lane (q, n) holds rows 4q + i of intermediate 16j + n.
+// Agent-coherent stores (sc1): visible to agent-coherent loads on every XCD
+// once they have completed, without a write-back of the writer's L2.
+__device__ __forceinline__ void store_u32_sc1(uint8_t* p, uint32_t v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_u8_sc1(uint8_t* p, uint8_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// GEMM1: lane (q, n) holds rows 4q + i of intermediate 16j + n. kPublish: the
+// intermediate is handed to GEMM2 workgroups of the same launch, so it is
+// written with agent-coherent stores.
+template <bool kPublish = false>
 __device__ __forceinline__ void gemm1_epilogue(const ExpArgs& a, const RowTile& rt, int e, int j, int n, int q,
                                                const floatx4& acc_g, const floatx4& acc_u) {
     const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
@@ -168,9 +180,15 @@ __device__ __forceinline__ void gemm1_epilogue(const ExpArgs& a, const RowTile& 
         b = b | (__shfl_xor(b, 4) << 16);                     // n % 8 == 0: 4 bytes
         if ((rt.vmask >> m) & 1u) {
             const int64_t row = rt.row0 + m;
-            if ((n & 7) == 0)
-                *reinterpret_cast<uint32_t*>(a.inter_codes + row * (a.I >> 1) + j * 8 + (n >> 1)) = b;
-            if (n == 0) a.inter_sf[row * (a.I >> 4) + j] = (uint8_t)bs.byte;
+            uint8_t* cp = a.inter_codes + row * (a.I >> 1) + j * 8 + (n >> 1);
+            uint8_t* sp = a.inter_sf + row * (a.I >> 4) + j;
+            if (kPublish) {
+                if ((n & 7) == 0) store_u32_sc1(cp, b);
+                if (n == 0) store_u8_sc1(sp, (uint8_t)bs.byte);
+            } else {
+                if ((n & 7) == 0) *reinterpret_cast<uint32_t*>(cp) = b;
+                if (n == 0) *sp = (uint8_t)bs.byte;
+            }
         }
     }
 }
@@ -245,17 +263,25 @@ __host__ __device__ constexpr int tile_lds_bytes(int K) { return 8 * K + K; }
 // one direct-to-LDS load moves 64 consecutive units, lane l taking row l % 16
 // (a lane of a 16-row MFMA tile, whose row base `cbase`/`sbase` it holds).
 // The four waves take every fourth load.
+// kCoherent: agent-coherent loads (a tile another XCD published in this launch).
+template <bool kCoherent = false>
 __device__ __forceinline__ void copy_tile(uint8_t* lds, int K, int wave, int lane, u32x4 crsrc, uint32_t cbase,
                                           u32x4 srsrc, uint32_t sbase) {
     const int code_chunks = K >> 1, sf_chunks = K >> 4;   // 16 rows x (K/32) and 16 rows x (K/256)
     const uint32_t l0 = lds_addr(lds);
     const uint32_t k = (uint32_t)(lane >> 4);
-    for (int x0 = wave * 64; x0 < code_chunks; x0 += kThreads)
-        lds_copy16(crsrc, __builtin_amdgcn_readfirstlane(l0 + x0 * 16), cbase + ((x0 >> 4) + k) * 16, 0);
+    for (int x0 = wave * 64; x0 < code_chunks; x0 += kThreads) {
+        const uint32_t l = __builtin_amdgcn_readfirstlane(l0 + x0 * 16), v = cbase + ((x0 >> 4) + k) * 16;
+        if (kCoherent) lds_copy16_sc1(crsrc, l, v, 0);
+        else lds_copy16(crsrc, l, v, 0);
+    }
     for (int x0 = wave * 64; x0 < sf_chunks; x0 += kThreads)
-        if (x0 + lane < sf_chunks)
-            lds_copy16(srsrc, __builtin_amdgcn_readfirstlane(l0 + (code_chunks + x0) * 16),
-                       sbase + ((x0 >> 4) + k) * 16, 0);
+        if (x0 + lane < sf_chunks) {
+            const uint32_t l = __builtin_amdgcn_readfirstlane(l0 + (code_chunks + x0) * 16);
+            const uint32_t v = sbase + ((x0 >> 4) + k) * 16;
+            if (kCoherent) lds_copy16_sc1(srsrc, l, v, 0);
+            else lds_copy16(srsrc, l, v, 0);
+        }
 }
 
 // A wave's loads of the copy issued by copy_tile: wait for those with all D
@@ -278,15 +304,19 @@ __device__ __forceinline__ void lds_act(uint2& a, uint32_t& s, const uint8_t* lc
 }
 
 template <int D>
-__device__ __forceinline__ void stream_lds(const Streams& p, const uint8_t* lc, const uint8_t* ls, int KT,
-                                           floatx4& acc0, floatx4& acc1) {
-    Stage st[D];
+__device__ __forceinline__ void preload_w(Stage (&st)[D], const Streams& p) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         load_w(st[d], p, d);
         __builtin_amdgcn_sched_barrier(0);
     }
-    copy_wait<D>();
+}
+
+// The k-tiles of a unit whose first D weight k-tiles are in flight in st and
+// whose tile is in LDS.
+template <int D>
+__device__ __forceinline__ void stream_lds_run(Stage (&st)[D], const Streams& p, const uint8_t* lc,
+                                               const uint8_t* ls, int KT, floatx4& acc0, floatx4& acc1) {
     uint2 na;
     uint32_t ns;
     lds_act(na, ns, lc, ls, 0);
@@ -310,6 +340,15 @@ __device__ __forceinline__ void stream_lds(const Streams& p, const uint8_t* lc, 
         use_stage(st[d], acc0, acc1);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+template <int D>
+__device__ __forceinline__ void stream_lds(const Streams& p, const uint8_t* lc, const uint8_t* ls, int KT,
+                                           floatx4& acc0, floatx4& acc1) {
+    Stage st[D];
+    preload_w<D>(st, p);
+    copy_wait<D>();
+    stream_lds_run<D>(st, p, lc, ls, KT, acc0, acc1);
 }
 
 // GEMM1 units 4b .. 4b + 3: intermediate pairs of one tile (I/16 % 4 == 0).
@@ -362,6 +401,101 @@ __global__ void __launch_bounds__(kThreads) gemm2_wg_kernel(ExpArgs a) {
     const uint8_t* ls = tile_lds + (a.I >> 1) * 16 + n * 16 + q;
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     stream_lds<D>(p, lc, ls, a.I >> 6, acc0, acc1);
+    gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+}
+
+// ---------------------------------------------------------------- both GEMMs in one launch
+// Workgroups [0, g1_blocks) are GEMM1's, as in gemm1_wg_kernel; the rest are
+// GEMM2's, as in gemm2_wg_kernel, except that a GEMM2 workgroup issues the
+// loads of its first D2 weight k-tiles at once and only then waits for its
+// 16-row tile's intermediate. The weights of both GEMMs thus stream from HBM
+// together, and what is left after GEMM1's stream ends is the hand-over of the
+// small intermediate and GEMM2's MFMAs on weights already in registers.
+//
+// Hand-over between XCDs, each with its own L2: a GEMM1 workgroup writes its
+// part of the intermediate with agent-coherent stores, waits until they have
+// completed, and adds 1 to the tile's ready counter. A GEMM2 workgroup polls
+// that counter until all I/64 GEMM1 workgroups of the tile have added theirs,
+// then copies the tile with agent-coherent loads. Nothing handed over passes
+// through plain stores, so no L2 write-back or invalidation is needed.
+//
+// Forward progress: workgroups are dispatched in index order, so every GEMM1
+// workgroup has been dispatched before a GEMM2 workgroup can wait, and GEMM1
+// workgroups wait for nothing. The wait is bounded all the same: after
+// kSpinMax polls it gives up and sets the status word to 1.
+//
+// Reset: after its copy each GEMM2 workgroup counts itself on the tile's done
+// counter; the last of the tile's H/128 returns both counters to 0, so the next
+// call on the same metadata starts from 0.
+constexpr uint32_t kSpinMax = 1u << 20;
+
+__device__ __forceinline__ void wait_ready(int32_t* ready, int target, int32_t* status) {
+    for (uint32_t it = 0;; ++it) {
+        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+        if (it >= kSpinMax) {
+            __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+template <int D1, int D2>
+__global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint32_t g1_blocks) {
+    extern __shared__ __align__(16) uint8_t tile_lds[];
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t* lc = tile_lds + ((q >> 1) * 16 + n) * 16 + (q & 1) * 8;
+    if (blockIdx.x < g1_blocks) {
+        const uint32_t n1 = a.I >> 4;
+        const uint32_t unit = blockIdx.x * kWavesPerBlock + wave;
+        const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
+        const RowTile rt = row_tile(a, sub, n);
+        if (rt.e < 0) return;
+        const int e = rt.e;
+        const uint32_t tok = rt.tok >= 0 ? (uint32_t)rt.tok : 0u;
+        copy_tile(tile_lds, a.H, wave, lane, buffer_desc(a.a_codes), tok * (uint32_t)(a.H >> 1),
+                  buffer_desc(a.a_sf), tok * (uint32_t)(a.H >> 4));
+        Streams p;
+        p.wc = a.w.w13 + e * a.w.w13_expert_stride_bytes + j * a.w.w13_pair_stride_bytes + lane * 16;
+        p.ws = a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + j * a.w.w13_sf_pair_stride_bytes + lane * 2;
+        const uint8_t* ls = tile_lds + (a.H >> 1) * 16 + n * 16 + q;
+        floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
+        stream_lds<D1>(p, lc, ls, a.H >> 6, acc_g, acc_u);
+        gemm1_epilogue<true>(a, rt, e, j, n, q, acc_g, acc_u);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(a.sync + kSubSyncStride * sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const uint32_t n2 = a.H >> 5;
+    const uint32_t unit = (blockIdx.x - g1_blocks) * kWavesPerBlock + wave;
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
+    const RowTile rt = row_tile(a, sub, n);
+    if (rt.e < 0) return;
+    const int e = rt.e;
+    Streams p;
+    p.wc = a.w.w2 + e * a.w.w2_expert_stride_bytes + c * a.w.w2_pair_stride_bytes + lane * 16;
+    p.ws = a.w.w2_sf + e * a.w.w2_sf_expert_stride_bytes + c * a.w.w2_sf_pair_stride_bytes + lane * 2;
+    Stage st[D2];
+    preload_w<D2>(st, p);
+    int32_t* ready = a.sync + kSubSyncStride * sub;
+    if (wave == 0) wait_ready(ready, a.I >> 6, a.status);
+    __syncthreads();
+    const uint32_t row = (uint32_t)(rt.row0 + n);
+    copy_tile<true>(tile_lds, a.I, wave, lane, buffer_desc(a.inter_codes), row * (uint32_t)(a.I >> 1),
+                    buffer_desc(a.inter_sf), row * (uint32_t)(a.I >> 4));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this wave's part of the copy has landed
+    __syncthreads();
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(ready + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (a.H >> 7) - 1) {
+        __hip_atomic_store(ready, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ready + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint8_t* ls = tile_lds + (a.I >> 1) * 16 + n * 16 + q;
+    floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    stream_lds_run<D2>(st, p, lc, ls, a.I >> 6, acc0, acc1);
     gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
 }
 
@@ -422,9 +556,29 @@ MOE_LAUNCH_WG(gemm1_wg_kernel)
 MOE_LAUNCH_WG(gemm2_wg_kernel)
 #undef MOE_LAUNCH_WG
 
+// The one-launch form holds GEMM2's first D2 weight k-tiles in registers
+// while it waits: 8 where that divides I/64, else 4. Up to 8 k-tiles (40
+// registers) the kernel stays within five waves per SIMD, so that on decode
+// shapes every workgroup is resident from the start; 12 (all of I = 768) cost
+// a wave per SIMD and were slower, and 6 measured no better than 4.
+static int fused_depth2(int kt2) { return kt2 % 8 == 0 ? 8 : 4; }
+
+static void launch_fused(int d1, int d2, dim3 grid, unsigned lds, hipStream_t s, const ExpArgs& a,
+                         uint32_t g1_blocks) {
+#define MOE_FUSED(D1, D2) hipLaunchKernelGGL((experts_fused_kernel<D1, D2>), grid, dim3(kThreads), lds, s, a, g1_blocks)
+    if (d1 == 8) {
+        if (d2 == 8) MOE_FUSED(8, 8);
+        else MOE_FUSED(8, 4);
+    } else {
+        if (d2 == 8) MOE_FUSED(4, 8);
+        else MOE_FUSED(4, 4);
+    }
+#undef MOE_FUSED
+}
+
 }  // namespace moe
 
-extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, const int32_t* meta,
+extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
                                const moe_nvfp4_weights* w, int T, int K, int E_local, int H,
                                int I, int tile_m, uint8_t* inter_codes, uint8_t* inter_sf,
                                uint16_t* rows, int64_t rows_stride, void* stream) {
@@ -467,6 +621,8 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
     args.w = *w; args.T = T; args.E_local = E_local; args.H = H; args.I = I; args.tile_m = tile_m;
     args.inter_codes = inter_codes; args.inter_sf = inter_sf; args.rows = rows;
     args.rows_stride = rows_stride;
+    args.sync = meta + args.L.sub_sync;
+    args.status = meta + args.L.sync_status;
     if (args.L.rows_max == 0) return MOE_OK;
     const int64_t subs = args.L.rows_max / 16;             // 16-row tiles, routed or not
     const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
@@ -489,6 +645,15 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, cons
     const bool wg1 = H % 256 == 0 && tile_lds_bytes(H) <= kMaxTileLds && (int64_t)T * (H / 2) < (1ll << 31);
     const bool wg2 = I % 256 == 0 && H % 128 == 0 && tile_lds_bytes(I) <= kMaxTileLds &&
                      args.L.rows_max * (I / 2) < (1ll << 31);
+    // Both workgroup forms: one launch, GEMM2's weights streamed beside GEMM1's
+    // (pipeline depths dividing H/64 and I/64, both multiples of 4).
+    if (wg1 && wg2 && grid1 + grid2 <= 0x7FFFFFFF) {
+        const unsigned lds = (unsigned)(tile_lds_bytes(H) > tile_lds_bytes(I) ? tile_lds_bytes(H) : tile_lds_bytes(I));
+        const int f1 = kt1 % 8 == 0 ? 8 : 4;
+        const int f2 = fused_depth2((int)kt2);
+        launch_fused(f1, f2, dim3((unsigned)(grid1 + grid2)), lds, s, args, (uint32_t)grid1);
+        return check_launch("moe_experts_fwd (GEMM1 + GEMM2)");
+    }
     if (wg1) launch_gemm1_wg_kernel(wg_depth((int)kt1, kWgDepth1), dim3((unsigned)grid1), (unsigned)tile_lds_bytes(H), s, args);
     else launch_gemm1_kernel(d1, dim3((unsigned)grid1), 0, s, args);
     int rc = check_launch("moe_experts_fwd (GEMM1)");

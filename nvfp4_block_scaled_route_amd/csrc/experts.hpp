@@ -17,6 +17,8 @@ struct ExpArgs {
     uint8_t* inter_sf;
     uint16_t* rows;
     int64_t rows_stride;
+    int32_t* sync;       // meta's sub_sync: per 16-row tile (kSubSyncStride apart), GEMM1 workgroups done, GEMM2 copies done
+    int32_t* status;     // meta's sync_status
 };
 
 constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;   // converted layout: per pair and k-tile
@@ -46,6 +48,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // caller's (vmcnt, which it shares with the loads issued around it).
 __device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+// The same load, agent-coherent (sc1): it returns what another XCD wrote with
+// agent-coherent stores, not a line its own L2 may still hold.
+__device__ __forceinline__ void lds_copy16_sc1(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc1 lds"
                  :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 

@@ -227,6 +227,14 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e) {
 }
 
 
+// The expert step's sync words start at zero: its status and the two counters
+// of every 16-row tile (moe_experts_fwd's one-launch form).
+__device__ __forceinline__ void clear_sync(const RouteArgs& a, int i, int step) {
+    int32_t* sync = a.meta + a.L.sub_sync;
+    for (int64_t x = i; x < 2 * a.L.subs_max; x += step) sync[(x >> 1) * kSubSyncStride + (x & 1)] = 0;
+    if (i == 0) a.meta[a.L.sync_status] = 0;
+}
+
 // The permutation metadata by one wave, with no workgroup barrier: routes in
 // chunks of 64 (one per lane), experts in runs of ceil(El / 64) per lane.
 constexpr int kWaveMaxRoutes = 512;
@@ -281,6 +289,7 @@ __device__ void permute_wave(const RouteArgs& a, const int32_t* ids, int32_t* ld
     }
     for (int tile = num_tiles + lane; tile < a.L.tiles_max; tile += 64) tile_expert[tile] = -1;
     for (int row = total_rows + lane; row < a.L.rows_max; row += 64) perm2tok[row] = -1;
+    clear_sync(a, lane, 64);
     // stable ranks, chunk by chunk, scattered at once
     for (int base = 0; base < R; base += 64) {
         const int r = base + lane;
@@ -357,6 +366,7 @@ __device__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* l
     }
     for (int tile = num_tiles + tid; tile < a.L.tiles_max; tile += kRouteThreads) tile_expert[tile] = -1;
     for (int row = total_rows + tid; row < a.L.rows_max; row += kRouteThreads) perm2tok[row] = -1;
+    clear_sync(a, tid, kRouteThreads);
     // pass 2: stable rank within the expert, in chunks of one route per thread
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     for (int base = 0; base < R; base += kRouteThreads) {

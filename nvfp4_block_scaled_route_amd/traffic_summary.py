@@ -30,7 +30,8 @@ SOURCES = ["nvfp4_block_scaled_route_amd/csrc/experts.hip",
            "nvfp4_block_scaled_route_amd/csrc/experts_tiled.hip",
            "nvfp4_block_scaled_route_amd/csrc/experts.hpp",
            "nvfp4_block_scaled_route_amd/csrc/common.hpp"]
-EXPERT_KERNELS = ("gemm1_kernel", "gemm2_kernel", "gemm1_wg_kernel", "gemm2_wg_kernel", "tiled_kernel")
+EXPERT_KERNELS = ("gemm1_kernel", "gemm2_kernel", "gemm1_wg_kernel", "gemm2_wg_kernel", "experts_fused_kernel",
+                  "tiled_kernel")
 
 
 def per_dispatch(run_dir: str, counter: str) -> dict:

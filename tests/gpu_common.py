@@ -31,6 +31,11 @@ def host(t: torch.Tensor) -> np.ndarray:
     return a.view(np.uint16) if a.dtype == np.int16 else a
 
 
+def sync_counters(meta: np.ndarray, L) -> np.ndarray:
+    """The two sync counters of every 16-row tile in a metadata buffer."""
+    return meta[L.sub_sync:L.sub_sync + 256 * L.subs_max].reshape(-1, 256)[:, :2]
+
+
 def upload_weights(inp: W.Inputs) -> N.Weights:
     w13c, w13s, w2c, w2s = dev(inp.w13_codes), dev(inp.w13_sf), dev(inp.w2_codes), dev(inp.w2_sf)
     w = LY.pack_weights(w13c, w13s, w2c, w2s, dev(inp.g1_alphas), dev(inp.g1_scale_c),
@@ -70,6 +75,7 @@ def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | Non
         exp2perm=meta[L.exp2perm:L.exp2perm + wl.T * wl.K].reshape(wl.T, wl.K),
         perm2tok=meta[L.perm2tok:L.perm2tok + L.rows_max],
         tile_expert=meta[L.tile_expert:L.tile_expert + L.tiles_max],
+        sync_status=int(meta[L.sync_status]), sub_sync=sync_counters(meta, L),
         inter_codes=host(bufs.inter_codes), inter_sf=host(bufs.inter_sf),
         rows=host(bufs.rows), out=host(bufs.out))
     return res

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
@@ -40,12 +40,15 @@ def test_rows_max_matches_oracle(T, K, E, m):
     assert N.moe_rows_max(T, K, E, m) == oracle_rows_max(T, K, E, m)
     lay = N.moe_meta_layout_get(T, K, E, m)
     assert lay.rows_max == oracle_rows_max(T, K, E, m) and lay.tiles_max * m == lay.rows_max
-    fields = [lay.expert_offsets, lay.expert_counts, lay.exp2perm, lay.perm2tok, lay.tile_expert]
-    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max]
+    assert lay.subs_max * 16 == lay.rows_max
+    fields = [lay.expert_offsets, lay.expert_counts, lay.exp2perm, lay.perm2tok, lay.tile_expert,
+              lay.sub_sync]
+    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max, 256 * lay.subs_max]
     assert all(f % 64 == 0 for f in fields)
     for (f, n), nxt in zip(zip(fields, sizes), fields[1:] + [lay.total_ints]):
         assert f + n <= nxt
-    assert lay.num_tiles < 64 and lay.total_rows < 64 and lay.num_tiles != lay.total_rows
+    header = {lay.num_tiles, lay.total_rows, lay.sync_status}
+    assert len(header) == 3 and max(header) < 64
 
 
 def test_invalid_sizes_are_refused():

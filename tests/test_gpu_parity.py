@@ -21,7 +21,7 @@ from oracle.permute import permute as o_permute
 from oracle.quant import quantize_nvfp4
 from oracle.routing import route as o_route
 
-from .gpu_common import DEV, dev, host, run_layer, say, upload_weights
+from .gpu_common import DEV, dev, host, run_layer, say, sync_counters, upload_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +140,7 @@ def _check_route(logits, bias, K, tile_m, offset=0, local=None, padding=None, ro
     assert np.array_equal(meta[L.exp2perm:L.exp2perm + T * K], om["exp2perm"].reshape(-1))
     assert np.array_equal(meta[L.perm2tok:L.perm2tok + L.rows_max], om["perm2tok"])
     assert np.array_equal(meta[L.tile_expert:L.tile_expert + L.tiles_max], om["tile_expert"])
+    assert meta[L.sync_status] == 0 and not np.any(sync_counters(meta, L))
     assert np.all(meta[L.total_ints:] == -777)                   # nothing written past the buffer
     return ids, w, meta
 
@@ -294,7 +295,15 @@ def _finalize_case(wbn, npart, use_norm, T, K, H):
 
 
 # ------------------------------------------------------------------ whole layer
+def _check_sync_words(res):
+    """The expert step's waits all ended normally and its per-tile counters
+    are back at zero (the next call on this metadata starts from them)."""
+    assert res["sync_status"] == 0
+    assert not np.any(res["sub_sync"])
+
+
 def _compare_layer(res, ref, name):
+    _check_sync_words(res)
     p = ref["rows_idx"]
     # routing and metadata: bit-exact
     assert np.array_equal(res["ids"], ref["ids"])
@@ -342,12 +351,15 @@ def test_layer_parity_tiled_path(T, H, I, E, K, m):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 16),
-                                         (7, 512, 768, 16, 4, 32), (3, 1024, 512, 4, 2, 16)])
+                                         (7, 512, 768, 16, 4, 32), (3, 1024, 512, 4, 2, 16),
+                                         (4, 512, 320, 8, 2, 16), (9, 768, 1280, 8, 3, 16)])
 def test_layer_parity_streaming_kernel_choices(T, H, I, E, K, m):
     """Few routes per expert, shapes that take each expert kernel: GEMM1 on the
     one-wave kernel (H % 256 != 0) or on the workgroup kernel with the LDS copy
-    of the activation, GEMM2 likewise (I % 256 and H % 128), pipeline depths
-    5 (H/64), 3, 6 (I/64 = 12) and 8."""
+    of the activation, GEMM2 likewise (I % 256 and H % 128), and both GEMMs in
+    one launch where both workgroup forms apply (H % 256 == 0 and I % 256 == 0:
+    GEMM2 weight preloads of 8 and 4 k-tiles, GEMM1 depths 8 and 4);
+    two-launch pipeline depths 5 (H/64), 3, 6 (I/64 = 12) and 8."""
     from oracle.layer import intermediate_amax
     wl = W.Workload(f"stream_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E, K=K, tile_m=m, seed=5)
     probe = W.make_inputs(wl, a2_gscale=1.0)
@@ -461,6 +473,7 @@ def test_experts_repeated_calls_on_one_metadata(inputs, name, tile_m):
                  dev(inp.norm_weight_bf16), wl.gain_center, wl.eps, bool(wl.weight_before_norm))
     valid = first["perm2tok"] >= 0
     say(f"repeated moe_experts_fwd {name} tile_m={tile_m}")
+    L = bufs.layout
     for it in range(6):
         bufs.rows.fill_(0)
         bufs.inter_codes.fill_(0)
@@ -469,6 +482,8 @@ def test_experts_repeated_calls_on_one_metadata(inputs, name, tile_m):
                           tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[0], None)
         torch.cuda.synchronize()
         assert np.array_equal(host(bufs.rows)[0][valid], first["rows"][0][valid]), it
+        meta = host(bufs.meta)
+        assert meta[L.sync_status] == 0 and not np.any(sync_counters(meta, L)), it
 
 
 def test_layer_leaves_padding_rows_untouched_and_is_deterministic(inputs):
