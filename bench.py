@@ -91,6 +91,31 @@ def algorithmic_bytes(wl, counts) -> dict:
                 total=touched * per_expert + act + inter + rows)
 
 
+def time_norm_quant(N, x, norm_w, gscale, wl, n: int) -> dict:
+    """The pre-expert RMSNorm + NVFP4 quantizer (nvfp4_norm_quant) on the
+    workload's activations, event-timed on its stream: 2H bytes read and 9H/16
+    written per row (the norm weight, 2H bytes, is read once and cached)."""
+    import torch
+    T, H = wl.T, wl.H
+    codes = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((T, H // 16), dtype=torch.uint8, device=x.device)
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        N.nvfp4_norm_quant(x, norm_w, 1.0, 1e-6, gscale, codes, sf, s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        torch.cuda._sleep(20000)
+        a.record(s)
+        N.nvfp4_norm_quant(x, norm_w, 1.0, 1e-6, gscale, codes, sf, s)
+        b.record(s)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    nbytes = T * (2 * H + H // 2 + H // 16) + 2 * H
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": us, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": gbs / HBM_PEAK_GBS, "bound": "hbm" if T >= 1024 else "latency"}
+
+
 def cpu_baseline(inp, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
     from oracle.layer import layer as o_layer
@@ -222,6 +247,7 @@ def main():
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                            "experts_touched": ab["touched"], "kernel_ms": k_ms}
+    out["extra_kernels"] = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -151,6 +151,26 @@ int moe_route(const float* logits, int64_t logits_row_stride, const float* exper
 int nvfp4_quant(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
                 uint8_t* codes, uint8_t* sf, void* stream);
 
+/* ------------------------------------------------------------------ norm + quantizer
+ * The pre-expert RMSNorm run inside the NVFP4 input quantizer (the model page,
+ * "MuseSpark1xMoE": pre_expert_norm with a weight, a zero-centred gain and
+ * rms_norm_eps; "norm_fuses_into_nvfp4_quant": the weight applies after
+ * normalizing; "_prepared_nvfp4_forward": norm_quant_trtllm_nvfp4(pooled,
+ * num_tokens, weight, eps, gain_center, global_scale)). Per row of H values:
+ *   s  = sum_j x_j^2 in fp64;  ms = fp32(s / H);  r = 1 / sqrt(ms + eps)  (fp32)
+ *   y_j = (x_j * r) * gamma_j,  gamma_j = fp32(norm_weight_j) + gain_center
+ * each fp32 step one correctly rounded operation; y (fp32, not rounded to bf16)
+ * is then quantized exactly as nvfp4_quant quantizes x.
+ *   x            device bf16 [T, H], row stride x_row_stride elements (>= H)
+ *   norm_weight  device bf16 [H] or NULL (ones)
+ *   eps          in (0, 1]
+ *   gscale       device fp32 [1]: the input global scale
+ *   codes, sf    as nvfp4_quant: device uint8 [T, H/2] and [T, H/16] out
+ * H % 16 == 0, H <= MOE_MAX_HIDDEN. One launch on `stream`. */
+int nvfp4_norm_quant(const uint16_t* x, int64_t x_row_stride, const uint16_t* norm_weight,
+                     float gain_center, float eps, const float* gscale, int T, int H,
+                     uint8_t* codes, uint8_t* sf, void* stream);
+
 /* ------------------------------------------------------------------ routing + quantizer
  * moe_route and nvfp4_quant in one launch: the same outputs as moe_route(...)
  * followed by nvfp4_quant(x, x_row_stride, gscale, T, H, codes, sf) on the

@@ -19,7 +19,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 # Every symbol include/moe_nvfp4.h declares.
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout_get",
            "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
-           "moe_experts_fwd", "moe_finalize")
+           "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant")
 
 
 class MoeMetaLayout(ctypes.Structure):
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         "moe_meta_layout_get": (i32, [i32, i32, i32, i32, ctypes.POINTER(MoeMetaLayout)]),
         "moe_route": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp]),
+        "nvfp4_norm_quant": (i32, [vp, i64, vp, f32, f32, vp, i32, i32, vp, vp, vp]),
         "moe_route_quant": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
                                   vp, i64, vp, i32, vp, vp, vp]),
         "moe_pack_w13": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
@@ -125,6 +126,13 @@ def nvfp4_quant(x, gscale, codes, sf, stream=None) -> None:
     T, H = x.shape
     _check(lib().nvfp4_quant(_ptr(x), x.stride(0), _ptr(gscale), T, H, _ptr(codes), _ptr(sf),
                              _stream(stream)), "nvfp4_quant")
+
+
+def nvfp4_norm_quant(x, norm_weight, gain_center, eps, gscale, codes, sf, stream=None) -> None:
+    T, H = x.shape
+    _check(lib().nvfp4_norm_quant(_ptr(x), x.stride(0), _ptr(norm_weight), gain_center, eps,
+                                  _ptr(gscale), T, H, _ptr(codes), _ptr(sf), _stream(stream)),
+           "nvfp4_norm_quant")
 
 
 def moe_route_quant(logits, expert_bias, is_padding, K, route_scale, tile_m, local_expert_offset,

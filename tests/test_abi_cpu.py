@@ -64,6 +64,10 @@ def test_invalid_sizes_are_refused():
         (L.moe_route, (None, 4, None, None, 4, 8, 2, f(1.0), 16, 0, 8, None, None, None, None), N.MOE_EINVAL),  # stride < E
         (L.nvfp4_quant, (None, 24, None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
         (L.nvfp4_quant, (None, 32, None, 4, 32, None, None, None), N.MOE_EINVAL),         # NULL
+        (L.nvfp4_norm_quant, (None, 24, None, f(1.0), f(1e-6), None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.nvfp4_norm_quant, (None, 32, None, f(1.0), f(1e-6), None, 4, 32, None, None, None), N.MOE_EINVAL),
+        (L.nvfp4_norm_quant, (16, 32, None, f(1.0), f(0.0), 16, 4, 32, 16, 16, None), N.MOE_EINVAL),   # eps 0
+        (L.nvfp4_norm_quant, (16, 32 * 1024, None, f(1.0), f(1e-6), 16, 4, 32 * 1024, 16, 16, None), N.MOE_EUNSUPPORTED),
         (L.moe_route_quant, (None, 8, None, None, 4, 8, 2, f(1.0), 16, 0, 8, None, None, None,
                              None, 24, None, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
         (L.moe_route_quant, (None, 8, None, None, 4, 8, 9, f(1.0), 16, 0, 8, None, None, None,
