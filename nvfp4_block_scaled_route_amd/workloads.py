@@ -82,7 +82,8 @@ WORKLOADS = {
 ORDER = ["tiny", "decode_b8", "decode_b64_zipf", "prefill_t4096", "expert_tp8_b32"]
 
 _STREAMS = ["x", "outlier_mask", "logits", "zipf_perm", "w13_codes", "w13_sf",
-            "w2_codes", "w2_sf", "g1_alphas", "g1_scale_c", "g2_alphas", "gamma"]
+            "w2_codes", "w2_sf", "g1_alphas", "g1_scale_c", "g2_alphas", "gamma",
+            "router_x", "router_w"]
 
 
 def _rng(seed: int, stream: str) -> np.random.Generator:
@@ -124,6 +125,18 @@ class Inputs:
 def _scale_bytes(rng: np.random.Generator, shape) -> np.ndarray:
     # e4m3 codes 0x30 (0.5) .. 0x40 (2.0): the codes whose values lie in [0.5, 2].
     return rng.integers(0x30, 0x41, size=shape, dtype=np.uint8)
+
+
+def make_router_inputs(wl: Workload, seed: int | None = None, tokens: int | None = None):
+    """The router's fp32 input [T, D] (N(0,1)) and weight [E, D] (N(0, 1/D), so
+    that the logits are about N(0,1) like the workloads' direct logits), with
+    D = H; `tokens` draws only the first rows of the input."""
+    seed = wl.seed if seed is None else seed
+    T = wl.T if tokens is None else tokens
+    x = _rng(seed, "router_x").standard_normal((T, wl.H), dtype=np.float32)
+    w = (_rng(seed, "router_w").standard_normal((wl.E, wl.H), dtype=np.float32)
+         * np.float32(1.0 / np.sqrt(wl.H))).astype(np.float32)
+    return x, w
 
 
 def make_weights(wl: Workload, seed: int | None = None):
