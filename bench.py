@@ -116,6 +116,43 @@ def time_norm_quant(N, x, norm_w, gscale, wl, n: int) -> dict:
             "frac": gbs / HBM_PEAK_GBS, "bound": "hbm" if T >= 1024 else "latency"}
 
 
+def _event_us(fn, n: int) -> float:
+    """Mean event-timed duration of fn() on the current stream, each launch
+    behind a sleep kernel so that host enqueue time stays out of it."""
+    import torch
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        fn(s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        torch.cuda._sleep(20000)
+        a.record(s)
+        fn(s)
+        b.record(s)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
+def time_router(N, W, wl, bufs, n: int) -> dict:
+    """The router logits (fp32 [T, D] x [E, D], D = H) alone and the full
+    routing chain (logits, then moe_route into the layer's buffers). Bytes:
+    the input, the weight and the logits, each moved once."""
+    import torch
+    xr, wr = W.make_router_inputs(wl)
+    x = torch.from_numpy(xr).to(bufs.ids.device)
+    w = torch.from_numpy(wr).to(bufs.ids.device)
+    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=x.device)
+    us_l = _event_us(lambda s: N.moe_router_logits(x, w, logits, s), n)
+    us_c = _event_us(lambda s: N.moe_router_route(x, w, None, None, wl.K, 1.0, wl.tile_m, 0, wl.E, logits,
+                                                  bufs.ids, bufs.weights, bufs.meta, s), n)
+    nbytes = 4 * (wl.T * wl.H + wl.E * wl.H + wl.T * wl.E)
+    gbs = nbytes / (us_l * 1e-6) / 1e9
+    return {"moe_router_logits": {"us": us_l, "bytes": nbytes, "achieved": gbs, "unit": "GB/s",
+                                  "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+                                  "bound": "hbm" if wl.T <= 64 else "fp64 alu"},
+            "moe_router_route": {"us": us_c}}
+
+
 def cpu_baseline(inp, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
     from oracle.layer import layer as o_layer
@@ -247,7 +284,8 @@ def main():
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                            "experts_touched": ab["touched"], "kernel_ms": k_ms}
-    out["extra_kernels"] = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
+    out["extra_kernels"] = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k),
+                            **time_router(N, W, wl, bufs, n_k)}
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -135,6 +135,32 @@ int moe_route(const float* logits, int64_t logits_row_stride, const float* exper
               int local_expert_offset, int local_num_experts, int32_t* topk_ids,
               float* topk_weights, int32_t* meta, void* stream);
 
+/* ------------------------------------------------------------------ router
+ * The router's linear layer (the model page, "MuseSpark1xMoE": GateLinear from
+ * the router input to the E local experts, no bias, fp32 parameters and
+ * output; the model's router output multiplier is folded into the weight as it
+ * loads, "_load_router_weight"; the router input is fp32 on the decode path,
+ * "wants_fp32_router_input"):
+ *   logits[t, e] = fp32( sum_d x[t, d] * w_router[e, d] )
+ * the products exact and the sum accumulated in fp64, rounded once to fp32.
+ *   x         device fp32 [T, D], row stride x_row_stride elements (>= D, % 4 == 0)
+ *   w_router  device fp32 [E, D], contiguous
+ *   logits    device fp32 [T, E] out, contiguous
+ * D % 4 == 0, E <= MOE_MAX_EXPERTS. One launch on `stream`. */
+int moe_router_logits(const float* x, int64_t x_row_stride, const float* w_router, int T, int D,
+                      int E, float* logits, void* stream);
+
+/* The full routing chain (the model page, "_route_topk_and_pool": the router,
+ * then "_compute_routing" on its logits): moe_router_logits into `logits`,
+ * then moe_route(logits, E, ...) with the remaining arguments, on `stream`; the
+ * same outputs as those two calls, bit for bit. Every check of both calls runs
+ * before the first launch. */
+int moe_router_route(const float* x, int64_t x_row_stride, const float* w_router, int D,
+                     const float* expert_bias, const uint8_t* is_padding, int T, int E, int K,
+                     float route_scale, int tile_m, int local_expert_offset, int local_num_experts,
+                     float* logits, int32_t* topk_ids, float* topk_weights, int32_t* meta,
+                     void* stream);
+
 /* ------------------------------------------------------------------ quantizer
  * NVFP4 quantization of the expert input with one global scale, scales in the
  * plain row-major layout (the model page, "_prepared_nvfp4_forward":

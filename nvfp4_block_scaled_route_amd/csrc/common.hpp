@@ -16,6 +16,11 @@ int fail(int code, const char* fmt, ...);          // sets the thread's message,
 int quant_check(const uint16_t* x, int64_t x_row_stride, const float* gscale, int T, int H,
                 uint8_t* codes, uint8_t* sf, const char* name);   // nvfp4_quant's validation
 int check_launch(const char* what);                // MOE_ELAUNCH on a pending launch error
+// moe_route's validation (shared with moe_router_route, which runs it before
+// its first launch)
+int moe_route_check(int T, int E, int K, int tile_m, int local_expert_offset, int local_num_experts,
+                    int64_t logits_row_stride, const float* logits, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* meta, const char* name);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m);
 // int32 words between the sync counters of consecutive 16-row tiles in the

@@ -438,12 +438,9 @@ static size_t permute_lds_bytes(int El) {
     return sizeof(int32_t) * ((size_t)(kRouteWaves + 3) * El + 1 + kRouteWaves);
 }
 
-static int route_launch(const float* logits, int64_t logits_row_stride, const float* expert_bias,
-                        const uint8_t* is_padding, int T, int E, int K, float route_scale,
-                        int tile_m, int local_expert_offset, int local_num_experts,
-                        int32_t* topk_ids, float* topk_weights, int32_t* meta,
-                        const uint16_t* x, int64_t x_row_stride, const float* gscale, int H,
-                        uint8_t* codes, uint8_t* sf, void* stream, const char* name) {
+int moe_route_check(int T, int E, int K, int tile_m, int local_expert_offset, int local_num_experts,
+                    int64_t logits_row_stride, const float* logits, const int32_t* topk_ids,
+                    const float* topk_weights, const int32_t* meta, const char* name) {
     if (T < 0) return fail(MOE_EINVAL, "%s: T=%d", name, T);
     if (E < 1 || E > MOE_MAX_EXPERTS)
         return fail(MOE_EUNSUPPORTED, "%s: E=%d outside [1, %d]", name, E, MOE_MAX_EXPERTS);
@@ -463,6 +460,18 @@ static int route_launch(const float* logits, int64_t logits_row_stride, const fl
                                         !aligned16(topk_weights))))
         return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
     if ((int64_t)T * K > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too many routes", name);
+    return MOE_OK;
+}
+
+static int route_launch(const float* logits, int64_t logits_row_stride, const float* expert_bias,
+                        const uint8_t* is_padding, int T, int E, int K, float route_scale,
+                        int tile_m, int local_expert_offset, int local_num_experts,
+                        int32_t* topk_ids, float* topk_weights, int32_t* meta,
+                        const uint16_t* x, int64_t x_row_stride, const float* gscale, int H,
+                        uint8_t* codes, uint8_t* sf, void* stream, const char* name) {
+    const int rc = moe_route_check(T, E, K, tile_m, local_expert_offset, local_num_experts, logits_row_stride,
+                                   logits, topk_ids, topk_weights, meta, name);
+    if (rc != MOE_OK) return rc;
     RouteArgs a;
     a.logits = logits; a.logits_row_stride = logits_row_stride; a.bias = expert_bias;
     a.is_padding = is_padding; a.T = T; a.E = E; a.K = K; a.route_scale = route_scale;

@@ -19,7 +19,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 # Every symbol include/moe_nvfp4.h declares.
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout_get",
            "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
-           "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant")
+           "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant", "moe_router_logits",
+           "moe_router_route")
 
 
 class MoeMetaLayout(ctypes.Structure):
@@ -63,6 +64,9 @@ def lib() -> ctypes.CDLL:
         "moe_route": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp]),
         "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp]),
         "nvfp4_norm_quant": (i32, [vp, i64, vp, f32, f32, vp, i32, i32, vp, vp, vp]),
+        "moe_router_logits": (i32, [vp, i64, vp, i32, i32, i32, vp, vp]),
+        "moe_router_route": (i32, [vp, i64, vp, i32, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp,
+                                   vp, vp, vp]),
         "moe_route_quant": (i32, [vp, i64, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
                                   vp, i64, vp, i32, vp, vp, vp]),
         "moe_pack_w13": (i32, [vp, vp, i32, i32, i32, vp, vp, vp]),
@@ -133,6 +137,21 @@ def nvfp4_norm_quant(x, norm_weight, gain_center, eps, gscale, codes, sf, stream
     _check(lib().nvfp4_norm_quant(_ptr(x), x.stride(0), _ptr(norm_weight), gain_center, eps,
                                   _ptr(gscale), T, H, _ptr(codes), _ptr(sf), _stream(stream)),
            "nvfp4_norm_quant")
+
+
+def moe_router_logits(x, w_router, logits, stream=None) -> None:
+    T, D = x.shape
+    _check(lib().moe_router_logits(_ptr(x), x.stride(0), _ptr(w_router), T, D, w_router.shape[0],
+                                   _ptr(logits), _stream(stream)), "moe_router_logits")
+
+
+def moe_router_route(x, w_router, expert_bias, is_padding, K, route_scale, tile_m, local_expert_offset,
+                     local_num_experts, logits, topk_ids, topk_weights, meta, stream=None) -> None:
+    T, D = x.shape
+    _check(lib().moe_router_route(_ptr(x), x.stride(0), _ptr(w_router), D, _ptr(expert_bias),
+                                  _ptr(is_padding), T, w_router.shape[0], K, route_scale, tile_m,
+                                  local_expert_offset, local_num_experts, _ptr(logits), _ptr(topk_ids),
+                                  _ptr(topk_weights), _ptr(meta), _stream(stream)), "moe_router_route")
 
 
 def moe_route_quant(logits, expert_bias, is_padding, K, route_scale, tile_m, local_expert_offset,

@@ -65,6 +65,13 @@ def test_invalid_sizes_are_refused():
         (L.nvfp4_quant, (None, 24, None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),   # H % 16
         (L.nvfp4_quant, (None, 32, None, 4, 32, None, None, None), N.MOE_EINVAL),         # NULL
         (L.nvfp4_norm_quant, (None, 24, None, f(1.0), f(1e-6), None, 4, 24, None, None, None), N.MOE_EUNSUPPORTED),
+        (L.moe_router_logits, (None, 64, None, 4, 62, 8, None, None), N.MOE_EUNSUPPORTED),        # D % 4
+        (L.moe_router_logits, (None, 64, None, 4, 64, 8, None, None), N.MOE_EINVAL),              # NULL
+        (L.moe_router_logits, (16, 60, 16, 4, 64, 8, 16, None), N.MOE_EINVAL),                    # stride < D
+        (L.moe_router_route, (16, 64, 16, 64, None, None, 4, 8, 9, f(1.0), 16, 0, 8, 16, 16, 16, 16, None),
+         N.MOE_EUNSUPPORTED),                                                                       # K > E
+        (L.moe_router_route, (16, 64, 16, 64, None, None, 4, 8, 2, f(1.0), 16, 0, 8, 16, 16, 16, None, None),
+         N.MOE_EINVAL),                                                                             # NULL meta
         (L.nvfp4_norm_quant, (None, 32, None, f(1.0), f(1e-6), None, 4, 32, None, None, None), N.MOE_EINVAL),
         (L.nvfp4_norm_quant, (16, 32, None, f(1.0), f(0.0), 16, 4, 32, 16, 16, None), N.MOE_EINVAL),   # eps 0
         (L.nvfp4_norm_quant, (16, 32 * 1024, None, f(1.0), f(1e-6), 16, 4, 32 * 1024, 16, 16, None), N.MOE_EUNSUPPORTED),
