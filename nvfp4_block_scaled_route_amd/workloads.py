@@ -83,7 +83,7 @@ ORDER = ["tiny", "decode_b8", "decode_b64_zipf", "prefill_t4096", "expert_tp8_b3
 
 _STREAMS = ["x", "outlier_mask", "logits", "zipf_perm", "w13_codes", "w13_sf",
             "w2_codes", "w2_sf", "g1_alphas", "g1_scale_c", "g2_alphas", "gamma",
-            "router_x", "router_w"]
+            "router_x", "router_w", "gs_gate", "gs_up", "gs_w2"]
 
 
 def _rng(seed: int, stream: str) -> np.random.Generator:
@@ -137,6 +137,14 @@ def make_router_inputs(wl: Workload, seed: int | None = None, tokens: int | None
     w = (_rng(seed, "router_w").standard_normal((wl.E, wl.H), dtype=np.float32)
          * np.float32(1.0 / np.sqrt(wl.H))).astype(np.float32)
     return x, w
+
+
+def make_weight_global_scales(wl: Workload, seed: int | None = None):
+    """Per-expert fp32 weight global scales of the W4A16 variant: the gate and
+    up halves of w13 and w2, each U[0.5, 1.5]."""
+    seed = wl.seed if seed is None else seed
+    return tuple(_rng(seed, s).uniform(0.5, 1.5, wl.E).astype(np.float32)
+                 for s in ("gs_gate", "gs_up", "gs_w2"))
 
 
 def make_weights(wl: Workload, seed: int | None = None):
