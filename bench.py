@@ -153,6 +153,28 @@ def time_router(N, W, wl, bufs, n: int) -> dict:
             "moe_router_route": {"us": us_c}}
 
 
+def time_w4a16(N, wl, x, bufs, weights, ab: dict, n: int) -> dict:
+    """The W4A16 expert step (bf16 activations, the same NVFP4 weights) on the
+    layer's routing, weight copies rotated as in the main measurement: the same
+    weight bytes, plus bf16 activations and a bf16 intermediate."""
+    import torch
+    L = bufs.layout
+    inter = torch.empty((L.rows_max, wl.I), dtype=torch.int16, device=x.device)
+    k = [0]
+
+    def call(s):
+        w = weights[k[0] % len(weights)]
+        k[0] += 1
+        N.moe_experts_fwd_w4a16(x, bufs.meta, w, wl.T, wl.K, wl.E, wl.H, wl.I, wl.tile_m, inter, bufs.rows[0], s)
+
+    us = _event_us(call, n)
+    routes = wl.T * wl.K
+    nbytes = ab["weights"] + wl.T * wl.H * 2 + 2 * routes * wl.I * 2 + routes * wl.H * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": us, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+
+
 def cpu_baseline(inp, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
     from oracle.layer import layer as o_layer
@@ -284,8 +306,11 @@ def main():
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                            "experts_touched": ab["touched"], "kernel_ms": k_ms}
-    out["extra_kernels"] = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k),
-                            **time_router(N, W, wl, bufs, n_k)}
+    extra = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
+    if wl.tp == 1 and not mfma_bound(wl):          # on the layer's routing, before the router rewrites it
+        extra["moe_experts_fwd_w4a16"] = time_w4a16(N, wl, x, bufs, weights, ab, n_k)
+    extra.update(time_router(N, W, wl, bufs, n_k))
+    out["extra_kernels"] = extra
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

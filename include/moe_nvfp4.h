@@ -307,6 +307,30 @@ int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
                     int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
                     int64_t rows_stride, void* stream);
 
+/* ------------------------------------------------------------------ experts, W4A16
+ * The W4A16 variant of the routed experts: bf16 activations, not quantized,
+ * against the same converted NVFP4 weights (the runner page,
+ * "MuseSparkModelOptNvFp4FusedMoE": route-major W4A16 GEMMs with SwiGLU;
+ * "_process_hopper_marlin_weights": GEMM1 applies the gate's weight global
+ * scale to both halves of w13, "keeping the SiLU gate input exact", and GEMM2's
+ * global scale carries the up/gate ratio). For every permuted row p that holds
+ * a route (token t = perm2tok[p], expert e of its tile):
+ *   acc1[n]    = sum_h x[t, h] * dq(w13[e, n, h])           n < 2I, fp32 accumulate
+ *   inter[p,i] = bf16(silu(acc1_gate * s13[e]) * (acc1_up * s13[e]))   nearest even
+ *   rows[p, n] = bf16(sum_i inter[p, i] * dq(w2[e, n, i]) * s2[e])
+ * with s13 = w->g1_alphas (the gate's global scale) and s2 = w->g2_alphas
+ * (w2's global scale times up/gate, formed by the caller); w->g1_scale_c is
+ * not read. Products of bf16 and NVFP4 values are exact in fp32.
+ *   x       device bf16 [T, H], row stride x_row_stride elements (>= H, % 8 == 0)
+ *   meta    moe_route's metadata for the same T, K, E_local, tile_m (read only)
+ *   inter   device bf16 [rows_max, I] out: the intermediate, permuted row order
+ *   rows    device bf16 [rows_max, rows_stride] out, as moe_experts_fwd
+ * Two launches on `stream`. H % 64 == 0, I % 64 == 0, both <= MOE_MAX_HIDDEN. */
+int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+                          const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                          int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
+                          void* stream);
+
 /* ------------------------------------------------------------------ finalize
  * Post-expert finalize (the runner page, "MusePostExpertFinalize",
  * "_finalize_native", "_finalize_chunk", "_effective_weight"): for each token t

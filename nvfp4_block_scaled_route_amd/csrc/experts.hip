@@ -124,31 +124,6 @@ __device__ __forceinline__ void stream_unit(const Streams& p, int KT, floatx4& a
     }
 }
 
-// The unit's 16-row tile: expert (-1: no unit) and the lane's row token.
-struct RowTile {
-    int e;
-    int row0;
-    int tok;                // token of row n (lane & 15), -1 for a padding row
-    uint32_t vmask;         // bit m: row m holds a route
-};
-
-__device__ __forceinline__ RowTile row_tile(const ExpArgs& a, int sub, int n) {
-    RowTile r;
-    const int per_tile = a.tile_m >> 4;
-    const int t = (int)((uint32_t)sub / (uint32_t)per_tile);
-    // Both metadata loads go out before any decision: the tile index is clamped
-    // so that they stay in bounds for units past the last tile.
-    const int tc = min(t, (int)a.L.tiles_max - 1);
-    r.row0 = tc * a.tile_m + (sub - t * per_tile) * 16;
-    const int e = a.meta[a.L.tile_expert + tc];
-    int tok = a.meta[a.L.perm2tok + r.row0 + n];
-    if (tok >= a.T) tok = -1;
-    r.tok = tok;
-    r.vmask = (uint32_t)(__ballot(tok >= 0) & 0xFFFFull);
-    r.e = (t < a.L.tiles_max && e >= 0 && e < a.E_local && r.vmask) ? e : -1;
-    return r;
-}
-
 // ---------------------------------------------------------------- epilogues
 // Agent-coherent stores (sc1): visible to agent-coherent loads on every XCD
 // once they have completed, without a write-back of the writer's L2.
@@ -189,21 +164,6 @@ __device__ __forceinline__ void gemm1_epilogue(const ExpArgs& a, const RowTile& 
                 if ((n & 7) == 0) *reinterpret_cast<uint32_t*>(cp) = b;
                 if (n == 0) *sp = (uint8_t)bs.byte;
             }
-        }
-    }
-}
-
-// GEMM2: lane (q, n) holds rows 4q + i of output columns 32c + n and 32c + 16 + n.
-__device__ __forceinline__ void gemm2_epilogue(const ExpArgs& a, const RowTile& rt, int e, int c, int n, int q,
-                                               const floatx4& acc0, const floatx4& acc1) {
-    const float alpha = a.w.g2_alphas[e];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;
-        if ((rt.vmask >> m) & 1u) {
-            uint16_t* out = a.rows + (int64_t)(rt.row0 + m) * a.rows_stride + c * 32 + n;
-            out[0] = (uint16_t)f32_to_bf16(acc0[i] * alpha);
-            out[16] = (uint16_t)f32_to_bf16(acc1[i] * alpha);
         }
     }
 }

@@ -1,0 +1,237 @@
+// moe_experts_fwd_w4a16: the W4A16 variant of the routed experts -- bf16
+// activations against the same converted NVFP4 weights (the runner page,
+// "MuseSparkModelOptNvFp4FusedMoE": route-major W4A16 GEMMs with SwiGLU;
+// "_process_hopper_marlin_weights": one global scale, the gate's, for both
+// halves of w13, and the up side's ratio up/gate folded into GEMM2's scale).
+//
+//   GEMM1  acc1 = x(t) . dq(w13[e])^T         x: the bf16 input row of token t
+//   act    h = bf16(silu(acc_gate * s13[e]) * (acc_up * s13[e]))
+//   GEMM2  rows = bf16(h . dq(w2[e])^T * s2[e])
+//
+// Operands: a bf16 activation times an NVFP4 weight (e2m1 * e4m3: at most 6
+// significant bits, between 2^-10 and 2688) is exact in fp32, so both GEMMs run
+// v_mfma_f32_16x16x32_bf16. The weight decode is exact too: 8 codes to fp32 at
+// scale 1, times the e4m3 block scale in fp32 (the hardware conversion applies
+// only its scale operand's exponent), then packed to bf16 (exact: 6 bits).
+// The K index is permuted as in the W4A4 kernels: lane (q, n) takes 16-element
+// block q of every 64-wide k-tile, for row n of both operands, so the weight
+// slot of the converted layout is again one 16-byte load; the activation block
+// is 32 bytes of row n.
+//
+// Decode is bound by the weight stream; one wave is one unit (16 routed rows x
+// one gate/up pair for GEMM1, 16 rows x 32 output columns for GEMM2) over all of
+// K through a D-stage register pipeline, activations read from the cache (they
+// are 64 times smaller than the weights at decode).
+#include "experts.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+constexpr int kW16Threads = 256;   // 4 independent waves per workgroup
+
+struct W16Args {
+    const uint16_t* x;          // GEMM1: bf16 [T, x_row_stride]; GEMM2: the intermediate
+    int64_t x_row_stride;
+    ExpArgs e;                  // metadata, weights (g1_alphas = s13, g2_alphas = s2), shape, rows
+    uint16_t* inter;            // bf16 [rows_max, I]
+};
+
+struct W16Stage {
+    uint4 w;         // weight slot: half 0 elements 0-7, 8-15, half 1 elements 0-7, 8-15
+    uint32_t wsf;    // e4m3 scales of half 0 (bits 0-7) and half 1 (bits 8-15)
+    uint4 a0, a1;    // bf16 activation elements 0-7 and 8-15 of the lane's block
+};
+
+struct W16Streams {
+    const uint8_t* wc;
+    const uint8_t* ws;
+    const uint16_t* a;          // k-tile c at + 64 c elements
+};
+
+__device__ __forceinline__ void w16_load(W16Stage& st, const W16Streams& p, int c) {
+    st.w = *reinterpret_cast<const uint4*>(p.wc + (int64_t)c * kSlotBytes);
+    st.wsf = *reinterpret_cast<const uint16_t*>(p.ws + (int64_t)c * kSlotSfBytes);
+    const uint4* a = reinterpret_cast<const uint4*>(p.a + c * 64);
+    st.a0 = a[0];
+    st.a1 = a[1];
+}
+
+// 8 e2m1 codes times one fp32 block scale -> 8 exact bf16 values.
+template <int B>
+__device__ __forceinline__ void fp4x2_to_bf16(uint32_t codes, float s, bf16x8& out) {
+    const floatx2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, B);
+    out[2 * B] = (__bf16)__fmul_rn(f[0], s);
+    out[2 * B + 1] = (__bf16)__fmul_rn(f[1], s);
+}
+
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float s) {
+    bf16x8 out;
+    fp4x2_to_bf16<0>(codes, s, out);
+    fp4x2_to_bf16<1>(codes, s, out);
+    fp4x2_to_bf16<2>(codes, s, out);
+    fp4x2_to_bf16<3>(codes, s, out);
+    return out;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ void w16_use(const W16Stage& st, floatx4& acc0, floatx4& acc1) {
+    const floatx2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.wsf, 1.0f, false);
+    const bf16x8 a0 = as_bf16x8(st.a0), a1 = as_bf16x8(st.a1);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp4x8_to_bf16(st.w.x, s[0]), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp4x8_to_bf16(st.w.z, s[1]), acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp4x8_to_bf16(st.w.y, s[0]), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp4x8_to_bf16(st.w.w, s[1]), acc1, 0, 0, 0);
+}
+
+// All KT k-tiles through a D-deep pipeline (KT % D == 0); loads of a stage
+// issue together and in stage order (vmcnt drains in issue order).
+template <int D>
+__device__ __forceinline__ void w16_stream(const W16Streams& p, int KT, floatx4& acc0, floatx4& acc1) {
+    W16Stage st[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        w16_load(st[d], p, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int c0 = 0;
+    for (; c0 + D < KT; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            w16_use(st[d], acc0, acc1);
+            w16_load(st[d], p, c0 + D + d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        w16_use(st[d], acc0, acc1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// GEMM1 unit (16 routed rows, intermediate pair j); lane (q, n) ends with rows
+// 4q + i of intermediate 16j + n, gate and up.
+template <int D>
+__global__ void __launch_bounds__(kW16Threads) w16_gemm1_kernel(W16Args a) {
+    const ExpArgs& e = a.e;
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const uint32_t unit = blockIdx.x * (kW16Threads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n1 = e.I >> 4;
+    const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
+    const RowTile rt = row_tile(e, sub, n);
+    if (rt.e < 0) return;
+    const int ex = rt.e;
+    W16Streams p;
+    p.wc = e.w.w13 + ex * e.w.w13_expert_stride_bytes + j * e.w.w13_pair_stride_bytes + lane * 16;
+    p.ws = e.w.w13_sf + ex * e.w.w13_sf_expert_stride_bytes + j * e.w.w13_sf_pair_stride_bytes + lane * 2;
+    const int64_t tok = rt.tok >= 0 ? rt.tok : 0;   // padding rows read token 0's row, never written
+    p.a = a.x + tok * a.x_row_stride + q * 16;
+    floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
+    w16_stream<D>(p, e.H >> 6, acc_g, acc_u);
+    const float s13 = e.w.g1_alphas[ex];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;
+        const float g = __fmul_rn(acc_g[i], s13);
+        const float u = __fmul_rn(acc_u[i], s13);
+        // silu(g) = g * sigmoid(g) with sigmoid from e^-|g| (never overflows): a
+        // bf16 intermediate keeps the tiny values of strongly negative gates,
+        // which g / (1 + e^-g) would flush to zero once e^-g overflows
+        const float eg = expf(-__builtin_fabsf(g));
+        const float sig = __fdiv_rn(g >= 0.0f ? 1.0f : eg, __fadd_rn(1.0f, eg));
+        const float h = __fmul_rn(__fmul_rn(g, sig), u);
+        if ((rt.vmask >> m) & 1u) a.inter[(int64_t)(rt.row0 + m) * e.I + j * 16 + n] = (uint16_t)f32_to_bf16(h);
+    }
+}
+
+// GEMM2 unit (16 routed rows, output pair c) on the bf16 intermediate.
+template <int D>
+__global__ void __launch_bounds__(kW16Threads) w16_gemm2_kernel(W16Args a) {
+    const ExpArgs& e = a.e;
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const uint32_t unit = blockIdx.x * (kW16Threads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n2 = e.H >> 5;
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
+    const RowTile rt = row_tile(e, sub, n);
+    if (rt.e < 0) return;
+    const int ex = rt.e;
+    W16Streams p;
+    p.wc = e.w.w2 + ex * e.w.w2_expert_stride_bytes + c * e.w.w2_pair_stride_bytes + lane * 16;
+    p.ws = e.w.w2_sf + ex * e.w.w2_sf_expert_stride_bytes + c * e.w.w2_sf_pair_stride_bytes + lane * 2;
+    p.a = a.inter + (int64_t)(rt.row0 + n) * e.I + q * 16;
+    floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    w16_stream<D>(p, e.I >> 6, acc0, acc1);
+    gemm2_epilogue(e, rt, ex, c, n, q, acc0, acc1);
+}
+
+static int w16_depth(int kt) { return kt % 4 == 0 ? 4 : kt % 2 == 0 ? 2 : 1; }
+
+}  // namespace moe
+
+extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+                                     const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                                     int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
+                                     void* stream) {
+    using namespace moe;
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E_local < 1 || E_local > MOE_MAX_EXPERTS)
+        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: T=%d K=%d E_local=%d out of range", T, K, E_local);
+    if (H < 64 || H % 64 || I < 64 || I % 64 || H > MOE_MAX_HIDDEN || I > MOE_MAX_HIDDEN)
+        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd_w4a16: H=%d and I=%d must be multiples of 64 up to %d", H, I,
+                    MOE_MAX_HIDDEN);
+    if (tile_m < 16 || tile_m > 256 || tile_m % 16)
+        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd_w4a16: tile_m=%d must be a multiple of 16 in [16, 256]",
+                    tile_m);
+    if (!w || !meta) return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: NULL weights or meta");
+    if (T == 0) return MOE_OK;
+    if (!x || !inter || !rows || !w->w13 || !w->w13_sf || !w->w2 || !w->w2_sf || !w->g1_alphas || !w->g2_alphas)
+        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: NULL pointer");
+    const void* ptrs[] = {x, meta, inter, rows, w->w13, w->w13_sf, w->w2, w->w2_sf, w->g1_alphas, w->g2_alphas};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: pointers must be 16-byte aligned");
+    if (x_row_stride < H || x_row_stride % 8)
+        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: x row stride must be >= H and a multiple of 8");
+    if (rows_stride < H || rows_stride % 8)
+        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: rows_stride must be >= H and a multiple of 8");
+    const int64_t kt1 = H / 64, kt2 = I / 64;
+    if (w->w13_pair_stride_bytes < kt1 * kSlotBytes || w->w13_sf_pair_stride_bytes < kt1 * kSlotSfBytes ||
+        w->w2_pair_stride_bytes < kt2 * kSlotBytes || w->w2_sf_pair_stride_bytes < kt2 * kSlotSfBytes ||
+        w->w13_expert_stride_bytes < (int64_t)(I / 16) * w->w13_pair_stride_bytes ||
+        w->w13_sf_expert_stride_bytes < (int64_t)(I / 16) * w->w13_sf_pair_stride_bytes ||
+        w->w2_expert_stride_bytes < (int64_t)(H / 32) * w->w2_pair_stride_bytes ||
+        w->w2_sf_expert_stride_bytes < (int64_t)(H / 32) * w->w2_sf_pair_stride_bytes ||
+        (w->w13_pair_stride_bytes | w->w13_sf_pair_stride_bytes | w->w2_pair_stride_bytes |
+         w->w2_sf_pair_stride_bytes | w->w13_expert_stride_bytes | w->w13_sf_expert_stride_bytes |
+         w->w2_expert_stride_bytes | w->w2_sf_expert_stride_bytes) % 16)
+        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: weight strides too small or not multiples of 16");
+    W16Args a;
+    a.x = x; a.x_row_stride = x_row_stride; a.inter = inter;
+    a.e.meta = meta; a.e.L = meta_layout(T, K, E_local, tile_m);
+    a.e.w = *w; a.e.T = T; a.e.E_local = E_local; a.e.H = H; a.e.I = I; a.e.tile_m = tile_m;
+    a.e.rows = rows; a.e.rows_stride = rows_stride;
+    a.e.a_codes = nullptr; a.e.a_sf = nullptr; a.e.inter_codes = nullptr; a.e.inter_sf = nullptr;
+    a.e.sync = nullptr; a.e.status = nullptr;
+    if (a.e.L.rows_max == 0) return MOE_OK;
+    const int64_t subs = a.e.L.rows_max / 16;
+    const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
+    if (units1 > 0x7FFFFFFF || units2 > 0x7FFFFFFF)
+        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd_w4a16: too many work units");
+    const int wpb = kW16Threads / 64;
+    const dim3 g1((unsigned)((units1 + wpb - 1) / wpb)), g2((unsigned)((units2 + wpb - 1) / wpb)), b(kW16Threads);
+    hipStream_t s = (hipStream_t)stream;
+    switch (w16_depth((int)kt1)) {
+        case 4: hipLaunchKernelGGL(w16_gemm1_kernel<4>, g1, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(w16_gemm1_kernel<2>, g1, b, 0, s, a); break;
+        default: hipLaunchKernelGGL(w16_gemm1_kernel<1>, g1, b, 0, s, a); break;
+    }
+    int rc = check_launch("moe_experts_fwd_w4a16 (GEMM1)");
+    if (rc) return rc;
+    switch (w16_depth((int)kt2)) {
+        case 4: hipLaunchKernelGGL(w16_gemm2_kernel<4>, g2, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL(w16_gemm2_kernel<2>, g2, b, 0, s, a); break;
+        default: hipLaunchKernelGGL(w16_gemm2_kernel<1>, g2, b, 0, s, a); break;
+    }
+    return check_launch("moe_experts_fwd_w4a16 (GEMM2)");
+}

@@ -109,6 +109,17 @@ def test_experts_refusals():
     assert b"stride" in L.moe_last_error()
 
 
+def test_experts_w4a16_refusals():
+    L = N.lib()
+    w = N.MoeNvfp4Weights()
+    args = lambda H, I, m: (None, H, None, ctypes.byref(w), 4, 2, 8, H, I, m, None, None, H, None)
+    assert L.moe_experts_fwd_w4a16(*args(96, 128, 16)) == N.MOE_EUNSUPPORTED     # H % 64
+    assert L.moe_experts_fwd_w4a16(*args(256, 96, 16)) == N.MOE_EUNSUPPORTED     # I % 64
+    assert L.moe_experts_fwd_w4a16(*args(256, 128, 24)) == N.MOE_EUNSUPPORTED    # tile
+    assert L.moe_experts_fwd_w4a16(*args(256, 128, 16)) == N.MOE_EINVAL          # NULL pointers
+    assert L.moe_experts_fwd_w4a16(None, 256, None, None, 4, 2, 8, 256, 128, 16, None, None, 256, None) == N.MOE_EINVAL
+
+
 def test_zero_tokens_is_a_no_op_without_device():
     L = N.lib()
     assert L.nvfp4_quant(None, 64, None, 0, 64, None, None, None) == N.MOE_OK
