@@ -83,7 +83,7 @@ ORDER = ["tiny", "decode_b8", "decode_b64_zipf", "prefill_t4096", "expert_tp8_b3
 
 _STREAMS = ["x", "outlier_mask", "logits", "zipf_perm", "w13_codes", "w13_sf",
             "w2_codes", "w2_sf", "g1_alphas", "g1_scale_c", "g2_alphas", "gamma",
-            "router_x", "router_w", "gs_gate", "gs_up", "gs_w2"]
+            "router_x", "router_w", "gs_gate", "gs_up", "gs_w2", "bf16_w13", "bf16_w2"]
 
 
 def _rng(seed: int, stream: str) -> np.random.Generator:
@@ -145,6 +145,16 @@ def make_weight_global_scales(wl: Workload, seed: int | None = None):
     seed = wl.seed if seed is None else seed
     return tuple(_rng(seed, s).uniform(0.5, 1.5, wl.E).astype(np.float32)
                  for s in ("gs_gate", "gs_up", "gs_w2"))
+
+
+def make_bf16_weights(wl: Workload, seed: int | None = None):
+    """bf16 expert weights for the BF16 expert layers, logical layout:
+    w13 [E, 2I, H] (gate rows first) ~ N(0, 1/H), w2 [E, H, I] ~ N(0, 1/I)."""
+    seed = wl.seed if seed is None else seed
+    E, H, I = wl.E, wl.H, wl.I
+    w13 = _rng(seed, "bf16_w13").standard_normal((E, 2 * I, H), dtype=np.float32) * np.float32(H ** -0.5)
+    w2 = _rng(seed, "bf16_w2").standard_normal((E, H, I), dtype=np.float32) * np.float32(I ** -0.5)
+    return to_bf16_bits(w13), to_bf16_bits(w2)
 
 
 def make_weights(wl: Workload, seed: int | None = None):
