@@ -175,6 +175,36 @@ def time_w4a16(N, wl, x, bufs, weights, ab: dict, n: int) -> dict:
             "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
 
 
+def time_bf16(N, W, wl, x, bufs, counts, n: int) -> dict:
+    """The BF16 expert layers' GEMMs (bf16 weights: 6 I H bytes per expert) on
+    the layer's routing; two weight copies alternate so that the 256 MB
+    Infinity Cache does not hold the next call's weights."""
+    import torch
+    w13h, w2h = W.make_bf16_weights(wl)
+    dev = x.device
+    copies = [(torch.from_numpy(w13h.view(np.int16)).to(dev), torch.from_numpy(w2h.view(np.int16)).to(dev))
+              for _ in range(2)]
+    del w13h, w2h
+    inter = torch.empty((bufs.layout.rows_max, wl.I), dtype=torch.int16, device=dev)
+    k = [0]
+
+    def call(s):
+        w13, w2 = copies[k[0] % 2]
+        k[0] += 1
+        N.moe_experts_fwd_bf16(x, bufs.meta, w13, w2, wl.T, wl.K, wl.E, wl.H, wl.I, wl.tile_m, inter,
+                               bufs.rows[0], s)
+
+    us = _event_us(call, n)
+    routes = wl.T * wl.K
+    touched = int((counts > 0).sum())
+    nbytes = touched * 6 * wl.I * wl.H + wl.T * wl.H * 2 + 2 * routes * wl.I * 2 + routes * wl.H * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del copies
+    torch.cuda.empty_cache()
+    return {"us": us, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+
+
 def cpu_baseline(inp, seconds: float) -> dict:
     from threadpoolctl import threadpool_info
     from oracle.layer import layer as o_layer
@@ -309,6 +339,8 @@ def main():
     extra = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
     if wl.tp == 1 and not mfma_bound(wl):          # on the layer's routing, before the router rewrites it
         extra["moe_experts_fwd_w4a16"] = time_w4a16(N, wl, x, bufs, weights, ab, n_k)
+        if wl.E * 3 * wl.H * wl.I * 2 <= 1 << 30:   # bf16 weights of at most 1 GiB
+            extra["moe_experts_fwd_bf16"] = time_bf16(N, W, wl, x, bufs, counts, n_k)
     extra.update(time_router(N, W, wl, bufs, n_k))
     out["extra_kernels"] = extra
     if args.cpu_seconds > 0:

@@ -331,6 +331,25 @@ int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, const int32_t
                           int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
                           void* stream);
 
+/* ------------------------------------------------------------------ experts, BF16 layers
+ * The routed experts of the BF16 layers (the flashinfer_ops page,
+ * "routed_experts_bf16", "bf16_arguments": the same routing on the router
+ * logits, bf16 w13 and w2, unfinalized rows; the runner page,
+ * "MuseSparkUnquantizedFusedMoE"). The routing is moe_route's; this call runs
+ * the GEMMs on its metadata. For every permuted row p that holds a route:
+ *   acc1[n]    = sum_h x[t, h] * w13[e, n, h]         n < 2I (gate rows first), fp32 accumulate
+ *   inter[p,i] = bf16(silu(acc1_gate[i]) * acc1_up[i])
+ *   rows[p, n] = bf16(sum_i inter[p, i] * w2[e, n, i])
+ *   x      device bf16 [T, H], row stride x_row_stride elements (>= H, % 8 == 0)
+ *   meta   moe_route's metadata for the same T, K, E_local, tile_m (read only)
+ *   w13    device bf16 [E_local, 2I, H], w2 device bf16 [E_local, H, I], contiguous
+ *   inter  device bf16 [rows_max, I] out;  rows as moe_experts_fwd
+ * Two launches on `stream`. H % 64 == 0, I % 64 == 0, both <= MOE_MAX_HIDDEN. */
+int moe_experts_fwd_bf16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+                         const uint16_t* w13, const uint16_t* w2, int T, int K, int E_local, int H,
+                         int I, int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
+                         void* stream);
+
 /* ------------------------------------------------------------------ finalize
  * Post-expert finalize (the runner page, "MusePostExpertFinalize",
  * "_finalize_native", "_finalize_chunk", "_effective_weight"): for each token t

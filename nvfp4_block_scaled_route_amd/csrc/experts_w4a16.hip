@@ -38,21 +38,44 @@ struct W16Args {
     uint16_t* inter;            // bf16 [rows_max, I]
 };
 
-struct W16Stage {
-    uint4 w;         // weight slot: half 0 elements 0-7, 8-15, half 1 elements 0-7, 8-15
+// A lane's weight operands of one k-tile: 16 elements (block q) of its row in
+// both halves (half 0, half 1), as they arrive from memory.
+template <bool kBf16> struct WSlot;
+template <> struct WSlot<false> {   // NVFP4: the converted layout's 16-byte slot and its 2 scale bytes
+    uint4 w;         // half 0 elements 0-7, 8-15, half 1 elements 0-7, 8-15
     uint32_t wsf;    // e4m3 scales of half 0 (bits 0-7) and half 1 (bits 8-15)
+};
+template <> struct WSlot<true> {    // bf16: 32 bytes of each half's row
+    uint4 h0a, h0b, h1a, h1b;
+};
+
+template <bool kBf16>
+struct W16Stage {
+    WSlot<kBf16> w;
     uint4 a0, a1;    // bf16 activation elements 0-7 and 8-15 of the lane's block
 };
 
+// NVFP4: p0 = the lane's slot, p1 = its scale bytes (k-tile c at + 1024 c, + 128 c).
+// bf16: p0, p1 = the lane's block in the half-0 and half-1 rows (k-tile c at + 128 c).
 struct W16Streams {
-    const uint8_t* wc;
-    const uint8_t* ws;
+    const uint8_t* p0;
+    const uint8_t* p1;
     const uint16_t* a;          // k-tile c at + 64 c elements
 };
 
-__device__ __forceinline__ void w16_load(W16Stage& st, const W16Streams& p, int c) {
-    st.w = *reinterpret_cast<const uint4*>(p.wc + (int64_t)c * kSlotBytes);
-    st.wsf = *reinterpret_cast<const uint16_t*>(p.ws + (int64_t)c * kSlotSfBytes);
+template <bool kBf16>
+__device__ __forceinline__ void w16_load(W16Stage<kBf16>& st, const W16Streams& p, int c) {
+    if constexpr (kBf16) {
+        const uint4* r0 = reinterpret_cast<const uint4*>(p.p0 + (int64_t)c * 128);
+        const uint4* r1 = reinterpret_cast<const uint4*>(p.p1 + (int64_t)c * 128);
+        st.w.h0a = r0[0];
+        st.w.h0b = r0[1];
+        st.w.h1a = r1[0];
+        st.w.h1b = r1[1];
+    } else {
+        st.w.w = *reinterpret_cast<const uint4*>(p.p0 + (int64_t)c * kSlotBytes);
+        st.w.wsf = *reinterpret_cast<const uint16_t*>(p.p1 + (int64_t)c * kSlotSfBytes);
+    }
     const uint4* a = reinterpret_cast<const uint4*>(p.a + c * 64);
     st.a0 = a[0];
     st.a1 = a[1];
@@ -77,44 +100,54 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float s) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ void w16_use(const W16Stage& st, floatx4& acc0, floatx4& acc1) {
-    const floatx2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.wsf, 1.0f, false);
+template <bool kBf16>
+__device__ __forceinline__ void w16_use(const W16Stage<kBf16>& st, floatx4& acc0, floatx4& acc1) {
     const bf16x8 a0 = as_bf16x8(st.a0), a1 = as_bf16x8(st.a1);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp4x8_to_bf16(st.w.x, s[0]), acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, fp4x8_to_bf16(st.w.z, s[1]), acc1, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp4x8_to_bf16(st.w.y, s[0]), acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, fp4x8_to_bf16(st.w.w, s[1]), acc1, 0, 0, 0);
+    bf16x8 w0a, w0b, w1a, w1b;
+    if constexpr (kBf16) {
+        w0a = as_bf16x8(st.w.h0a); w0b = as_bf16x8(st.w.h0b);
+        w1a = as_bf16x8(st.w.h1a); w1b = as_bf16x8(st.w.h1b);
+    } else {
+        const floatx2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st.w.wsf, 1.0f, false);
+        w0a = fp4x8_to_bf16(st.w.w.x, s[0]); w0b = fp4x8_to_bf16(st.w.w.y, s[0]);
+        w1a = fp4x8_to_bf16(st.w.w.z, s[1]); w1b = fp4x8_to_bf16(st.w.w.w, s[1]);
+    }
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w0a, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, w1a, acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w0b, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, w1b, acc1, 0, 0, 0);
 }
 
 // All KT k-tiles through a D-deep pipeline (KT % D == 0); loads of a stage
 // issue together and in stage order (vmcnt drains in issue order).
-template <int D>
+template <bool kBf16, int D>
 __device__ __forceinline__ void w16_stream(const W16Streams& p, int KT, floatx4& acc0, floatx4& acc1) {
-    W16Stage st[D];
+    W16Stage<kBf16> st[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        w16_load(st[d], p, d);
+        w16_load<kBf16>(st[d], p, d);
         __builtin_amdgcn_sched_barrier(0);
     }
     int c0 = 0;
     for (; c0 + D < KT; c0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            w16_use(st[d], acc0, acc1);
-            w16_load(st[d], p, c0 + D + d);
+            w16_use<kBf16>(st[d], acc0, acc1);
+            w16_load<kBf16>(st[d], p, c0 + D + d);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        w16_use(st[d], acc0, acc1);
+        w16_use<kBf16>(st[d], acc0, acc1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // GEMM1 unit (16 routed rows, intermediate pair j); lane (q, n) ends with rows
-// 4q + i of intermediate 16j + n, gate and up.
-template <int D>
+// 4q + i of intermediate 16j + n, gate and up. bf16 weights: w13 [E, 2I, H],
+// gate rows first; no global scales.
+template <bool kBf16, int D>
 __global__ void __launch_bounds__(kW16Threads) w16_gemm1_kernel(W16Args a) {
     const ExpArgs& e = a.e;
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
@@ -125,13 +158,19 @@ __global__ void __launch_bounds__(kW16Threads) w16_gemm1_kernel(W16Args a) {
     if (rt.e < 0) return;
     const int ex = rt.e;
     W16Streams p;
-    p.wc = e.w.w13 + ex * e.w.w13_expert_stride_bytes + j * e.w.w13_pair_stride_bytes + lane * 16;
-    p.ws = e.w.w13_sf + ex * e.w.w13_sf_expert_stride_bytes + j * e.w.w13_sf_pair_stride_bytes + lane * 2;
+    if constexpr (kBf16) {
+        const uint8_t* w13 = e.w.w13 + ex * e.w.w13_expert_stride_bytes;
+        p.p0 = w13 + ((int64_t)(16 * j + n) * e.H + 16 * q) * 2;
+        p.p1 = w13 + ((int64_t)(e.I + 16 * j + n) * e.H + 16 * q) * 2;
+    } else {
+        p.p0 = e.w.w13 + ex * e.w.w13_expert_stride_bytes + j * e.w.w13_pair_stride_bytes + lane * 16;
+        p.p1 = e.w.w13_sf + ex * e.w.w13_sf_expert_stride_bytes + j * e.w.w13_sf_pair_stride_bytes + lane * 2;
+    }
     const int64_t tok = rt.tok >= 0 ? rt.tok : 0;   // padding rows read token 0's row, never written
     p.a = a.x + tok * a.x_row_stride + q * 16;
     floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
-    w16_stream<D>(p, e.H >> 6, acc_g, acc_u);
-    const float s13 = e.w.g1_alphas[ex];
+    w16_stream<kBf16, D>(p, e.H >> 6, acc_g, acc_u);
+    const float s13 = kBf16 ? 1.0f : e.w.g1_alphas[ex];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = 4 * q + i;
@@ -147,8 +186,9 @@ __global__ void __launch_bounds__(kW16Threads) w16_gemm1_kernel(W16Args a) {
     }
 }
 
-// GEMM2 unit (16 routed rows, output pair c) on the bf16 intermediate.
-template <int D>
+// GEMM2 unit (16 routed rows, output pair c: columns 32c + n and 32c + 16 + n)
+// on the bf16 intermediate. bf16 weights: w2 [E, H, I]; no global scale.
+template <bool kBf16, int D>
 __global__ void __launch_bounds__(kW16Threads) w16_gemm2_kernel(W16Args a) {
     const ExpArgs& e = a.e;
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
@@ -159,15 +199,85 @@ __global__ void __launch_bounds__(kW16Threads) w16_gemm2_kernel(W16Args a) {
     if (rt.e < 0) return;
     const int ex = rt.e;
     W16Streams p;
-    p.wc = e.w.w2 + ex * e.w.w2_expert_stride_bytes + c * e.w.w2_pair_stride_bytes + lane * 16;
-    p.ws = e.w.w2_sf + ex * e.w.w2_sf_expert_stride_bytes + c * e.w.w2_sf_pair_stride_bytes + lane * 2;
+    if constexpr (kBf16) {
+        const uint8_t* w2 = e.w.w2 + ex * e.w.w2_expert_stride_bytes;
+        p.p0 = w2 + ((int64_t)(32 * c + n) * e.I + 16 * q) * 2;
+        p.p1 = w2 + ((int64_t)(32 * c + 16 + n) * e.I + 16 * q) * 2;
+    } else {
+        p.p0 = e.w.w2 + ex * e.w.w2_expert_stride_bytes + c * e.w.w2_pair_stride_bytes + lane * 16;
+        p.p1 = e.w.w2_sf + ex * e.w.w2_sf_expert_stride_bytes + c * e.w.w2_sf_pair_stride_bytes + lane * 2;
+    }
     p.a = a.inter + (int64_t)(rt.row0 + n) * e.I + q * 16;
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    w16_stream<D>(p, e.I >> 6, acc0, acc1);
-    gemm2_epilogue(e, rt, ex, c, n, q, acc0, acc1);
+    w16_stream<kBf16, D>(p, e.I >> 6, acc0, acc1);
+    const float alpha = kBf16 ? 1.0f : e.w.g2_alphas[ex];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;
+        if ((rt.vmask >> m) & 1u) {
+            uint16_t* out = e.rows + (int64_t)(rt.row0 + m) * e.rows_stride + c * 32 + n;
+            out[0] = (uint16_t)f32_to_bf16(__fmul_rn(acc0[i], alpha));
+            out[16] = (uint16_t)f32_to_bf16(__fmul_rn(acc1[i], alpha));
+        }
+    }
 }
 
-static int w16_depth(int kt) { return kt % 4 == 0 ? 4 : kt % 2 == 0 ? 2 : 1; }
+static int w16_depth(int kt, int cap) {
+    for (int d = cap; d > 1; d >>= 1)
+        if (kt % d == 0) return d;
+    return 1;
+}
+
+// The checks both variants share; then the two launches. kBf16 stages hold 4x
+// the weight bytes of NVFP4 ones, so their pipeline is at most 2 deep (8 KB in
+// flight per wave either way).
+template <bool kBf16>
+static int w16_launch(const char* name, const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+                      const moe_nvfp4_weights& w, int T, int K, int E_local, int H, int I, int tile_m,
+                      uint16_t* inter, uint16_t* rows, int64_t rows_stride, hipStream_t s) {
+    if (x_row_stride < H || x_row_stride % 8)
+        return fail(MOE_EINVAL, "%s: x row stride must be >= H and a multiple of 8", name);
+    if (rows_stride < H || rows_stride % 8)
+        return fail(MOE_EINVAL, "%s: rows_stride must be >= H and a multiple of 8", name);
+    W16Args a;
+    a.x = x; a.x_row_stride = x_row_stride; a.inter = inter;
+    a.e.meta = meta; a.e.L = meta_layout(T, K, E_local, tile_m);
+    a.e.w = w; a.e.T = T; a.e.E_local = E_local; a.e.H = H; a.e.I = I; a.e.tile_m = tile_m;
+    a.e.rows = rows; a.e.rows_stride = rows_stride;
+    a.e.a_codes = nullptr; a.e.a_sf = nullptr; a.e.inter_codes = nullptr; a.e.inter_sf = nullptr;
+    a.e.sync = nullptr; a.e.status = nullptr;
+    if (a.e.L.rows_max == 0) return MOE_OK;
+    const int64_t subs = a.e.L.rows_max / 16;
+    const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
+    if (units1 > 0x7FFFFFFF || units2 > 0x7FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too many work units", name);
+    const int wpb = kW16Threads / 64;
+    const dim3 g1((unsigned)((units1 + wpb - 1) / wpb)), g2((unsigned)((units2 + wpb - 1) / wpb)), b(kW16Threads);
+    const int cap = kBf16 ? 2 : 4;
+    switch (w16_depth(H / 64, cap)) {
+        case 4: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 4>), g1, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 2>), g1, b, 0, s, a); break;
+        default: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 1>), g1, b, 0, s, a); break;
+    }
+    int rc = check_launch(name);
+    if (rc) return rc;
+    switch (w16_depth(I / 64, cap)) {
+        case 4: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 4>), g2, b, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 2>), g2, b, 0, s, a); break;
+        default: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 1>), g2, b, 0, s, a); break;
+    }
+    return check_launch(name);
+}
+
+static int w16_shape_check(const char* name, int T, int K, int E_local, int H, int I, int tile_m) {
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E_local < 1 || E_local > MOE_MAX_EXPERTS)
+        return fail(MOE_EINVAL, "%s: T=%d K=%d E_local=%d out of range", name, T, K, E_local);
+    if (H < 64 || H % 64 || I < 64 || I % 64 || H > MOE_MAX_HIDDEN || I > MOE_MAX_HIDDEN)
+        return fail(MOE_EUNSUPPORTED, "%s: H=%d and I=%d must be multiples of 64 up to %d", name, H, I,
+                    MOE_MAX_HIDDEN);
+    if (tile_m < 16 || tile_m > 256 || tile_m % 16)
+        return fail(MOE_EUNSUPPORTED, "%s: tile_m=%d must be a multiple of 16 in [16, 256]", name, tile_m);
+    return MOE_OK;
+}
 
 }  // namespace moe
 
@@ -176,25 +286,16 @@ extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, co
                                      int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
                                      void* stream) {
     using namespace moe;
-    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E_local < 1 || E_local > MOE_MAX_EXPERTS)
-        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: T=%d K=%d E_local=%d out of range", T, K, E_local);
-    if (H < 64 || H % 64 || I < 64 || I % 64 || H > MOE_MAX_HIDDEN || I > MOE_MAX_HIDDEN)
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd_w4a16: H=%d and I=%d must be multiples of 64 up to %d", H, I,
-                    MOE_MAX_HIDDEN);
-    if (tile_m < 16 || tile_m > 256 || tile_m % 16)
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd_w4a16: tile_m=%d must be a multiple of 16 in [16, 256]",
-                    tile_m);
-    if (!w || !meta) return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: NULL weights or meta");
+    const char* name = "moe_experts_fwd_w4a16";
+    int rc = w16_shape_check(name, T, K, E_local, H, I, tile_m);
+    if (rc) return rc;
+    if (!w || !meta) return fail(MOE_EINVAL, "%s: NULL weights or meta", name);
     if (T == 0) return MOE_OK;
     if (!x || !inter || !rows || !w->w13 || !w->w13_sf || !w->w2 || !w->w2_sf || !w->g1_alphas || !w->g2_alphas)
-        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: NULL pointer");
+        return fail(MOE_EINVAL, "%s: NULL pointer", name);
     const void* ptrs[] = {x, meta, inter, rows, w->w13, w->w13_sf, w->w2, w->w2_sf, w->g1_alphas, w->g2_alphas};
     for (const void* ptr : ptrs)
-        if (!aligned16(ptr)) return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: pointers must be 16-byte aligned");
-    if (x_row_stride < H || x_row_stride % 8)
-        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: x row stride must be >= H and a multiple of 8");
-    if (rows_stride < H || rows_stride % 8)
-        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: rows_stride must be >= H and a multiple of 8");
+        if (!aligned16(ptr)) return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
     const int64_t kt1 = H / 64, kt2 = I / 64;
     if (w->w13_pair_stride_bytes < kt1 * kSlotBytes || w->w13_sf_pair_stride_bytes < kt1 * kSlotSfBytes ||
         w->w2_pair_stride_bytes < kt2 * kSlotBytes || w->w2_sf_pair_stride_bytes < kt2 * kSlotSfBytes ||
@@ -205,33 +306,30 @@ extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, co
         (w->w13_pair_stride_bytes | w->w13_sf_pair_stride_bytes | w->w2_pair_stride_bytes |
          w->w2_sf_pair_stride_bytes | w->w13_expert_stride_bytes | w->w13_sf_expert_stride_bytes |
          w->w2_expert_stride_bytes | w->w2_sf_expert_stride_bytes) % 16)
-        return fail(MOE_EINVAL, "moe_experts_fwd_w4a16: weight strides too small or not multiples of 16");
-    W16Args a;
-    a.x = x; a.x_row_stride = x_row_stride; a.inter = inter;
-    a.e.meta = meta; a.e.L = meta_layout(T, K, E_local, tile_m);
-    a.e.w = *w; a.e.T = T; a.e.E_local = E_local; a.e.H = H; a.e.I = I; a.e.tile_m = tile_m;
-    a.e.rows = rows; a.e.rows_stride = rows_stride;
-    a.e.a_codes = nullptr; a.e.a_sf = nullptr; a.e.inter_codes = nullptr; a.e.inter_sf = nullptr;
-    a.e.sync = nullptr; a.e.status = nullptr;
-    if (a.e.L.rows_max == 0) return MOE_OK;
-    const int64_t subs = a.e.L.rows_max / 16;
-    const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
-    if (units1 > 0x7FFFFFFF || units2 > 0x7FFFFFFF)
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd_w4a16: too many work units");
-    const int wpb = kW16Threads / 64;
-    const dim3 g1((unsigned)((units1 + wpb - 1) / wpb)), g2((unsigned)((units2 + wpb - 1) / wpb)), b(kW16Threads);
-    hipStream_t s = (hipStream_t)stream;
-    switch (w16_depth((int)kt1)) {
-        case 4: hipLaunchKernelGGL(w16_gemm1_kernel<4>, g1, b, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(w16_gemm1_kernel<2>, g1, b, 0, s, a); break;
-        default: hipLaunchKernelGGL(w16_gemm1_kernel<1>, g1, b, 0, s, a); break;
-    }
-    int rc = check_launch("moe_experts_fwd_w4a16 (GEMM1)");
+        return fail(MOE_EINVAL, "%s: weight strides too small or not multiples of 16", name);
+    return w16_launch<false>(name, x, x_row_stride, meta, *w, T, K, E_local, H, I, tile_m, inter, rows,
+                             rows_stride, (hipStream_t)stream);
+}
+
+extern "C" int moe_experts_fwd_bf16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+                                    const uint16_t* w13, const uint16_t* w2, int T, int K, int E_local, int H,
+                                    int I, int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
+                                    void* stream) {
+    using namespace moe;
+    const char* name = "moe_experts_fwd_bf16";
+    int rc = w16_shape_check(name, T, K, E_local, H, I, tile_m);
     if (rc) return rc;
-    switch (w16_depth((int)kt2)) {
-        case 4: hipLaunchKernelGGL(w16_gemm2_kernel<4>, g2, b, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(w16_gemm2_kernel<2>, g2, b, 0, s, a); break;
-        default: hipLaunchKernelGGL(w16_gemm2_kernel<1>, g2, b, 0, s, a); break;
-    }
-    return check_launch("moe_experts_fwd_w4a16 (GEMM2)");
+    if (!meta) return fail(MOE_EINVAL, "%s: NULL meta", name);
+    if (T == 0) return MOE_OK;
+    if (!x || !w13 || !w2 || !inter || !rows) return fail(MOE_EINVAL, "%s: NULL pointer", name);
+    const void* ptrs[] = {x, meta, w13, w2, inter, rows};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
+    moe_nvfp4_weights w = {};
+    w.w13 = reinterpret_cast<const uint8_t*>(w13);
+    w.w2 = reinterpret_cast<const uint8_t*>(w2);
+    w.w13_expert_stride_bytes = (int64_t)2 * I * H * 2;
+    w.w2_expert_stride_bytes = (int64_t)H * I * 2;
+    return w16_launch<true>(name, x, x_row_stride, meta, w, T, K, E_local, H, I, tile_m, inter, rows, rows_stride,
+                            (hipStream_t)stream);
 }

@@ -20,7 +20,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout_get",
            "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
            "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant", "moe_router_logits",
-           "moe_router_route", "moe_experts_fwd_w4a16")
+           "moe_router_route", "moe_experts_fwd_w4a16", "moe_experts_fwd_bf16")
 
 
 class MoeMetaLayout(ctypes.Structure):
@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         "nvfp4_quant": (i32, [vp, i64, vp, i32, i32, vp, vp, vp]),
         "nvfp4_norm_quant": (i32, [vp, i64, vp, f32, f32, vp, i32, i32, vp, vp, vp]),
         "moe_router_logits": (i32, [vp, i64, vp, i32, i32, i32, vp, vp]),
+        "moe_experts_fwd_bf16": (i32, [vp, i64, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i64, vp]),
         "moe_experts_fwd_w4a16": (i32, [vp, i64, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32, i32,
                                         i32, i32, vp, vp, i64, vp]),
         "moe_router_route": (i32, [vp, i64, vp, i32, vp, vp, i32, i32, i32, f32, i32, i32, i32, vp, vp,
@@ -226,6 +227,12 @@ def moe_experts_fwd_w4a16(x, meta, weights: Weights, T, K, E_local, H, I, tile_m
     _check(lib().moe_experts_fwd_w4a16(_ptr(x), x.stride(0), _ptr(meta), ctypes.byref(ws), T, K, E_local, H,
                                        I, tile_m, _ptr(inter), _ptr(rows), rows.stride(0), _stream(stream)),
            "moe_experts_fwd_w4a16")
+
+
+def moe_experts_fwd_bf16(x, meta, w13, w2, T, K, E_local, H, I, tile_m, inter, rows, stream=None) -> None:
+    _check(lib().moe_experts_fwd_bf16(_ptr(x), x.stride(0), _ptr(meta), _ptr(w13), _ptr(w2), T, K, E_local, H, I,
+                                      tile_m, _ptr(inter), _ptr(rows), rows.stride(0), _stream(stream)),
+           "moe_experts_fwd_bf16")
 
 
 def moe_finalize(rows, n_partials, partial_stride, exp2perm, topk_weights, norm_weight,

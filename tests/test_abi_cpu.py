@@ -120,6 +120,15 @@ def test_experts_w4a16_refusals():
     assert L.moe_experts_fwd_w4a16(None, 256, None, None, 4, 2, 8, 256, 128, 16, None, None, 256, None) == N.MOE_EINVAL
 
 
+def test_experts_bf16_refusals():
+    L = N.lib()
+    args = lambda H, I, m: (None, H, None, None, None, 4, 2, 8, H, I, m, None, None, H, None)
+    assert L.moe_experts_fwd_bf16(*args(96, 128, 16)) == N.MOE_EUNSUPPORTED     # H % 64
+    assert L.moe_experts_fwd_bf16(*args(256, 96, 16)) == N.MOE_EUNSUPPORTED     # I % 64
+    assert L.moe_experts_fwd_bf16(*args(256, 128, 16)) == N.MOE_EINVAL          # NULL meta
+    assert L.moe_experts_fwd_bf16(16, 256, 16, None, 16, 4, 2, 8, 256, 128, 16, 16, 16, 256, None) == N.MOE_EINVAL
+
+
 def test_zero_tokens_is_a_no_op_without_device():
     L = N.lib()
     assert L.nvfp4_quant(None, 64, None, 0, 64, None, None, None) == N.MOE_OK
