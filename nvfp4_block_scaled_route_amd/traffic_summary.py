@@ -30,8 +30,15 @@ SOURCES = ["nvfp4_block_scaled_route_amd/csrc/experts.hip",
            "nvfp4_block_scaled_route_amd/csrc/experts_tiled.hip",
            "nvfp4_block_scaled_route_amd/csrc/experts.hpp",
            "nvfp4_block_scaled_route_amd/csrc/common.hpp"]
+# the kernels moe_experts_fwd launches (the other expert variants the bench
+# times beside it, W4A16 and BF16, are not part of the step)
 EXPERT_KERNELS = ("gemm1_kernel", "gemm2_kernel", "gemm1_wg_kernel", "gemm2_wg_kernel", "experts_fused_kernel",
                   "tiled_kernel")
+
+
+def is_expert_kernel(name: str) -> bool:
+    """Whether a demangled kernel name is one of EXPERT_KERNELS (whole name)."""
+    return any(f"moe::{k}<" in name or f"moe::{k}(" in name for k in EXPERT_KERNELS)
 
 
 def per_dispatch(run_dir: str, counter: str) -> dict:
@@ -65,7 +72,7 @@ def main():
     fetch_factor = max(cfetch.values()) / copy_kib
     write_factor = max(cwrite.values()) / copy_kib
 
-    kernels = sorted(k for k in fetch if any(s in k for s in EXPERT_KERNELS))
+    kernels = sorted(k for k in fetch if is_expert_kernel(k))
     rows, total = [], 0.0
     rec = {"workload": args.workload, "kernels": kernels, "fetch_factor": fetch_factor,
            "write_factor": write_factor}
