@@ -70,8 +70,8 @@ struct Streams {
 };
 
 __device__ __forceinline__ void load_w(Stage& st, const Streams& p, int c) {
-    st.w = *reinterpret_cast<const uint4*>(p.wc + (int64_t)c * kSlotBytes);
-    st.wsf = *reinterpret_cast<const uint16_t*>(p.ws + (int64_t)c * kSlotSfBytes);
+    st.w = load_stream16(p.wc + (int64_t)c * kSlotBytes);
+    st.wsf = load_stream2(p.ws + (int64_t)c * kSlotSfBytes);
 }
 
 __device__ __forceinline__ void load_stage(Stage& st, const Streams& p, int c) {

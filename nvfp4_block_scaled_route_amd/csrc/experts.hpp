@@ -39,6 +39,18 @@ __device__ __forceinline__ u32x4 buffer_desc(const void* base) {
     return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
 }
 
+// Expert weights are read once per call: non-temporal loads keep them from
+// displacing what is read again (metadata, activations, intermediate, rows) in
+// the L2 and Infinity Cache. Measured on decode_b8: expert step 31.3 -> 29.4 us,
+// whole layer 45.3 -> 42.5 us.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t load_stream2(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -66,6 +66,8 @@ struct W16Streams {
 template <bool kBf16>
 __device__ __forceinline__ void w16_load(W16Stage<kBf16>& st, const W16Streams& p, int c) {
     if constexpr (kBf16) {
+        // plain loads: on the bf16 rows (two 32-byte pieces of two rows a lane)
+        // the non-temporal hint measured slower (decode_b8 95 vs 91 us)
         const uint4* r0 = reinterpret_cast<const uint4*>(p.p0 + (int64_t)c * 128);
         const uint4* r1 = reinterpret_cast<const uint4*>(p.p1 + (int64_t)c * 128);
         st.w.h0a = r0[0];
@@ -73,8 +75,8 @@ __device__ __forceinline__ void w16_load(W16Stage<kBf16>& st, const W16Streams& 
         st.w.h1a = r1[0];
         st.w.h1b = r1[1];
     } else {
-        st.w.w = *reinterpret_cast<const uint4*>(p.p0 + (int64_t)c * kSlotBytes);
-        st.w.wsf = *reinterpret_cast<const uint16_t*>(p.p1 + (int64_t)c * kSlotSfBytes);
+        st.w.w = load_stream16(p.p0 + (int64_t)c * kSlotBytes);
+        st.w.wsf = load_stream2(p.p1 + (int64_t)c * kSlotSfBytes);
     }
     const uint4* a = reinterpret_cast<const uint4*>(p.a + c * 64);
     st.a0 = a[0];
