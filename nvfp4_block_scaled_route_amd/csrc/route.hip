@@ -17,9 +17,10 @@
 // a second pass gives every route its rank among the earlier routes of its
 // expert (ballot matching over the expert index bits within a wave: a stable
 // counting sort, no ordering atomics, deterministic) and scatters it at once.
-// Up to 512 routes one wave does it, chunk by chunk, with no workgroup
-// barrier; beyond, one workgroup (LDS atomics for the counts, a scan across
-// its waves for the ranks).
+// Up to 512 routes one wave counts and ranks them, chunk by chunk, while the
+// workgroup's other waves write the per-row and per-tile fields; beyond, the
+// whole workgroup does it (LDS atomics for the counts, a scan across its waves
+// for the ranks).
 // Small batches run top-k and the permutation in one workgroup, the top-k ids
 // staying in LDS; larger ones take a top-k grid, then the permutation.
 // moe_route_quant appends the quantizer's workgroups to the first launch: they
@@ -235,74 +236,92 @@ __device__ __forceinline__ void clear_sync(const RouteArgs& a, int i, int step) 
     if (i == 0) a.meta[a.L.sync_status] = 0;
 }
 
-// The permutation metadata by one wave, with no workgroup barrier: routes in
-// chunks of 64 (one per lane), experts in runs of ceil(El / 64) per lane.
+// The permutation metadata for up to 512 routes, by one workgroup. Wave 0
+// counts the routes per expert (chunks of 64 routes, one per lane; experts in
+// runs of ceil(El / 64) per lane) and scans the padded offsets. Then, while wave
+// 0 ranks the routes and scatters them, the other waves write the per-row and
+// per-tile fields -- tile -> expert, -1 on padding rows and past the last tile,
+// the cleared sync words -- as coalesced strided stores, each row's expert read
+// from an LDS copy of the tile map.
 constexpr int kWaveMaxRoutes = 512;
 
-__device__ void permute_wave(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
+__device__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
     const int El = a.local_num;
     int32_t* count = lds;                          // [El]
     int32_t* offs = count + El;                    // [El + 1]
     int32_t* running = offs + El + 1;              // [El]
-    const int lane = threadIdx.x & 63;
+    int32_t* tile_e = running + El;                // [tiles_max]: tile -> expert, -1 past the last tile
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int R = a.T * a.K;
     const int m = a.tile_m;
+    const int tiles_max = (int)a.L.tiles_max, rows_max = (int)a.L.rows_max;
     int32_t* exp2perm = a.meta + a.L.exp2perm;
     int32_t* perm2tok = a.meta + a.L.perm2tok;
     int32_t* tile_expert = a.meta + a.L.tile_expert;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-    for (int x = lane; x < El; x += 64) count[x] = 0;
-    wave_lds_sync();
-    for (int base = 0; base < R; base += 64) {
-        const int r = base + lane;
-        const int e = r < R ? local_expert(a, ids[r]) : -1;
-        const uint64_t match = same_expert_lanes(e);
-        if (e >= 0 && (match & lt_mask) == 0) count[e] += __popcll(match);   // one lane per expert
+    if (w == 0) {
+        for (int x = lane; x < El; x += 64) count[x] = 0;
         wave_lds_sync();
-    }
-    // padded offsets
-    const int per = (El + 63) >> 6;
-    const int x0 = lane * per, x1 = min(El, x0 + per);
-    int mine = 0;
-    for (int x = x0; x < x1; ++x) mine += (count[x] + m - 1) / m * m;
-    const int incl = wave_inclusive_scan(mine);
-    const int total_rows = __builtin_amdgcn_readlane(incl, 63);
-    int acc = incl - mine;
-    for (int x = x0; x < x1; ++x) {
-        offs[x] = acc;
-        running[x] = acc;
-        acc += (count[x] + m - 1) / m * m;
-    }
-    if (lane == 0) offs[El] = total_rows;
-    wave_lds_sync();
-    const int num_tiles = total_rows / m;
-    for (int x = lane; x <= El; x += 64) a.meta[a.L.expert_offsets + x] = offs[x];
-    for (int x = lane; x < El; x += 64) a.meta[a.L.expert_counts + x] = count[x];
-    if (lane == 0) {
-        a.meta[a.L.num_tiles] = num_tiles;
-        a.meta[a.L.total_rows] = total_rows;
-    }
-    for (int x = lane; x < El; x += 64) {
-        for (int tile = offs[x] / m; tile < offs[x + 1] / m; ++tile) tile_expert[tile] = x;
-        for (int row = offs[x] + count[x]; row < offs[x + 1]; ++row) perm2tok[row] = -1;
-    }
-    for (int tile = num_tiles + lane; tile < a.L.tiles_max; tile += 64) tile_expert[tile] = -1;
-    for (int row = total_rows + lane; row < a.L.rows_max; row += 64) perm2tok[row] = -1;
-    clear_sync(a, lane, 64);
-    // stable ranks, chunk by chunk, scattered at once
-    for (int base = 0; base < R; base += 64) {
-        const int r = base + lane;
-        const int e = r < R ? local_expert(a, ids[r]) : -1;
-        const uint64_t match = same_expert_lanes(e);
-        const int pos = e >= 0 ? running[e] + __popcll(match & lt_mask) : -1;
-        wave_lds_sync();
-        if (e >= 0 && (match & lt_mask) == 0) running[e] += __popcll(match);
-        wave_lds_sync();
-        if (r < R) {
-            exp2perm[r] = pos;
-            if (pos >= 0) perm2tok[pos] = r / a.K;
+        for (int base = 0; base < R; base += 64) {
+            const int r = base + lane;
+            const int e = r < R ? local_expert(a, ids[r]) : -1;
+            const uint64_t match = same_expert_lanes(e);
+            if (e >= 0 && (match & lt_mask) == 0) count[e] += __popcll(match);   // one lane per expert
+            wave_lds_sync();
         }
+        // padded offsets
+        const int per = (El + 63) >> 6;
+        const int x0 = lane * per, x1 = min(El, x0 + per);
+        int mine = 0;
+        for (int x = x0; x < x1; ++x) mine += (count[x] + m - 1) / m * m;
+        const int incl = wave_inclusive_scan(mine);
+        const int total_rows = __builtin_amdgcn_readlane(incl, 63);
+        int acc = incl - mine;
+        for (int x = x0; x < x1; ++x) {
+            offs[x] = acc;
+            running[x] = acc;
+            acc += (count[x] + m - 1) / m * m;
+        }
+        if (lane == 0) offs[El] = total_rows;
+        wave_lds_sync();
+        for (int x = lane; x <= El; x += 64) a.meta[a.L.expert_offsets + x] = offs[x];
+        for (int x = lane; x < El; x += 64) a.meta[a.L.expert_counts + x] = count[x];
+        if (lane == 0) {
+            a.meta[a.L.num_tiles] = total_rows / m;
+            a.meta[a.L.total_rows] = total_rows;
+        }
+    }
+    __syncthreads();
+    const int total_rows = offs[El];
+    const int num_tiles = total_rows / m;
+    for (int x = tid; x < El; x += kRouteThreads)
+        for (int tile = offs[x] / m; tile < offs[x + 1] / m; ++tile) tile_e[tile] = x;
+    for (int tile = num_tiles + tid; tile < tiles_max; tile += kRouteThreads) tile_e[tile] = -1;
+    __syncthreads();
+    if (w == 0) {
+        // stable ranks, chunk by chunk, scattered at once
+        for (int base = 0; base < R; base += 64) {
+            const int r = base + lane;
+            const int e = r < R ? local_expert(a, ids[r]) : -1;
+            const uint64_t match = same_expert_lanes(e);
+            const int pos = e >= 0 ? running[e] + __popcll(match & lt_mask) : -1;
+            wave_lds_sync();
+            if (e >= 0 && (match & lt_mask) == 0) running[e] += __popcll(match);
+            wave_lds_sync();
+            if (r < R) {
+                exp2perm[r] = pos;
+                if (pos >= 0) perm2tok[pos] = r / a.K;
+            }
+        }
+    } else {
+        const int i = tid - 64, step = kRouteThreads - 64;
+        for (int tile = i; tile < tiles_max; tile += step) tile_expert[tile] = tile_e[tile];
+        for (int row = i; row < rows_max; row += step) {
+            const int e = tile_e[row / m];
+            if (e < 0 || row - offs[e] >= count[e]) perm2tok[row] = -1;   // padding: no route lands here
+        }
+        clear_sync(a, i, step);
     }
 }
 
@@ -417,7 +436,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int m
         topk_tokens(a, blockIdx.x * kRouteWaves, a.route_blocks * kRouteWaves, lds, nullptr);
     } else if (mode == kPermuteOnly) {
         if (a.T * a.K > kWaveMaxRoutes) permute_block(a, a.ids, lds);
-        else if (threadIdx.x < 64) permute_wave(a, a.ids, lds);
+        else permute_small(a, a.ids, lds);
     } else {
         // ids of all routes first, then the region top-k and permutation share
         int32_t* s_ids = lds;
@@ -425,7 +444,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int m
         topk_tokens(a, 0, kRouteWaves, work, s_ids);
         __syncthreads();
         if (a.T * a.K > kWaveMaxRoutes) permute_block(a, s_ids, work);
-        else if (threadIdx.x < 64) permute_wave(a, s_ids, work);
+        else permute_small(a, s_ids, work);
     }
 }
 
@@ -434,8 +453,10 @@ static size_t topk_lds_bytes(int E, int K) {
     return sizeof(int32_t) * ((size_t)2 * kRouteWaves * ((E + 3) & ~3) + (size_t)kRouteWaves * K * 2);
 }
 
-static size_t permute_lds_bytes(int El) {
-    return sizeof(int32_t) * ((size_t)(kRouteWaves + 3) * El + 1 + kRouteWaves);
+static size_t permute_lds_bytes(int El, int64_t tiles_max) {
+    const size_t block = (size_t)(kRouteWaves + 3) * El + 1 + kRouteWaves;   // permute_block
+    const size_t small = (size_t)3 * El + 1 + (size_t)tiles_max;              // permute_small
+    return sizeof(int32_t) * (block > small ? block : small);
 }
 
 int moe_route_check(int T, int E, int K, int tile_m, int local_expert_offset, int local_num_experts,
@@ -481,7 +502,7 @@ static int route_launch(const float* logits, int64_t logits_row_stride, const fl
     a.x = x; a.x_row_stride = x_row_stride; a.gscale = gscale; a.H = H; a.codes = codes; a.sf = sf;
     const int64_t qblocks = x ? ((int64_t)T * (H / 16) + kRouteThreads - 1) / kRouteThreads : 0;
     if (qblocks > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too large", name);
-    const size_t topk_lds = topk_lds_bytes(E, K), perm_lds = permute_lds_bytes(local_num_experts);
+    const size_t topk_lds = topk_lds_bytes(E, K), perm_lds = permute_lds_bytes(local_num_experts, a.L.tiles_max);
     hipStream_t s = (hipStream_t)stream;
     if (T <= kFusedMaxTokens) {
         const size_t lds = sizeof(int32_t) * (((size_t)T * K + 3) & ~(size_t)3) +
