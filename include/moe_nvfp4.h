@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 3
+#define MOE_NVFP4_ABI_VERSION 4
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -87,6 +87,10 @@ int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
  *                                moe_route; moe_experts_fwd's one-launch form
  *                                uses them and leaves them at 0 again. The
  *                                other words are not used.
+ *   perm_counts     [ceil(T*K/512) * E_local]  moe_route's working space when it
+ *                                routes more than 32 tokens: per chunk of 512
+ *                                routes, the routes of each expert, then the
+ *                                chunk's first row in each expert
  * Order (the counting-sort reading of the flashinfer_ops page's metadata,
  * "FlashInferOps.slot"): experts ascending, routes of one expert in ascending
  * t*K+k, each expert's rows padded to a multiple of m. */
@@ -104,6 +108,7 @@ typedef struct moe_meta_layout {
     int64_t sync_status;
     int64_t sub_sync;
     int64_t subs_max;
+    int64_t perm_counts;
 } moe_meta_layout;
 
 int moe_meta_layout_get(int T, int K, int E_local, int tile_m, moe_meta_layout* out);

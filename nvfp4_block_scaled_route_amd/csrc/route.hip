@@ -448,6 +448,148 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int m
     }
 }
 
+// ---------------------------------------------------------------- many routes
+// The same metadata as permute_block, by the whole grid: a stable counting
+// sort in three launches over chunks of 512 consecutive routes.
+//   count:   per chunk, the routes of each local expert (LDS atomics; counts do
+//            not depend on their order) -> meta's perm_counts [chunk][expert]
+//   scan:    one workgroup: per-expert totals, padded offsets, each chunk's
+//            first row in each expert (in place), the tile map
+//   scatter: per chunk, each route's rank among the chunk's earlier routes of
+//            its expert (ballot matching within a wave, a prefix over the
+//            chunk's waves in LDS), added to the chunk's first row; and a
+//            share of the padding rows and of the sync words per workgroup
+constexpr int kChunk = kRouteThreads;
+
+__global__ void __launch_bounds__(kRouteThreads) perm_count_kernel(RouteArgs a) {
+    extern __shared__ int32_t lds[];                   // [El]
+    const int El = a.local_num, R = a.T * a.K, tid = threadIdx.x;
+    for (int x = tid; x < El; x += kRouteThreads) lds[x] = 0;
+    __syncthreads();
+    const int r = blockIdx.x * kChunk + tid;
+    if (r < R) {
+        const int e = local_expert(a, a.ids[r]);
+        if (e >= 0) atomicAdd(&lds[e], 1);
+    }
+    __syncthreads();
+    int32_t* cnt = a.meta + a.L.perm_counts + (int64_t)blockIdx.x * El;
+    for (int x = tid; x < El; x += kRouteThreads) cnt[x] = lds[x];
+}
+
+__global__ void __launch_bounds__(kRouteThreads) perm_scan_kernel(RouteArgs a, int nchunks) {
+    extern __shared__ int32_t lds[];
+    const int El = a.local_num, m = a.tile_m;
+    const int tiles_max = (int)a.L.tiles_max;
+    int32_t* count = lds;                          // [El]
+    int32_t* offs = count + El;                    // [El + 1]
+    int32_t* scan = offs + El + 1;                 // [kRouteWaves]
+    int32_t* tile_e = scan + kRouteWaves;          // [tiles_max]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t* cnt = a.meta + a.L.perm_counts;
+    int32_t* tile_expert = a.meta + a.L.tile_expert;
+    // each thread owns a contiguous run of experts
+    const int per = (El + kRouteThreads - 1) / kRouteThreads;
+    const int e0 = tid * per, e1 = min(El, e0 + per);
+    int my_total = 0;
+    for (int x = e0; x < e1; ++x) {
+        int c = 0;
+#pragma unroll 8
+        for (int b = 0; b < nchunks; ++b) c += cnt[(int64_t)b * El + x];   // independent loads, pipelined
+        count[x] = c;
+        my_total += (c + m - 1) / m * m;
+    }
+    const int incl = wave_inclusive_scan(my_total);
+    if (lane == 63) scan[w] = incl;
+    __syncthreads();
+    int wave_base = 0;
+    for (int ww = 0; ww < w; ++ww) wave_base += scan[ww];
+    int acc = wave_base + incl - my_total;
+    for (int x = e0; x < e1; ++x) {
+        offs[x] = acc;
+        int base = acc;                            // the chunks' first rows, in place
+        for (int b0 = 0; b0 < nchunks; b0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = b0 + i < nchunks ? cnt[(int64_t)(b0 + i) * El + x] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (b0 + i < nchunks) {
+                    cnt[(int64_t)(b0 + i) * El + x] = base;
+                    base += c[i];
+                }
+        }
+        acc += (count[x] + m - 1) / m * m;
+    }
+    if (tid == kRouteThreads - 1) offs[El] = wave_base + incl;
+    __syncthreads();
+    const int total_rows = offs[El], num_tiles = total_rows / m;
+    for (int x = tid; x <= El; x += kRouteThreads) a.meta[a.L.expert_offsets + x] = offs[x];
+    for (int x = tid; x < El; x += kRouteThreads) a.meta[a.L.expert_counts + x] = count[x];
+    if (tid == 0) {
+        a.meta[a.L.num_tiles] = num_tiles;
+        a.meta[a.L.total_rows] = total_rows;
+    }
+    for (int x = tid; x < El; x += kRouteThreads)
+        for (int tile = offs[x] / m; tile < offs[x + 1] / m; ++tile) tile_e[tile] = x;
+    for (int tile = num_tiles + tid; tile < tiles_max; tile += kRouteThreads) tile_e[tile] = -1;
+    __syncthreads();
+    for (int tile = tid; tile < tiles_max; tile += kRouteThreads) tile_expert[tile] = tile_e[tile];
+}
+
+__global__ void __launch_bounds__(kRouteThreads) perm_scatter_kernel(RouteArgs a) {
+    extern __shared__ int32_t lds[];                   // [kRouteWaves][El]
+    const int El = a.local_num, R = a.T * a.K;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int32_t* first = a.meta + a.L.perm_counts + (int64_t)blockIdx.x * El;
+    int32_t* exp2perm = a.meta + a.L.exp2perm;
+    int32_t* perm2tok = a.meta + a.L.perm2tok;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int i = tid; i < kRouteWaves * El; i += kRouteThreads) lds[i] = 0;
+    __syncthreads();
+    const int r = blockIdx.x * kChunk + tid;
+    const int e = r < R ? local_expert(a, a.ids[r]) : -1;
+    const uint64_t match = same_expert_lanes(e);
+    const int rank_in_wave = __popcll(match & lt_mask);
+    if (e >= 0 && rank_in_wave == 0) lds[w * El + e] = __popcll(match);
+    __syncthreads();
+    for (int x = tid; x < El; x += kRouteThreads) {   // exclusive prefix over the chunk's waves
+        int acc = first[x];
+#pragma unroll
+        for (int ww = 0; ww < kRouteWaves; ++ww) {
+            const int c = lds[ww * El + x];
+            lds[ww * El + x] = acc;
+            acc += c;
+        }
+    }
+    __syncthreads();
+    if (r < R) {
+        if (e >= 0) {
+            const int pos = lds[w * El + e] + rank_in_wave;
+            exp2perm[r] = pos;
+            perm2tok[pos] = r / a.K;
+        } else {
+            exp2perm[r] = -1;
+        }
+    }
+    // this workgroup's share of the padding rows (-1: no route lands there) and
+    // of the sync words; the tile map, offsets and counts are the scan's
+    const int rows_max = (int)a.L.rows_max, m = a.tile_m;
+    const int share = (rows_max + gridDim.x - 1) / gridDim.x;
+    const int row0 = blockIdx.x * share, row1 = min(rows_max, row0 + share);
+    const int32_t* tile_expert = a.meta + a.L.tile_expert;
+    const int32_t* offs = a.meta + a.L.expert_offsets;
+    const int32_t* counts = a.meta + a.L.expert_counts;
+    for (int row = row0 + tid; row < row1; row += kRouteThreads) {
+        const int ex = tile_expert[row / m];
+        if (ex < 0 || row - offs[ex] >= counts[ex]) perm2tok[row] = -1;
+    }
+    const int64_t words = 2 * a.L.subs_max, wshare = (words + gridDim.x - 1) / gridDim.x;
+    int32_t* sync = a.meta + a.L.sub_sync;
+    for (int64_t x = blockIdx.x * wshare + tid; x < min(words, (blockIdx.x + 1) * wshare); x += kRouteThreads)
+        sync[(x >> 1) * kSubSyncStride + (x & 1)] = 0;
+    if (blockIdx.x == 0 && tid == 0) a.meta[a.L.sync_status] = 0;
+}
+
 static size_t topk_lds_bytes(int E, int K) {
     if (E > kRankMaxExperts) return 0;
     return sizeof(int32_t) * ((size_t)2 * kRouteWaves * ((E + 3) & ~3) + (size_t)kRouteWaves * K * 2);
@@ -503,6 +645,12 @@ static int route_launch(const float* logits, int64_t logits_row_stride, const fl
     const int64_t qblocks = x ? ((int64_t)T * (H / 16) + kRouteThreads - 1) / kRouteThreads : 0;
     if (qblocks > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too large", name);
     const size_t topk_lds = topk_lds_bytes(E, K), perm_lds = permute_lds_bytes(local_num_experts, a.L.tiles_max);
+    // more than 512 routes of more than 32 tokens: the grid-wide permutation,
+    // as long as its scan's LDS (tile map included) fits; else one workgroup
+    const int64_t R = (int64_t)T * K;
+    const size_t scan_lds =
+        sizeof(int32_t) * ((size_t)2 * local_num_experts + 1 + kRouteWaves + (size_t)a.L.tiles_max);
+    const bool grid_perm = T > kFusedMaxTokens && R > kWaveMaxRoutes && scan_lds <= 64 * 1024;
     hipStream_t s = (hipStream_t)stream;
     if (T <= kFusedMaxTokens) {
         const size_t lds = sizeof(int32_t) * (((size_t)T * K + 3) & ~(size_t)3) +
@@ -519,8 +667,22 @@ static int route_launch(const float* logits, int64_t logits_row_stride, const fl
         if (rc) return rc;
         a.route_blocks = 1;
         a.x = nullptr;
-        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), perm_lds, s, a,
-                           (int)kPermuteOnly);
+        if (!grid_perm) {
+            hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), perm_lds, s, a,
+                               (int)kPermuteOnly);
+        } else {
+            const int nchunks = (int)((R + kChunk - 1) / kChunk);
+            const int El = local_num_experts;
+            hipLaunchKernelGGL(perm_count_kernel, dim3((unsigned)nchunks), dim3(kRouteThreads),
+                               sizeof(int32_t) * El, s, a);
+            rc = check_launch(name);
+            if (rc) return rc;
+            hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kRouteThreads), scan_lds, s, a, nchunks);
+            rc = check_launch(name);
+            if (rc) return rc;
+            hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)nchunks), dim3(kRouteThreads),
+                               sizeof(int32_t) * kRouteWaves * El, s, a);
+        }
     }
     return check_launch(name);
 }

@@ -26,7 +26,7 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout
 class MoeMetaLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_tiles", "total_rows", "expert_offsets", "expert_counts", "exp2perm", "perm2tok",
-        "tile_expert", "total_ints", "rows_max", "tiles_max", "sync_status", "sub_sync", "subs_max")]
+        "tile_expert", "total_ints", "rows_max", "tiles_max", "sync_status", "sub_sync", "subs_max", "perm_counts")]
 
 
 class MoeNvfp4Weights(ctypes.Structure):

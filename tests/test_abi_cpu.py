@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
@@ -42,8 +42,8 @@ def test_rows_max_matches_oracle(T, K, E, m):
     assert lay.rows_max == oracle_rows_max(T, K, E, m) and lay.tiles_max * m == lay.rows_max
     assert lay.subs_max * 16 == lay.rows_max
     fields = [lay.expert_offsets, lay.expert_counts, lay.exp2perm, lay.perm2tok, lay.tile_expert,
-              lay.sub_sync]
-    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max, 256 * lay.subs_max]
+              lay.sub_sync, lay.perm_counts]
+    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max, 256 * lay.subs_max, -(-T * K // 512) * E]
     assert all(f % 64 == 0 for f in fields)
     for (f, n), nxt in zip(zip(fields, sizes), fields[1:] + [lay.total_ints]):
         assert f + n <= nxt

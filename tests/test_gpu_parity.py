@@ -176,9 +176,12 @@ def test_route_sigmoid_bits_many_tokens():
     _check_route(logits, None, 8, 128)
 
 
-def test_route_expert_parallel_subset():
-    rng = np.random.default_rng(6)
-    logits = rng.standard_normal((40, 64)).astype(np.float32)
+@pytest.mark.parametrize("T", [40, 600])
+def test_route_expert_parallel_subset(T):
+    """Experts outside [16, 32) are not served here: their routes map to -1
+    (one-workgroup permutation at 320 routes, the grid-wide one at 4800)."""
+    rng = np.random.default_rng(6 + T)
+    logits = rng.standard_normal((T, 64)).astype(np.float32)
     _, _, meta = _check_route(logits, None, 8, 16, offset=16, local=16)
 
 
