@@ -64,7 +64,7 @@ struct W16Streams {
 };
 
 template <bool kBf16>
-__device__ __forceinline__ void w16_load(W16Stage<kBf16>& st, const W16Streams& p, int c) {
+__device__ __forceinline__ void w16_load_w(W16Stage<kBf16>& st, const W16Streams& p, int c) {
     if constexpr (kBf16) {
         // plain loads: on the bf16 rows (two 32-byte pieces of two rows a lane)
         // the non-temporal hint measured slower (decode_b8 95 vs 91 us)
@@ -78,6 +78,11 @@ __device__ __forceinline__ void w16_load(W16Stage<kBf16>& st, const W16Streams& 
         st.w.w = load_stream16(p.p0 + (int64_t)c * kSlotBytes);
         st.w.wsf = load_stream2(p.p1 + (int64_t)c * kSlotSfBytes);
     }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void w16_load(W16Stage<kBf16>& st, const W16Streams& p, int c) {
+    w16_load_w<kBf16>(st, p, c);
     const uint4* a = reinterpret_cast<const uint4*>(p.a + c * 64);
     st.a0 = a[0];
     st.a1 = a[1];
@@ -146,6 +151,27 @@ __device__ __forceinline__ void w16_stream(const W16Streams& p, int KT, floatx4&
     }
 }
 
+// GEMM1 epilogue: lane (q, n) holds rows 4q + i of intermediate 16j + n.
+template <bool kBf16>
+__device__ __forceinline__ void w16_gemm1_epilogue(const W16Args& a, const RowTile& rt, int ex, int j, int n, int q,
+                                                   const floatx4& acc_g, const floatx4& acc_u) {
+    const ExpArgs& e = a.e;
+    const float s13 = kBf16 ? 1.0f : e.w.g1_alphas[ex];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q + i;
+        const float g = __fmul_rn(acc_g[i], s13);
+        const float u = __fmul_rn(acc_u[i], s13);
+        // silu(g) = g * sigmoid(g) with sigmoid from e^-|g| (never overflows): a
+        // bf16 intermediate keeps the tiny values of strongly negative gates,
+        // which g / (1 + e^-g) would flush to zero once e^-g overflows
+        const float eg = expf(-__builtin_fabsf(g));
+        const float sig = __fdiv_rn(g >= 0.0f ? 1.0f : eg, __fadd_rn(1.0f, eg));
+        const float h = __fmul_rn(__fmul_rn(g, sig), u);
+        if ((rt.vmask >> m) & 1u) a.inter[(int64_t)(rt.row0 + m) * e.I + j * 16 + n] = (uint16_t)f32_to_bf16(h);
+    }
+}
+
 // GEMM1 unit (16 routed rows, intermediate pair j); lane (q, n) ends with rows
 // 4q + i of intermediate 16j + n, gate and up. bf16 weights: w13 [E, 2I, H],
 // gate rows first; no global scales.
@@ -172,19 +198,22 @@ __global__ void __launch_bounds__(kW16Threads) w16_gemm1_kernel(W16Args a) {
     p.a = a.x + tok * a.x_row_stride + q * 16;
     floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
     w16_stream<kBf16, D>(p, e.H >> 6, acc_g, acc_u);
-    const float s13 = kBf16 ? 1.0f : e.w.g1_alphas[ex];
+    w16_gemm1_epilogue<kBf16>(a, rt, ex, j, n, q, acc_g, acc_u);
+}
+
+// GEMM2 epilogue: lane (q, n) holds rows 4q + i of columns 32c + n and 32c + 16 + n.
+template <bool kBf16>
+__device__ __forceinline__ void w16_gemm2_epilogue(const ExpArgs& e, const RowTile& rt, int ex, int c, int n, int q,
+                                                   const floatx4& acc0, const floatx4& acc1) {
+    const float alpha = kBf16 ? 1.0f : e.w.g2_alphas[ex];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = 4 * q + i;
-        const float g = __fmul_rn(acc_g[i], s13);
-        const float u = __fmul_rn(acc_u[i], s13);
-        // silu(g) = g * sigmoid(g) with sigmoid from e^-|g| (never overflows): a
-        // bf16 intermediate keeps the tiny values of strongly negative gates,
-        // which g / (1 + e^-g) would flush to zero once e^-g overflows
-        const float eg = expf(-__builtin_fabsf(g));
-        const float sig = __fdiv_rn(g >= 0.0f ? 1.0f : eg, __fadd_rn(1.0f, eg));
-        const float h = __fmul_rn(__fmul_rn(g, sig), u);
-        if ((rt.vmask >> m) & 1u) a.inter[(int64_t)(rt.row0 + m) * e.I + j * 16 + n] = (uint16_t)f32_to_bf16(h);
+        if ((rt.vmask >> m) & 1u) {
+            uint16_t* out = e.rows + (int64_t)(rt.row0 + m) * e.rows_stride + c * 32 + n;
+            out[0] = (uint16_t)f32_to_bf16(__fmul_rn(acc0[i], alpha));
+            out[16] = (uint16_t)f32_to_bf16(__fmul_rn(acc1[i], alpha));
+        }
     }
 }
 
@@ -212,16 +241,143 @@ __global__ void __launch_bounds__(kW16Threads) w16_gemm2_kernel(W16Args a) {
     p.a = a.inter + (int64_t)(rt.row0 + n) * e.I + q * 16;
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     w16_stream<kBf16, D>(p, e.I >> 6, acc0, acc1);
-    const float alpha = kBf16 ? 1.0f : e.w.g2_alphas[ex];
+    w16_gemm2_epilogue<kBf16>(e, rt, ex, c, n, q, acc0, acc1);
+}
+
+// ---------------------------------------------------------------- four units per workgroup
+// A workgroup's four waves take four units of one 16-row tile and share its
+// activation rows through LDS, staged 256 columns (4 k-tiles, 8 KB of bf16) at
+// a time in two buffers: while the waves run chunk c from one buffer, the
+// workgroup's loads of chunk c + 1 are in flight and land in the other, one
+// barrier a chunk. Without it every wave read its rows' 32-byte blocks from the
+// cache itself -- 16 rows x 2 KB per k-tile per wave beside its weight slot.
+// Rows are 528 bytes apart in LDS (256 bf16 + 16 bytes): a k-tile's 16-byte
+// reads by 16 lanes of one q (16 rows, one column) then fall on 16 distinct
+// groups of 4 banks. The weights stream through a register pipeline of D
+// stages (whole chunks) across the chunks.
+constexpr int kW16Chunk = 256;                  // columns per LDS chunk
+constexpr int kW16RowBytes = kW16Chunk * 2 + 16;
+constexpr int kW16BufBytes = 16 * kW16RowBytes;
+
+// Runs all KT k-tiles (KT % D == 0): the weights stream D k-tiles ahead (4,
+// one chunk, or 8, two), the activations one chunk ahead. srow: the bf16 row
+// this thread stages (row threadIdx.x / 16 of the tile), 32 bytes at column
+// 16 (threadIdx.x % 16) of each chunk.
+template <bool kBf16, int D>
+__device__ __forceinline__ void w16_wg_run(const W16Streams& p, const uint16_t* srow, int KT, uint8_t* lds,
+                                           floatx4& acc0, floatx4& acc1) {
+    constexpr int CK = kW16Chunk / 64;          // k-tiles per chunk
+    constexpr int H = D / CK;                   // chunks per pass over the pipeline
+    static_assert(D % CK == 0, "the pipeline holds whole chunks");
+    const int lane = threadIdx.x & 63, t = threadIdx.x;
+    const int NC = KT / CK;
+    uint8_t* wpos = lds + (t >> 4) * kW16RowBytes + (t & 15) * 32;
+    const uint8_t* rpos = lds + (lane & 15) * kW16RowBytes + (lane >> 4) * 32;
+    const u32x4* src = reinterpret_cast<const u32x4*>(srow + (t & 15) * 16);
+    W16Stage<kBf16> st[D];
+    // chunk 0's rows, then the first weights and chunk 1's rows go out before
+    // chunk 0 is stored, so that their latencies overlap
+    const u32x4 f0 = src[0], f1 = src[1];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q + i;
-        if ((rt.vmask >> m) & 1u) {
-            uint16_t* out = e.rows + (int64_t)(rt.row0 + m) * e.rows_stride + c * 32 + n;
-            out[0] = (uint16_t)f32_to_bf16(__fmul_rn(acc0[i], alpha));
-            out[16] = (uint16_t)f32_to_bf16(__fmul_rn(acc1[i], alpha));
+    for (int d = 0; d < D; ++d) {
+        w16_load_w<kBf16>(st[d], p, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 s0 = f0, s1 = f1;
+    if (NC > 1) {
+        s0 = src[kW16Chunk / 8];                // chunk 1: + 256 bf16 = 32 x 16 bytes
+        s1 = src[kW16Chunk / 8 + 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    reinterpret_cast<u32x4*>(wpos)[0] = f0;
+    reinterpret_cast<u32x4*>(wpos)[1] = f1;
+    __syncthreads();
+    for (int c0 = 0; c0 < NC; c0 += H) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            const int c = c0 + h;
+            const uint8_t* buf = rpos + (c & 1) * kW16BufBytes;
+#pragma unroll
+            for (int d = 0; d < CK; ++d) {
+                W16Stage<kBf16>& sd = st[CK * h + d];
+                sd.a0 = *reinterpret_cast<const uint4*>(buf + d * 128);
+                sd.a1 = *reinterpret_cast<const uint4*>(buf + d * 128 + 16);
+                w16_use<kBf16>(sd, acc0, acc1);
+                if (CK * c + d + D < KT) w16_load_w<kBf16>(sd, p, CK * c + d + D);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (c + 1 < NC) {
+                u32x4* nxt = reinterpret_cast<u32x4*>(wpos + ((c + 1) & 1) * kW16BufBytes);
+                nxt[0] = s0;
+                nxt[1] = s1;
+            }
+            __syncthreads();
+            if (c + 2 < NC) {
+                s0 = src[(c + 2) * (kW16Chunk / 8)];
+                s1 = src[(c + 2) * (kW16Chunk / 8) + 1];
+            }
         }
     }
+}
+
+// GEMM1: the 4 units of a workgroup are intermediate pairs of one tile (I/16
+// % 4 == 0); thread t stages the input row of the tile's row t / 16 (gathered
+// by token; a padding row stages token 0's row, which feeds no written
+// output).
+template <bool kBf16, int D>
+__global__ void __launch_bounds__(kW16Threads) w16_wg_gemm1_kernel(W16Args a) {
+    __shared__ __align__(16) uint8_t lds[2 * kW16BufBytes];
+    const ExpArgs& e = a.e;
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const uint32_t unit = blockIdx.x * (kW16Threads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n1 = e.I >> 4;
+    const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
+    const RowTile rt = row_tile(e, sub, n);     // one tile for the whole workgroup
+    if (rt.e < 0) return;
+    const int ex = rt.e;
+    W16Streams p;
+    if constexpr (kBf16) {
+        const uint8_t* w13 = e.w.w13 + ex * e.w.w13_expert_stride_bytes;
+        p.p0 = w13 + ((int64_t)(16 * j + n) * e.H + 16 * q) * 2;
+        p.p1 = w13 + ((int64_t)(e.I + 16 * j + n) * e.H + 16 * q) * 2;
+    } else {
+        p.p0 = e.w.w13 + ex * e.w.w13_expert_stride_bytes + j * e.w.w13_pair_stride_bytes + lane * 16;
+        p.p1 = e.w.w13_sf + ex * e.w.w13_sf_expert_stride_bytes + j * e.w.w13_sf_pair_stride_bytes + lane * 2;
+    }
+    int tok = e.meta[e.L.perm2tok + rt.row0 + (threadIdx.x >> 4)];
+    if (tok < 0 || tok >= e.T) tok = 0;
+    floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
+    w16_wg_run<kBf16, D>(p, a.x + (int64_t)tok * a.x_row_stride, e.H >> 6, lds, acc_g, acc_u);
+    w16_gemm1_epilogue<kBf16>(a, rt, ex, j, n, q, acc_g, acc_u);
+}
+
+// GEMM2: the 4 units of a workgroup are output pairs of one tile (H/32 % 4 ==
+// 0); the tile's 16 intermediate rows are consecutive.
+template <bool kBf16, int D>
+__global__ void __launch_bounds__(kW16Threads) w16_wg_gemm2_kernel(W16Args a) {
+    __shared__ __align__(16) uint8_t lds[2 * kW16BufBytes];
+    const ExpArgs& e = a.e;
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const uint32_t unit = blockIdx.x * (kW16Threads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t n2 = e.H >> 5;
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
+    const RowTile rt = row_tile(e, sub, n);
+    if (rt.e < 0) return;
+    const int ex = rt.e;
+    W16Streams p;
+    if constexpr (kBf16) {
+        const uint8_t* w2 = e.w.w2 + ex * e.w.w2_expert_stride_bytes;
+        p.p0 = w2 + ((int64_t)(32 * c + n) * e.I + 16 * q) * 2;
+        p.p1 = w2 + ((int64_t)(32 * c + 16 + n) * e.I + 16 * q) * 2;
+    } else {
+        p.p0 = e.w.w2 + ex * e.w.w2_expert_stride_bytes + c * e.w.w2_pair_stride_bytes + lane * 16;
+        p.p1 = e.w.w2_sf + ex * e.w.w2_sf_expert_stride_bytes + c * e.w.w2_sf_pair_stride_bytes + lane * 2;
+    }
+    floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    w16_wg_run<kBf16, D>(p, a.inter + (int64_t)(rt.row0 + (threadIdx.x >> 4)) * e.I, e.I >> 6, lds,
+                              acc0, acc1);
+    w16_gemm2_epilogue<kBf16>(e, rt, ex, c, n, q, acc0, acc1);
 }
 
 static int w16_depth(int kt, int cap) {
@@ -255,17 +411,29 @@ static int w16_launch(const char* name, const uint16_t* x, int64_t x_row_stride,
     const int wpb = kW16Threads / 64;
     const dim3 g1((unsigned)((units1 + wpb - 1) / wpb)), g2((unsigned)((units2 + wpb - 1) / wpb)), b(kW16Threads);
     const int cap = kBf16 ? 2 : 4;
-    switch (w16_depth(H / 64, cap)) {
-        case 4: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 4>), g1, b, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 2>), g1, b, 0, s, a); break;
-        default: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 1>), g1, b, 0, s, a); break;
+    // the workgroup forms where the shape allows: whole 256-column chunks, and
+    // for GEMM2 four output pairs in one tile (H % 128 == 0). The weights
+    // stream one chunk (4 k-tiles) ahead: 8 measured no faster, and neither did
+    // 8 waves a workgroup sharing one tile's rows.
+    if (H % kW16Chunk == 0) {
+        hipLaunchKernelGGL((w16_wg_gemm1_kernel<kBf16, 4>), g1, b, 0, s, a);
+    } else {
+        switch (w16_depth(H / 64, cap)) {
+            case 4: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 4>), g1, b, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 2>), g1, b, 0, s, a); break;
+            default: hipLaunchKernelGGL((w16_gemm1_kernel<kBf16, 1>), g1, b, 0, s, a); break;
+        }
     }
     int rc = check_launch(name);
     if (rc) return rc;
-    switch (w16_depth(I / 64, cap)) {
-        case 4: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 4>), g2, b, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 2>), g2, b, 0, s, a); break;
-        default: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 1>), g2, b, 0, s, a); break;
+    if (I % kW16Chunk == 0 && H % 128 == 0) {
+        hipLaunchKernelGGL((w16_wg_gemm2_kernel<kBf16, 4>), g2, b, 0, s, a);
+    } else {
+        switch (w16_depth(I / 64, cap)) {
+            case 4: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 4>), g2, b, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 2>), g2, b, 0, s, a); break;
+            default: hipLaunchKernelGGL((w16_gemm2_kernel<kBf16, 1>), g2, b, 0, s, a); break;
+        }
     }
     return check_launch(name);
 }

@@ -63,9 +63,11 @@ def test_bf16_layer_on_workload(name):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 32),
-                                         (40, 256, 128, 4, 2, 64)])
+                                         (40, 256, 128, 4, 2, 64), (3, 1024, 512, 4, 2, 16),
+                                         (7, 512, 192, 8, 2, 16)])
 def test_bf16_layer_shapes(T, H, I, E, K, m):
-    """Pipeline depths 1 (H/64 = 5, I/64 = 3) and 2; tiles of 16 to 64 rows."""
+    """Per-wave kernels at pipeline depths 1 (H/64 = 5, I/64 = 3) and 2, and the
+    LDS-staged workgroup kernels (K a multiple of 256); tiles of 16 to 64 rows."""
     wl = dataclasses.replace(W.WORKLOADS["tiny"], name=f"bf16_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E,
                              K=K, tile_m=m, seed=13)
     _compare(wl)

@@ -80,10 +80,12 @@ def test_w4a16_on_workload(name):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 32),
-                                         (3, 1024, 512, 4, 2, 16), (40, 256, 128, 4, 2, 64)])
+                                         (3, 1024, 512, 4, 2, 16), (40, 256, 128, 4, 2, 64), (7, 512, 192, 8, 2, 16)])
 def test_w4a16_shapes(T, H, I, E, K, m):
-    """Pipeline depths 1 (H/64 = 5, I/64 = 3), 2 and 4; tiles of 16 to 64 rows,
-    several routed 16-row tiles per expert."""
+    """Per-wave kernels at pipeline depths 1 (H/64 = 5, I/64 = 3), 2 and 4, and
+    the LDS-staged workgroup kernels (K a multiple of 256: GEMM1 at H = 256,
+    512, 1024, GEMM2 at I = 256, 512, one or several chunks); tiles of 16 to 64
+    rows, several routed 16-row tiles per expert."""
     wl = dataclasses.replace(W.WORKLOADS["tiny"], name=f"w4a16_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E,
                              K=K, tile_m=m, seed=11)
     _compare(wl)
