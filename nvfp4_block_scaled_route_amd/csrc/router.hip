@@ -98,13 +98,56 @@ __global__ void __launch_bounds__(kRlThreads) router_logits_kernel(RlArgs a) {
 }
 
 // Many tokens: an LDS-tiled product. A workgroup computes 32 tokens x 64
-// experts; per 32-column step it stages both operands in LDS as fp64 (each
+// experts; per 128-column step it stages both operands in LDS as fp64 (each
 // value converted once), then each thread accumulates 2 tokens x 4 experts
 // with fp64 fused multiply-adds (a product of two fp32 values is exact in
-// fp64, so the fused and the separate multiply-add round alike). The fp64
-// matrix instruction (v_mfma_f64_16x16x4_f64) measured slower here: 451 us
-// against 357 at 4096 tokens.
-constexpr int kTileT = 32, kTileE = 64, kTileK = 32;
+// fp64, so the fused and the separate multiply-add round alike). The next
+// step's operands are loaded into registers while this step computes, so that
+// the memory latency hides behind 128 columns of arithmetic. The fp64 matrix
+// instruction (v_mfma_f64_16x16x4_f64) measured slower than this kernel's
+// unpipelined form.
+constexpr int kTileT = 32, kTileE = 64, kTileK = 128;
+constexpr int kTileXVecs = kTileT * kTileK / 4 / 256;    // float4 of x a thread stages per step
+constexpr int kTileWVecs = kTileE * kTileK / 4 / 256;    // float4 of w
+
+struct RlTileRegs {
+    float4 x[kTileXVecs];
+    float4 w[kTileWVecs];
+};
+
+// Thread tid stages rows tid / 32 + 8 h of each operand tile, 4 columns at
+// 4 (tid % 32): 32 threads read 512 contiguous bytes of a row. Out-of-range
+// rows and columns read as zero (D % 4 == 0, so a float4 is in or out whole).
+__device__ __forceinline__ void rl_tile_load(RlTileRegs& r, const RlArgs& a, int t0, int e0, int k0) {
+    const int tid = threadIdx.x, c = (tid & 31) * 4, k = k0 + c;
+#pragma unroll
+    for (int h = 0; h < kTileXVecs; ++h) {
+        const int t = t0 + (tid >> 5) + 8 * h;
+        r.x[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < a.T && k < a.D) r.x[h] = *reinterpret_cast<const float4*>(a.x + (int64_t)t * a.x_row_stride + k);
+    }
+#pragma unroll
+    for (int h = 0; h < kTileWVecs; ++h) {
+        const int e = e0 + (tid >> 5) + 8 * h;
+        r.w[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e < a.E && k < a.D) r.w[h] = *reinterpret_cast<const float4*>(a.w + (int64_t)e * a.D + k);
+    }
+}
+
+__device__ __forceinline__ void rl_tile_store(const RlTileRegs& r, double (*xs)[kTileK + 1],
+                                              double (*ws)[kTileK + 1]) {
+    const int tid = threadIdx.x, c = (tid & 31) * 4;
+#pragma unroll
+    for (int h = 0; h < kTileXVecs; ++h) {
+        double* d = &xs[(tid >> 5) + 8 * h][c];
+        d[0] = r.x[h].x; d[1] = r.x[h].y; d[2] = r.x[h].z; d[3] = r.x[h].w;
+    }
+#pragma unroll
+    for (int h = 0; h < kTileWVecs; ++h) {
+        double* d = &ws[(tid >> 5) + 8 * h][c];
+        d[0] = r.w[h].x; d[1] = r.w[h].y; d[2] = r.w[h].z; d[3] = r.w[h].w;
+    }
+}
 
 __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
     __shared__ double xs[kTileT][kTileK + 1];
@@ -113,24 +156,13 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
     const int t0 = blockIdx.x * kTileT, e0 = blockIdx.y * kTileE;
     const int tr = tid >> 4, tc = tid & 15;          // tokens t0 + 2 tr + {0, 1}, experts e0 + tc + 16 j
     double acc[2][4] = {};
+    RlTileRegs r;
+    rl_tile_load(r, a, t0, e0, 0);
+    rl_tile_store(r, xs, ws);
+    __syncthreads();
     for (int k0 = 0; k0 < a.D; k0 += kTileK) {
-        // stage: 32 x 32 of x and 64 x 32 of w, 4 consecutive columns a thread
-        {
-            const int r = tid >> 3, c = (tid & 7) * 4;   // 32 rows x 8 column groups
-            const int t = t0 + r, k = k0 + c;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < a.T && k < a.D) v = *reinterpret_cast<const float4*>(a.x + (int64_t)t * a.x_row_stride + k);
-            xs[r][c] = v.x; xs[r][c + 1] = v.y; xs[r][c + 2] = v.z; xs[r][c + 3] = v.w;
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = (tid >> 3) + 32 * h, c = (tid & 7) * 4;
-            const int e = e0 + r, k = k0 + c;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < a.E && k < a.D) v = *reinterpret_cast<const float4*>(a.w + (int64_t)e * a.D + k);
-            ws[r][c] = v.x; ws[r][c + 1] = v.y; ws[r][c + 2] = v.z; ws[r][c + 3] = v.w;
-        }
-        __syncthreads();
+        const bool more = k0 + kTileK < a.D;
+        if (more) rl_tile_load(r, a, t0, e0, k0 + kTileK);
 #pragma unroll 8
         for (int k = 0; k < kTileK; ++k) {
             const double x0 = xs[2 * tr][k], x1 = xs[2 * tr + 1][k];
@@ -142,6 +174,10 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
             }
         }
         __syncthreads();
+        if (more) {
+            rl_tile_store(r, xs, ws);
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
