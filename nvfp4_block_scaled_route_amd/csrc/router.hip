@@ -107,6 +107,7 @@ __global__ void __launch_bounds__(kRlThreads) router_logits_kernel(RlArgs a) {
 // instruction (v_mfma_f64_16x16x4_f64) measured slower than this kernel's
 // unpipelined form.
 constexpr int kTileT = 32, kTileE = 64, kTileK = 128;
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 constexpr int kTileXVecs = kTileT * kTileK / 4 / 256;    // float4 of x a thread stages per step
 constexpr int kTileWVecs = kTileE * kTileK / 4 / 256;    // float4 of w
 
@@ -154,8 +155,9 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
     __shared__ double ws[kTileE][kTileK + 1];
     const int tid = threadIdx.x;
     const int t0 = blockIdx.x * kTileT, e0 = blockIdx.y * kTileE;
-    const int tr = tid >> 4, tc = tid & 15;          // tokens t0 + 2 tr + {0, 1}, experts e0 + tc + 16 j
-    double acc[2][4] = {};
+    const int lane = tid & 63, n = lane & 15, q = lane >> 4;
+    const int ew = 16 * (tid >> 6);                  // the wave's 16 experts: e0 + ew + [0, 16)
+    doublex4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     RlTileRegs r;
     rl_tile_load(r, a, t0, e0, 0);
     rl_tile_store(r, xs, ws);
@@ -164,14 +166,10 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
         const bool more = k0 + kTileK < a.D;
         if (more) rl_tile_load(r, a, t0, e0, k0 + kTileK);
 #pragma unroll 8
-        for (int k = 0; k < kTileK; ++k) {
-            const double x0 = xs[2 * tr][k], x1 = xs[2 * tr + 1][k];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const double wv = ws[tc + 16 * j][k];
-                acc[0][j] = __fma_rn(x0, wv, acc[0][j]);
-                acc[1][j] = __fma_rn(x1, wv, acc[1][j]);
-            }
+        for (int k = 0; k < kTileK; k += 4) {
+            const double x0 = xs[n][k + q], x1 = xs[16 + n][k + q], wv = ws[ew + n][k + q];
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(x0, wv, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(x1, wv, acc1, 0, 0, 0);
         }
         __syncthreads();
         if (more) {
@@ -179,14 +177,13 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
             __syncthreads();
         }
     }
+    // lane (n, q) holds tokens q + 4 i of each 16-token block, expert n
+    const int e = e0 + ew + n;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = t0 + 2 * tr + i;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + tc + 16 * j;
-            if (t < a.T && e < a.E) a.logits[(int64_t)t * a.E + e] = __double2float_rn(acc[i][j]);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + q + 4 * i;
+        if (e < a.E && t < a.T) a.logits[(int64_t)t * a.E + e] = __double2float_rn(acc0[i]);
+        if (e < a.E && t + 16 < a.T) a.logits[(int64_t)(t + 16) * a.E + e] = __double2float_rn(acc1[i]);
     }
 }
 
