@@ -43,6 +43,7 @@ def parse():
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense f16 matrix peak
+MFMA_F64_PEAK_TFLOPS = 78.6       # MI355X fp64 peak (matrix and vector)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -146,11 +147,16 @@ def time_router(N, W, wl, bufs, n: int) -> dict:
     us_c = _event_us(lambda s: N.moe_router_route(x, w, None, None, wl.K, 1.0, wl.tile_m, 0, wl.E, logits,
                                                   bufs.ids, bufs.weights, bufs.meta, s), n)
     nbytes = 4 * (wl.T * wl.H + wl.E * wl.H + wl.T * wl.E)
-    gbs = nbytes / (us_l * 1e-6) / 1e9
-    return {"moe_router_logits": {"us": us_l, "bytes": nbytes, "achieved": gbs, "unit": "GB/s",
-                                  "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
-                                  "bound": "hbm" if wl.T <= 64 else "fp64 alu"},
-            "moe_router_route": {"us": us_c}}
+    if wl.T > 256:      # the tiled kernel: fp64 matrix products, 2 T E D flops
+        flops = 2.0 * wl.T * wl.E * wl.H
+        tfs = flops / (us_l * 1e-6) / 1e12
+        logits_rec = {"us": us_l, "flops": flops, "bytes": nbytes, "achieved": tfs, "unit": "TFLOP/s",
+                      "peak": MFMA_F64_PEAK_TFLOPS, "frac": tfs / MFMA_F64_PEAK_TFLOPS, "bound": "mfma fp64"}
+    else:
+        gbs = nbytes / (us_l * 1e-6) / 1e9
+        logits_rec = {"us": us_l, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                      "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+    return {"moe_router_logits": logits_rec, "moe_router_route": {"us": us_c}}
 
 
 def time_w4a16(N, wl, x, bufs, weights, ab: dict, n: int) -> dict:

@@ -97,16 +97,16 @@ __global__ void __launch_bounds__(kRlThreads) router_logits_kernel(RlArgs a) {
     if (lane < nt) a.logits[(int64_t)(t0 + lane) * a.E + e] = mine;
 }
 
-// Many tokens: an LDS-tiled product. A workgroup computes 32 tokens x 64
-// experts; per 128-column step it stages both operands in LDS as fp64 (each
-// value converted once), then each thread accumulates 2 tokens x 4 experts
-// with fp64 fused multiply-adds (a product of two fp32 values is exact in
-// fp64, so the fused and the separate multiply-add round alike). The next
-// step's operands are loaded into registers while this step computes, so that
-// the memory latency hides behind 128 columns of arithmetic. The fp64 matrix
-// instruction (v_mfma_f64_16x16x4_f64) measured slower than this kernel's
-// unpipelined form.
-constexpr int kTileT = 32, kTileE = 64, kTileK = 128;
+// Many tokens: an LDS-tiled product on the fp64 matrix instruction. A
+// workgroup computes 16 tokens x 64 experts, a wave 16 x 16 with
+// v_mfma_f64_16x16x4_f64; per 128-column step both operands are staged in LDS
+// as fp32 and widened to fp64 as they are read (a product of two fp32 values
+// is exact in fp64, so only the fp64 additions round). The next step's
+// operands are loaded into registers while this step computes, so that the
+// memory latency hides behind 128 columns of arithmetic. Rows are 132 floats
+// apart: the 64 lanes of a read (16 rows x 4 columns) fall on 64 distinct
+// banks.
+constexpr int kTileT = 16, kTileE = 64, kTileK = 128, kTileRow = kTileK + 4;
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 constexpr int kTileXVecs = kTileT * kTileK / 4 / 256;    // float4 of x a thread stages per step
 constexpr int kTileWVecs = kTileE * kTileK / 4 / 256;    // float4 of w
@@ -135,29 +135,22 @@ __device__ __forceinline__ void rl_tile_load(RlTileRegs& r, const RlArgs& a, int
     }
 }
 
-__device__ __forceinline__ void rl_tile_store(const RlTileRegs& r, double (*xs)[kTileK + 1],
-                                              double (*ws)[kTileK + 1]) {
+__device__ __forceinline__ void rl_tile_store(const RlTileRegs& r, float (*xs)[kTileRow], float (*ws)[kTileRow]) {
     const int tid = threadIdx.x, c = (tid & 31) * 4;
 #pragma unroll
-    for (int h = 0; h < kTileXVecs; ++h) {
-        double* d = &xs[(tid >> 5) + 8 * h][c];
-        d[0] = r.x[h].x; d[1] = r.x[h].y; d[2] = r.x[h].z; d[3] = r.x[h].w;
-    }
+    for (int h = 0; h < kTileXVecs; ++h) *reinterpret_cast<float4*>(&xs[(tid >> 5) + 8 * h][c]) = r.x[h];
 #pragma unroll
-    for (int h = 0; h < kTileWVecs; ++h) {
-        double* d = &ws[(tid >> 5) + 8 * h][c];
-        d[0] = r.w[h].x; d[1] = r.w[h].y; d[2] = r.w[h].z; d[3] = r.w[h].w;
-    }
+    for (int h = 0; h < kTileWVecs; ++h) *reinterpret_cast<float4*>(&ws[(tid >> 5) + 8 * h][c]) = r.w[h];
 }
 
 __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
-    __shared__ double xs[kTileT][kTileK + 1];
-    __shared__ double ws[kTileE][kTileK + 1];
+    __shared__ __align__(16) float xs[kTileT][kTileRow];
+    __shared__ __align__(16) float ws[kTileE][kTileRow];
     const int tid = threadIdx.x;
     const int t0 = blockIdx.x * kTileT, e0 = blockIdx.y * kTileE;
     const int lane = tid & 63, n = lane & 15, q = lane >> 4;
     const int ew = 16 * (tid >> 6);                  // the wave's 16 experts: e0 + ew + [0, 16)
-    doublex4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    doublex4 acc = {0, 0, 0, 0};
     RlTileRegs r;
     rl_tile_load(r, a, t0, e0, 0);
     rl_tile_store(r, xs, ws);
@@ -167,9 +160,8 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
         if (more) rl_tile_load(r, a, t0, e0, k0 + kTileK);
 #pragma unroll 8
         for (int k = 0; k < kTileK; k += 4) {
-            const double x0 = xs[n][k + q], x1 = xs[16 + n][k + q], wv = ws[ew + n][k + q];
-            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(x0, wv, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(x1, wv, acc1, 0, 0, 0);
+            const double xv = xs[n][k + q], wv = ws[ew + n][k + q];
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xv, wv, acc, 0, 0, 0);
         }
         __syncthreads();
         if (more) {
@@ -177,13 +169,12 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(RlArgs a) {
             __syncthreads();
         }
     }
-    // lane (n, q) holds tokens q + 4 i of each 16-token block, expert n
+    // lane (n, q) holds tokens q + 4 i of the tile, expert n of the wave's 16
     const int e = e0 + ew + n;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = t0 + q + 4 * i;
-        if (e < a.E && t < a.T) a.logits[(int64_t)t * a.E + e] = __double2float_rn(acc0[i]);
-        if (e < a.E && t + 16 < a.T) a.logits[(int64_t)(t + 16) * a.E + e] = __double2float_rn(acc1[i]);
+        if (e < a.E && t < a.T) a.logits[(int64_t)t * a.E + e] = __double2float_rn(acc[i]);
     }
 }
 
