@@ -12,7 +12,7 @@ profiles/experts_<W>_traffic.json (with the SHA-256 of the kernel sources, so
 that bench.py reports the figure only while they are unchanged) and prints a
 markdown table.
 
-    python -m nvfp4_block_scaled_route_amd.traffic_summary --dir gpurun_out/pmc \\
+    python -m nvfp4_block_scaled_route_amd.traffic_summary --dir <rocprofv3 output dir> \\
         --workload prefill_t4096 --copy-mib 256
 """
 from __future__ import annotations

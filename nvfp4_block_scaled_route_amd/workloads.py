@@ -15,7 +15,7 @@ chunk, and one expert-tensor-parallel slice set (the expert_tp page).
 Every tensor draws from its own child stream of ``SeedSequence(seed)`` so the
 order of generation does not matter.
 
-Readings of the workload descriptions (also listed in the design doc):
+Readings of the workload descriptions:
   * block scales "drawn from U[0.5, 2]": the scale byte is drawn uniformly from
     the e4m3 codes whose values lie in [0.5, 2] (0x30 .. 0x40 inclusive);
   * weight global scales are 1.0, so the per-expert kernel scalars are the
