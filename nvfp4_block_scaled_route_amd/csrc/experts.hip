@@ -400,7 +400,24 @@ __device__ __forceinline__ void wait_ready(int32_t* ready, int target, int32_t* 
     }
 }
 
-template <int D1, int D2>
+// Two output pairs a GEMM2 wave where I = 256 (4 k-tiles, all held from the
+// start): the pairs share the wave's metadata loads, wait, copy and LDS reads.
+template <int D>
+__device__ __forceinline__ void run_two_pairs(const Stage (&sa)[D], const Stage (&sb)[D], const uint8_t* lc,
+                                              const uint8_t* ls, floatx4& a0, floatx4& a1, floatx4& b0,
+                                              floatx4& b1) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        Stage x = sa[d], y = sb[d];
+        lds_act(x.a, x.asf, lc, ls, d);
+        y.a = x.a;
+        y.asf = x.asf;
+        use_stage(x, a0, a1);
+        use_stage(y, b0, b1);
+    }
+}
+
+template <int D1, int D2, int P2>
 __global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint32_t g1_blocks) {
     extern __shared__ __align__(16) uint8_t tile_lds[];
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
@@ -429,17 +446,20 @@ __global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint
             __hip_atomic_fetch_add(a.sync + kSubSyncStride * sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const uint32_t n2 = a.H >> 5;
+    const uint32_t n2 = (a.H >> 5) / P2;        // GEMM2 units a tile
     const uint32_t unit = (blockIdx.x - g1_blocks) * kWavesPerBlock + wave;
-    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2) * P2;   // first output pair
     const RowTile rt = row_tile(a, sub, n);
     if (rt.e < 0) return;
     const int e = rt.e;
-    Streams p;
+    Streams p, p1;
     p.wc = a.w.w2 + e * a.w.w2_expert_stride_bytes + c * a.w.w2_pair_stride_bytes + lane * 16;
     p.ws = a.w.w2_sf + e * a.w.w2_sf_expert_stride_bytes + c * a.w.w2_sf_pair_stride_bytes + lane * 2;
-    Stage st[D2];
+    p1.wc = p.wc + a.w.w2_pair_stride_bytes;
+    p1.ws = p.ws + a.w.w2_sf_pair_stride_bytes;
+    Stage st[D2], st1[P2 == 2 ? D2 : 1];
     preload_w<D2>(st, p);
+    if constexpr (P2 == 2) preload_w<D2>(st1, p1);
     int32_t* ready = a.sync + kSubSyncStride * sub;
     if (wave == 0) wait_ready(ready, a.I >> 6, a.status);
     __syncthreads();
@@ -449,14 +469,21 @@ __global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // this wave's part of the copy has landed
     __syncthreads();
     if (threadIdx.x == 0 &&
-        __hip_atomic_fetch_add(ready + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (a.H >> 7) - 1) {
+        __hip_atomic_fetch_add(ready + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (a.H >> (6 + P2)) - 1) {
         __hip_atomic_store(ready, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(ready + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const uint8_t* ls = tile_lds + (a.I >> 1) * 16 + n * 16 + q;
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    stream_lds_run<D2>(st, p, lc, ls, a.I >> 6, acc0, acc1);
-    gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+    if constexpr (P2 == 2) {
+        floatx4 acc2 = {0, 0, 0, 0}, acc3 = {0, 0, 0, 0};
+        run_two_pairs<D2>(st, st1, lc, ls, acc0, acc1, acc2, acc3);
+        gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+        gemm2_epilogue(a, rt, e, c + 1, n, q, acc2, acc3);
+    } else {
+        stream_lds_run<D2>(st, p, lc, ls, a.I >> 6, acc0, acc1);
+        gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+    }
 }
 
 // ---------------------------------------------------------------- launch
@@ -523,15 +550,19 @@ MOE_LAUNCH_WG(gemm2_wg_kernel)
 // a wave per SIMD and were slower, and 6 measured no better than 4.
 static int fused_depth2(int kt2) { return kt2 % 8 == 0 ? 8 : 4; }
 
-static void launch_fused(int d1, int d2, dim3 grid, unsigned lds, hipStream_t s, const ExpArgs& a,
-                         uint32_t g1_blocks) {
-#define MOE_FUSED(D1, D2) hipLaunchKernelGGL((experts_fused_kernel<D1, D2>), grid, dim3(kThreads), lds, s, a, g1_blocks)
-    if (d1 == 8) {
-        if (d2 == 8) MOE_FUSED(8, 8);
-        else MOE_FUSED(8, 4);
+static void launch_fused(int d1, int d2, bool two_pairs, dim3 grid, unsigned lds, hipStream_t s,
+                         const ExpArgs& a, uint32_t g1_blocks) {
+#define MOE_FUSED(D1, D2, P2) \
+    hipLaunchKernelGGL((experts_fused_kernel<D1, D2, P2>), grid, dim3(kThreads), lds, s, a, g1_blocks)
+    if (two_pairs) {
+        if (d1 == 8) MOE_FUSED(8, 4, 2);
+        else MOE_FUSED(4, 4, 2);
+    } else if (d1 == 8) {
+        if (d2 == 8) MOE_FUSED(8, 8, 1);
+        else MOE_FUSED(8, 4, 1);
     } else {
-        if (d2 == 8) MOE_FUSED(4, 8);
-        else MOE_FUSED(4, 4);
+        if (d2 == 8) MOE_FUSED(4, 8, 1);
+        else MOE_FUSED(4, 4, 1);
     }
 #undef MOE_FUSED
 }
@@ -611,7 +642,10 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int3
         const unsigned lds = (unsigned)(tile_lds_bytes(H) > tile_lds_bytes(I) ? tile_lds_bytes(H) : tile_lds_bytes(I));
         const int f1 = kt1 % 8 == 0 ? 8 : 4;
         const int f2 = fused_depth2((int)kt2);
-        launch_fused(f1, f2, dim3((unsigned)(grid1 + grid2)), lds, s, args, (uint32_t)grid1);
+        // I = 256: a GEMM2 wave holds all 4 k-tiles of two output pairs (H % 256 == 0)
+        const bool two_pairs = kt2 == 4 && H % 256 == 0;
+        const int64_t g2 = two_pairs ? grid2 / 2 : grid2;
+        launch_fused(f1, f2, two_pairs, dim3((unsigned)(grid1 + g2)), lds, s, args, (uint32_t)grid1);
         return check_launch("moe_experts_fwd (GEMM1 + GEMM2)");
     }
     if (wg1) launch_gemm1_wg_kernel(wg_depth((int)kt1, kWgDepth1), dim3((unsigned)grid1), (unsigned)tile_lds_bytes(H), s, args);

@@ -355,14 +355,16 @@ def test_layer_parity_tiled_path(T, H, I, E, K, m):
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 16),
                                          (7, 512, 768, 16, 4, 32), (3, 1024, 512, 4, 2, 16),
-                                         (4, 512, 320, 8, 2, 16), (9, 768, 1280, 8, 3, 16)])
+                                         (4, 512, 320, 8, 2, 16), (9, 768, 1280, 8, 3, 16),
+                                         (6, 512, 256, 8, 2, 16), (5, 1024, 256, 8, 3, 32)])
 def test_layer_parity_streaming_kernel_choices(T, H, I, E, K, m):
     """Few routes per expert, shapes that take each expert kernel: GEMM1 on the
     one-wave kernel (H % 256 != 0) or on the workgroup kernel with the LDS copy
     of the activation, GEMM2 likewise (I % 256 and H % 128), and both GEMMs in
     one launch where both workgroup forms apply (H % 256 == 0 and I % 256 == 0:
-    GEMM2 weight preloads of 8 and 4 k-tiles, GEMM1 depths 8 and 4);
-    two-launch pipeline depths 5 (H/64), 3, 6 (I/64 = 12) and 8."""
+    GEMM2 weight preloads of 8 and 4 k-tiles, GEMM1 depths 8 and 4, and at
+    I = 256 two output pairs a GEMM2 wave); two-launch pipeline depths 5
+    (H/64), 3, 6 (I/64 = 12) and 8."""
     from oracle.layer import intermediate_amax
     wl = W.Workload(f"stream_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E, K=K, tile_m=m, seed=5)
     probe = W.make_inputs(wl, a2_gscale=1.0)
