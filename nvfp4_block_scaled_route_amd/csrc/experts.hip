@@ -400,20 +400,17 @@ __device__ __forceinline__ void wait_ready(int32_t* ready, int target, int32_t* 
     }
 }
 
-// Two output pairs a GEMM2 wave where I = 256 (4 k-tiles, all held from the
-// start): the pairs share the wave's metadata loads, wait, copy and LDS reads.
+// A GEMM2 unit whose D = KT weight k-tiles are all held in st (I = 256: two
+// output pairs a wave, run one after the other, share the wave's metadata
+// loads, wait and copy).
 template <int D>
-__device__ __forceinline__ void run_two_pairs(const Stage (&sa)[D], const Stage (&sb)[D], const uint8_t* lc,
-                                              const uint8_t* ls, floatx4& a0, floatx4& a1, floatx4& b0,
-                                              floatx4& b1) {
+__device__ __forceinline__ void run_held(const Stage (&st)[D], const uint8_t* lc, const uint8_t* ls, floatx4& acc0,
+                                         floatx4& acc1) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        Stage x = sa[d], y = sb[d];
+        Stage x = st[d];
         lds_act(x.a, x.asf, lc, ls, d);
-        y.a = x.a;
-        y.asf = x.asf;
-        use_stage(x, a0, a1);
-        use_stage(y, b0, b1);
+        use_stage(x, acc0, acc1);
     }
 }
 
@@ -476,10 +473,12 @@ __global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint
     const uint8_t* ls = tile_lds + (a.I >> 1) * 16 + n * 16 + q;
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     if constexpr (P2 == 2) {
-        floatx4 acc2 = {0, 0, 0, 0}, acc3 = {0, 0, 0, 0};
-        run_two_pairs<D2>(st, st1, lc, ls, acc0, acc1, acc2, acc3);
+        run_held<D2>(st, lc, ls, acc0, acc1);
         gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
-        gemm2_epilogue(a, rt, e, c + 1, n, q, acc2, acc3);
+        acc0 = floatx4{0, 0, 0, 0};
+        acc1 = floatx4{0, 0, 0, 0};
+        run_held<D2>(st1, lc, ls, acc0, acc1);
+        gemm2_epilogue(a, rt, e, c + 1, n, q, acc0, acc1);
     } else {
         stream_lds_run<D2>(st, p, lc, ls, a.I >> 6, acc0, acc1);
         gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
