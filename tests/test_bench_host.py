@@ -1,0 +1,85 @@
+"""Host-side accounting of bench.py, on the CPU: the algorithmic bytes and
+flops it divides by (checked against the per-expert weight bytes 27/16 I H and
+the 6 R H I matrix flops of the routed rows), the dispatch rule that picks the
+MFMA roofline, the committed HBM-traffic record and its source hash, and the
+refusal of more than one GPU."""
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from nvfp4_block_scaled_route_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_weight_bytes_per_expert():
+    """w13 codes + scales (2I x H/2, 2I x H/16) and w2 codes + scales (H x I/2,
+    H x I/16): 27/16 I H bytes an expert; decode_b8's 42 touched experts are the
+    111 476 736 weight bytes its bench line reports."""
+    for name in ("decode_b8", "decode_b64_zipf", "expert_tp8_b32", "prefill_t4096"):
+        wl = W.WORKLOADS[name]
+        counts = np.zeros(wl.E, np.int64)
+        counts[0] = 1
+        ab = bench.algorithmic_bytes(wl, counts)
+        assert ab["weights"] * 16 == 27 * wl.I * wl.H, name
+    wl = W.WORKLOADS["decode_b8"]
+    counts = np.zeros(wl.E, np.int64)
+    counts[:42] = 1
+    counts[:22] += 1                                     # 64 routes over 42 experts
+    ab = bench.algorithmic_bytes(wl, counts)
+    assert ab["touched"] == 42 and ab["weights"] == 111_476_736
+    routes = int(counts.sum())
+    assert routes == 64
+    other = wl.T * (wl.H // 2 + wl.H // 16) + 2 * routes * (wl.I // 2 + wl.I // 16) + routes * wl.H * 2
+    assert ab["other"] == other and ab["total"] == ab["weights"] + other
+
+
+def test_matrix_flops_of_the_routed_rows():
+    """GEMM1 (2I x H) and GEMM2 (H x I) per route, 2 flops a multiply-add:
+    6 R H I; prefill_t4096's 32768 routes give 1.237 TFLOP."""
+    wl = W.WORKLOADS["prefill_t4096"]
+    counts = np.full(wl.E, wl.T * wl.K // wl.E, np.int64)
+    f = bench.algorithmic_flops(wl, counts)
+    assert f == 6.0 * wl.T * wl.K * wl.H * wl.I
+    assert abs(f - 1.23695e12) < 1e8
+
+
+def test_roofline_choice_follows_the_dispatch_rule():
+    """The register-tiled MFMA kernels (and the f16 MFMA roofline) only where
+    an expert has on average a quarter of a 128-row block or more."""
+    assert bench.mfma_bound(W.WORKLOADS["prefill_t4096"])
+    for name in ("decode_b8", "decode_b64_zipf", "expert_tp8_b32", "tiny"):
+        assert not bench.mfma_bound(W.WORKLOADS[name]), name
+
+
+def test_traffic_record_matches_its_sources(tmp_path, monkeypatch):
+    """The committed record is used while the kernel sources hash the same,
+    and dropped (None) once one of them changes."""
+    for name in ("decode_b8", "prefill_t4096"):
+        with open(os.path.join(ROOT, "profiles", f"experts_{name}_traffic.json")) as f:
+            rec = json.load(f)
+        assert bench.measured_traffic(name) == float(rec["traffic_bytes"])
+    with open(os.path.join(ROOT, "profiles", "experts_decode_b8_traffic.json")) as f:
+        rec = json.load(f)
+    for src in rec["sources"]:
+        os.makedirs(tmp_path / os.path.dirname(src), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, src), tmp_path / src)
+    os.makedirs(tmp_path / "profiles")
+    shutil.copy(os.path.join(ROOT, "profiles", "experts_decode_b8_traffic.json"), tmp_path / "profiles")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("decode_b8") == float(rec["traffic_bytes"])
+    with open(tmp_path / rec["sources"][0], "ab") as f:
+        f.write(b"\n// changed\n")
+    assert bench.measured_traffic("decode_b8") is None
+    assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
