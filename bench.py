@@ -8,7 +8,10 @@ come from HBM (the cold-cache timing the flashinfer_ops page's tuning
 configuration asks for). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. ``roofline`` is the dominant kernel (the experts step),
-timed with HIP events on its own stream. With few routes per expert (decode)
+timed with HIP events on its own stream: ``kernel_ms`` over 16 consecutive
+steps replayed from one graph (back to back, as the layer runs them), and
+``kernel_ms_isolated`` one step at a time behind a sleep kernel, which adds a
+launch's dispatch to each. With few routes per expert (decode)
 it is bound by HBM: algorithmic bytes per launch (codes + e4m3 scales of the
 experts that have a route, the NVFP4 input read once, the NVFP4 intermediate
 written and re-read, the GEMM2 rows written) over its average duration. With
@@ -291,25 +294,51 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # the dominant kernel, timed with HIP events on the stream it is launched on;
-    # a sleep kernel ahead of each timed launch keeps host enqueue time out of it
+    # the dominant kernel, timed with HIP events on the stream it is launched on
     counts = bufs.meta[bufs.layout.expert_counts:bufs.layout.expert_counts + wl.E].cpu().numpy()
     ab = algorithmic_bytes(wl, counts)
     s = torch.cuda.current_stream()
     n_k = min(args.steps, 400)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
     I_part = wl.I // wl.tp
-    for i in range(n_k):
+
+    def expert_step(i, stream):
         w = weights[i % copies]
         sl = [w] if wl.tp == 1 else [LY.slice_weights(w, r, wl.tp, wl.H, wl.I) for r in range(wl.tp)]
-        torch.cuda._sleep(20000)
-        ev[i][0].record(s)
         for r, ww in enumerate(sl):
             N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H,
-                              I_part, wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], s)
+                              I_part, wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
+
+    # (1) one step at a time, a sleep kernel ahead of each so that host enqueue
+    # time stays out: the step's duration plus one launch's dispatch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    for i in range(n_k):
+        torch.cuda._sleep(20000)
+        ev[i][0].record(s)
+        expert_step(i, s)
         ev[i][1].record(s)
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    k_ms_isolated = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # (2) 16 consecutive steps (weight copies rotating) captured in one graph and
+    # replayed between two events: the launches run back to back, as the
+    # layer's do, and the per-step figure is the kernel's own duration plus the
+    # gap between consecutive launches
+    group = 16
+    g_steps = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_steps, stream=cap):
+        for j in range(group):
+            expert_step(j, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g_steps.replay()
+    torch.cuda.synchronize()
+    n_g = max(4, n_k // group)
+    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_g)]
+    for a, b in evg:
+        torch.cuda._sleep(20000)
+        a.record(s)
+        g_steps.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evg])) / group
     achieved = ab["total"] / (k_ms * 1e-3) / 1e9
 
     routes = wl.T * wl.K
@@ -333,7 +362,7 @@ def main():
                            "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                            "algorithmic_flops": flops, "algorithmic_bytes": ab["total"], "hbm_gbs": achieved,
-                           "kernel_ms": k_ms}
+                           "kernel_ms": k_ms, "kernel_ms_isolated": k_ms_isolated}
     else:
         out["roofline"] = {"bound": "hbm", "kernel": "moe_experts_fwd (experts_fused_kernel: GEMM1+SwiGLU+requant "
                                                      "and GEMM2 in one launch)",
@@ -341,7 +370,8 @@ def main():
                            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
-                           "experts_touched": ab["touched"], "kernel_ms": k_ms}
+                           "experts_touched": ab["touched"], "kernel_ms": k_ms,
+                           "kernel_ms_isolated": k_ms_isolated}
     extra = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
     if wl.tp == 1 and not mfma_bound(wl):          # on the layer's routing, before the router rewrites it
         extra["moe_experts_fwd_w4a16"] = time_w4a16(N, wl, x, bufs, weights, ab, n_k)
