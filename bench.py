@@ -103,26 +103,19 @@ def time_norm_quant(N, x, norm_w, gscale, wl, n: int) -> dict:
     T, H = wl.T, wl.H
     codes = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
     sf = torch.empty((T, H // 16), dtype=torch.uint8, device=x.device)
-    s = torch.cuda.current_stream()
-    for _ in range(3):
-        N.nvfp4_norm_quant(x, norm_w, 1.0, 1e-6, gscale, codes, sf, s)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in ev:
-        torch.cuda._sleep(20000)
-        a.record(s)
-        N.nvfp4_norm_quant(x, norm_w, 1.0, 1e-6, gscale, codes, sf, s)
-        b.record(s)
-    torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    us, us_iso = _event_us(lambda s: N.nvfp4_norm_quant(x, norm_w, 1.0, 1e-6, gscale, codes, sf, s), n)
     nbytes = T * (2 * H + H // 2 + H // 16) + 2 * H
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"us": us, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
-            "frac": gbs / HBM_PEAK_GBS, "bound": "hbm" if T >= 1024 else "latency"}
+    return {"us": us, "us_isolated": us_iso, "bytes": nbytes, "achieved": gbs, "unit": "GB/s",
+            "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "bound": "hbm" if T >= 1024 else "latency"}
 
 
-def _event_us(fn, n: int) -> float:
-    """Mean event-timed duration of fn() on the current stream, each launch
-    behind a sleep kernel so that host enqueue time stays out of it."""
+def _event_us(fn, n: int, group: int = 16):
+    """Event-timed duration of fn(stream) in microseconds, as (back to back,
+    isolated): 16 consecutive calls captured in one graph and replayed between
+    two events, and single calls each between two events; a sleep kernel ahead
+    of every timed region keeps host enqueue time out of it, and the isolated
+    figure also holds one launch's dispatch."""
     import torch
     s = torch.cuda.current_stream()
     for _ in range(3):
@@ -134,7 +127,25 @@ def _event_us(fn, n: int) -> float:
         fn(s)
         b.record(s)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    iso = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for _ in range(group):
+            fn(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(4, n // group))]
+    for a, b in evg:
+        torch.cuda._sleep(20000)
+        a.record(s)
+        g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    batched = float(np.mean([a.elapsed_time(b) for a, b in evg])) * 1e3 / group
+    del g
+    return batched, iso
 
 
 def time_router(N, W, wl, bufs, n: int) -> dict:
@@ -146,20 +157,22 @@ def time_router(N, W, wl, bufs, n: int) -> dict:
     x = torch.from_numpy(xr).to(bufs.ids.device)
     w = torch.from_numpy(wr).to(bufs.ids.device)
     logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=x.device)
-    us_l = _event_us(lambda s: N.moe_router_logits(x, w, logits, s), n)
-    us_c = _event_us(lambda s: N.moe_router_route(x, w, None, None, wl.K, 1.0, wl.tile_m, 0, wl.E, logits,
-                                                  bufs.ids, bufs.weights, bufs.meta, s), n)
+    us_l, iso_l = _event_us(lambda s: N.moe_router_logits(x, w, logits, s), n)
+    us_c, iso_c = _event_us(lambda s: N.moe_router_route(x, w, None, None, wl.K, 1.0, wl.tile_m, 0, wl.E, logits,
+                                                          bufs.ids, bufs.weights, bufs.meta, s), n)
     nbytes = 4 * (wl.T * wl.H + wl.E * wl.H + wl.T * wl.E)
     if wl.T > 256:      # the tiled kernel: fp64 matrix products, 2 T E D flops
         flops = 2.0 * wl.T * wl.E * wl.H
         tfs = flops / (us_l * 1e-6) / 1e12
-        logits_rec = {"us": us_l, "flops": flops, "bytes": nbytes, "achieved": tfs, "unit": "TFLOP/s",
+        logits_rec = {"us": us_l, "us_isolated": iso_l, "flops": flops, "bytes": nbytes, "achieved": tfs,
+                      "unit": "TFLOP/s",
                       "peak": MFMA_F64_PEAK_TFLOPS, "frac": tfs / MFMA_F64_PEAK_TFLOPS, "bound": "mfma fp64"}
     else:
         gbs = nbytes / (us_l * 1e-6) / 1e9
-        logits_rec = {"us": us_l, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
+        logits_rec = {"us": us_l, "us_isolated": iso_l, "bytes": nbytes, "achieved": gbs, "unit": "GB/s",
+                      "peak": HBM_PEAK_GBS,
                       "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
-    return {"moe_router_logits": logits_rec, "moe_router_route": {"us": us_c}}
+    return {"moe_router_logits": logits_rec, "moe_router_route": {"us": us_c, "us_isolated": iso_c}}
 
 
 def time_w4a16(N, wl, x, bufs, weights, ab: dict, n: int) -> dict:
@@ -176,12 +189,12 @@ def time_w4a16(N, wl, x, bufs, weights, ab: dict, n: int) -> dict:
         k[0] += 1
         N.moe_experts_fwd_w4a16(x, bufs.meta, w, wl.T, wl.K, wl.E, wl.H, wl.I, wl.tile_m, inter, bufs.rows[0], s)
 
-    us = _event_us(call, n)
+    us, us_iso = _event_us(call, n)
     routes = wl.T * wl.K
     nbytes = ab["weights"] + wl.T * wl.H * 2 + 2 * routes * wl.I * 2 + routes * wl.H * 2
     gbs = nbytes / (us * 1e-6) / 1e9
-    return {"us": us, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
-            "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+    return {"us": us, "us_isolated": us_iso, "bytes": nbytes, "achieved": gbs, "unit": "GB/s",
+            "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
 
 
 def time_bf16(N, W, wl, x, bufs, counts, n: int) -> dict:
@@ -203,15 +216,15 @@ def time_bf16(N, W, wl, x, bufs, counts, n: int) -> dict:
         N.moe_experts_fwd_bf16(x, bufs.meta, w13, w2, wl.T, wl.K, wl.E, wl.H, wl.I, wl.tile_m, inter,
                                bufs.rows[0], s)
 
-    us = _event_us(call, n)
+    us, us_iso = _event_us(call, n)
     routes = wl.T * wl.K
     touched = int((counts > 0).sum())
     nbytes = touched * 6 * wl.I * wl.H + wl.T * wl.H * 2 + 2 * routes * wl.I * 2 + routes * wl.H * 2
     gbs = nbytes / (us * 1e-6) / 1e9
     del copies
     torch.cuda.empty_cache()
-    return {"us": us, "bytes": nbytes, "achieved": gbs, "unit": "GB/s", "peak": HBM_PEAK_GBS,
-            "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+    return {"us": us, "us_isolated": us_iso, "bytes": nbytes, "achieved": gbs, "unit": "GB/s",
+            "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
 
 
 def cpu_baseline(inp, seconds: float) -> dict:
