@@ -59,6 +59,76 @@ def test_gemm_unit_scales_is_integer_matmul():
     assert np.array_equal(acc * 4, (ai @ wi.T).astype(np.float64))
 
 
+def test_gemm2_against_rational_triple_loop():
+    """GEMM2 of routes whose experts interleave (2, 0, 1, 0, 2): every route's
+    intermediate row against its own expert's w2, summed as rationals. A row
+    gathered from the wrong route or the wrong expert's weights fails it."""
+    rng = np.random.default_rng(8)
+    R, H, I, E = 5, 32, 64, 3
+    h_codes, h_sf = _rand_nvfp4(rng, R, I)
+    w_codes = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w_sf = rng.integers(0x01, 0x7E, (E, H, I // 16), dtype=np.uint8)
+    experts = np.array([2, 0, 1, 0, 2])
+    acc = ex.gemm2(h_codes, h_sf, experts, w_codes, w_sf)
+    Hn = F.unpack_nibbles(h_codes)
+    Wn = F.unpack_nibbles(w_codes)
+    e2m1 = [Fraction(v) for v in F.E2M1]
+    e4m3 = [Fraction(v) if np.isfinite(v) else None for v in F.E4M3]
+    for r, e in enumerate(experts):
+        for n in range(H):
+            tot = Fraction(0)
+            for i in range(I):
+                tot += (e2m1[Hn[r, i]] * e4m3[h_sf[r, i // 16]]
+                        * e2m1[Wn[e, n, i]] * e4m3[w_sf[e, n, i // 16]])
+            assert Fraction(acc[r, n]) == tot
+
+
+def test_gemm2_unit_scales_is_integer_matmul_per_expert():
+    """Unit scales: each route's row is the integer product of its own
+    intermediate codes with its expert's w2 codes (experts interleaved)."""
+    rng = np.random.default_rng(9)
+    R, N, K, E = 7, 40, 128, 3
+    h_codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    w_codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    one = np.full((R, K // 16), 0x38, np.uint8)
+    wone = np.full((E, N, K // 16), 0x38, np.uint8)
+    experts = np.array([1, 2, 0, 1, 0, 2, 1])
+    acc = ex.gemm2(h_codes, one, experts, w_codes, wone)
+    half_units = np.rint(F.E2M1 * 2).astype(np.int64)
+    hi = half_units[F.unpack_nibbles(h_codes)]
+    for r, e in enumerate(experts):
+        wi = half_units[F.unpack_nibbles(w_codes[e])]
+        assert np.array_equal(acc[r] * 4, (wi @ hi[r]).astype(np.float64))
+
+
+def test_experts_forward_gathers_tokens_per_route():
+    """Routes whose tokens differ from their index and repeat (3, 0, 3, 1):
+    each route's rows equal those of the same (token, expert) run alone."""
+    rng = np.random.default_rng(10)
+    T, H, I, E = 4, 128, 64, 2
+    a_codes, a_sf = _rand_nvfp4(rng, T, H)
+    w13c = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
+    w13s = rng.integers(0x30, 0x41, (E, 2 * I, H // 16), dtype=np.uint8)
+    w2c = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w2s = rng.integers(0x30, 0x41, (E, H, I // 16), dtype=np.uint8)
+    g1a = rng.uniform(0.5, 1.5, E).astype(np.float32)
+    g1c = (rng.uniform(0.5, 1.5, E) * 0.05).astype(np.float32)
+    g2a = rng.uniform(0.5, 1.5, E).astype(np.float32)
+    tokens = np.array([3, 0, 3, 1])
+    experts = np.array([1, 0, 0, 1])
+    fw = ex.experts_forward(a_codes, a_sf, tokens, experts, w13c, w13s, w2c, w2s, g1a, g1c, g2a)
+    for r, (t, e) in enumerate(zip(tokens, experts)):
+        one = ex.experts_forward(a_codes[t:t + 1], a_sf[t:t + 1], [0], [0], w13c[e:e + 1],
+                                 w13s[e:e + 1], w2c[e:e + 1], w2s[e:e + 1], g1a[e:e + 1],
+                                 g1c[e:e + 1], g2a[e:e + 1])
+        assert np.array_equal(fw["acc1"][r], one["acc1"][0])
+        assert np.array_equal(fw["h_codes"][r], one["h_codes"][0])
+        assert np.array_equal(fw["acc2"][r], one["acc2"][0])
+        assert np.array_equal(fw["rows"][r], one["rows"][0])
+    # the two routes of token 3 go to different experts: different rows
+    assert not np.array_equal(fw["acc1"][0], fw["acc1"][2])
+
+
 def test_exactness_guard_raises():
     a = np.full((1, 4096), 2688.0)
     with pytest.raises(ArithmeticError):
@@ -102,6 +172,38 @@ def test_finalize_k1_is_textbook_rmsnorm():
     x = torch.from_numpy(F.bf16_to_f64(rows))
     g = torch.from_numpy(F.bf16_to_f64(w_bf16))
     ref = torch.nn.functional.rms_norm(x, (H,), g, eps=float(np.float32(1e-6))).numpy()
+    assert np.array_equal(out, F.f64_to_bf16(ref.astype(np.float32).astype(np.float64)))
+
+
+def test_finalize_weight_before_norm_closed_form():
+    """A unit row under a gain alternating 2, 0: with the weight applied before
+    the norm, z = (2, 0, 2, 0, ...) has mean square 2 and y = sqrt(2) on the even
+    columns; with the weight after it, r / rms(r) = 1 and y = 2. Normalizing by
+    the rms of r instead of that of gamma * r gives 2, not sqrt(2)."""
+    H = 64
+    rows = F.f32_to_bf16(np.ones((1, H), np.float32))
+    gamma = np.tile(np.array([2.0, 0.0], np.float32), H // 2)
+    w_bf16 = F.f32_to_bf16(gamma)                                   # gain centre 0
+    e2p = np.zeros((1, 1), np.int64)
+    wk = np.ones((1, 1), np.float32)
+    before = F.bf16_to_f64(finalize(rows, e2p, wk, w_bf16, 0.0, 0.0, True))[0]
+    after = F.bf16_to_f64(finalize(rows, e2p, wk, w_bf16, 0.0, 0.0, False))[0]
+    assert np.all(before[1::2] == 0) and np.all(after[1::2] == 0)
+    assert np.all(before[0::2] == F.bf16_to_f64(F.f64_to_bf16(np.array([np.sqrt(2.0)])))[0])
+    assert np.all(after[0::2] == 2.0)
+
+
+def test_finalize_weight_before_norm_is_textbook_rmsnorm_of_the_weighted_row():
+    """With the weight before the norm, K = 1 and w = 1, the output is the
+    library RMSNorm (no weight) of gamma * r, gamma = stored weight + centre."""
+    rng = np.random.default_rng(12)
+    T, H = 5, 256
+    rows = F.f32_to_bf16((rng.standard_normal((T, H)) * 7).astype(np.float32))
+    nw = F.f32_to_bf16(rng.uniform(-0.5, 0.5, H).astype(np.float32))
+    out = finalize(rows, np.arange(T)[:, None], np.ones((T, 1), np.float32), nw, 1.0, 1e-6, True)
+    gamma = (F.bf16_to_f64(nw).astype(np.float32) + np.float32(1.0)).astype(np.float64)
+    z = torch.from_numpy(F.bf16_to_f64(rows) * gamma)
+    ref = torch.nn.functional.rms_norm(z, (H,), None, eps=float(np.float32(1e-6))).numpy()
     assert np.array_equal(out, F.f64_to_bf16(ref.astype(np.float32).astype(np.float64)))
 
 
