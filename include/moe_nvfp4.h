@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 4
+#define MOE_NVFP4_ABI_VERSION 5
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -79,7 +79,10 @@ int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
  *                                and for every row >= total_rows
  *   tile_expert     [rows_max/m] local expert of each tile; -1 beyond num_tiles
  *   sync_status     [1]          0; moe_experts_fwd sets 1 if one of its waits
- *                                gave up (its results are then not valid)
+ *                                gave up: its intermediate and rows are then NOT
+ *                                valid, and neither is anything computed from them
+ *                                (a caller that cannot rule this out reads the word
+ *                                after the stream completes and drops the results)
  *   sub_sync        [256*subs_max] (subs_max = rows_max/16): two counters per
  *                                16-row tile s, at 256*s and 256*s + 1 (1 KB
  *                                apart, so that the polls on different tiles
@@ -275,6 +278,46 @@ typedef struct moe_nvfp4_weights {
     const float* g1_scale_c;
     const float* g2_alphas;
 } moe_nvfp4_weights;
+
+/* Host-only check of a converted-weight descriptor for E_local experts of H x I
+ * (I: the full intermediate width the descriptor spans), and for tp > 1 of its
+ * cut into tp intermediate slices -- why the weights cannot be cut tp ways, as
+ * the expert_tp page's "unsupported" and "shape_of" state it: tp must divide I,
+ * and the slice I/tp and H must be multiples of 64 and 128 (the scale tile's
+ * k-width and row count), so that every slice is a byte view of the converted
+ * layout (moe_experts_fwd on the view). Checks every pointer for NULL and
+ * 16-byte alignment and every stride against the shape, as moe_experts_fwd
+ * does before a launch. Reads no device memory and launches nothing.
+ * Returns MOE_OK, MOE_EINVAL (NULL, alignment, strides) or MOE_EUNSUPPORTED
+ * (shape, limits, the tp cut), with the reason in moe_last_error(). */
+int moe_validate_weights(const moe_nvfp4_weights* w, int E_local, int H, int I, int tp);
+
+/* The device buffers one layer call reads and writes besides its inputs and
+ * its output (the flashinfer_ops page: buffers are sized once, "gemm2_rows"
+ * bounds the routed rows), as byte offsets into one caller-owned allocation,
+ * each a multiple of 256:
+ *   meta          int32 [moe_meta_layout_get(T, K, E_local, tile_m).total_ints]
+ *   topk_ids      int32 [T, K];  topk_weights fp32 [T, K]
+ *   a_codes       uint8 [T, H/2];  a_sf uint8 [T, H/16]   (the quantized input)
+ *   inter_codes   uint8 [rows_max, (I/tp)/2];  inter_sf uint8 [rows_max, (I/tp)/16]
+ *   rows          bf16 [tp, rows_max, H]   (one GEMM2 partial per expert-TP slice)
+ * rows_max = moe_rows_max(T, K, E_local, tile_m). Returns total_bytes and
+ * fills *layout when it is not NULL; -1 for invalid arguments (the reason in
+ * moe_last_error()). Host only: reads and launches nothing. */
+typedef struct moe_workspace_layout {
+    int64_t meta;
+    int64_t topk_ids;
+    int64_t topk_weights;
+    int64_t a_codes;
+    int64_t a_sf;
+    int64_t inter_codes;
+    int64_t inter_sf;
+    int64_t rows;
+    int64_t total_bytes;
+} moe_workspace_layout;
+
+int64_t moe_workspace_bytes(int T, int K, int E_local, int H, int I, int tile_m, int tp,
+                            moe_workspace_layout* layout);
 
 /* ------------------------------------------------------------------ experts
  * The routed experts up to the GEMM2 rows, as the op with do_finalize=False

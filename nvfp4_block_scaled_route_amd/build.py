@@ -35,7 +35,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
+           "-Wno-unused-result", "-Werror=inline-asm", "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -46,6 +46,34 @@ moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m) {
     return L;
 }
 
+int check_weights(const moe_nvfp4_weights* w, int H, int I, bool need_scale_c, const char* name) {
+    if (!w) return fail(MOE_EINVAL, "%s: NULL weights", name);
+    if (!w->w13 || !w->w13_sf || !w->w2 || !w->w2_sf || !w->g1_alphas || !w->g2_alphas ||
+        (need_scale_c && !w->g1_scale_c))
+        return fail(MOE_EINVAL, "%s: NULL weight pointer", name);
+    const void* ptrs[] = {w->w13, w->w13_sf, w->w2, w->w2_sf, w->g1_alphas, w->g2_alphas};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return fail(MOE_EINVAL, "%s: weight pointers must be 16-byte aligned", name);
+    if (need_scale_c && !aligned16(w->g1_scale_c))
+        return fail(MOE_EINVAL, "%s: weight pointers must be 16-byte aligned", name);
+    const int64_t kt1 = H / 64, kt2 = I / 64;
+    if (w->w13_pair_stride_bytes < kt1 * kSlotBytes || w->w13_sf_pair_stride_bytes < kt1 * kSlotSfBytes ||
+        w->w2_pair_stride_bytes < kt2 * kSlotBytes || w->w2_sf_pair_stride_bytes < kt2 * kSlotSfBytes ||
+        (w->w13_pair_stride_bytes | w->w13_sf_pair_stride_bytes | w->w2_pair_stride_bytes |
+         w->w2_sf_pair_stride_bytes) % 16)
+        return fail(MOE_EINVAL, "%s: pair strides too small or not multiples of 16", name);
+    if (w->w13_expert_stride_bytes < (int64_t)(I / 16) * w->w13_pair_stride_bytes ||
+        w->w13_sf_expert_stride_bytes < (int64_t)(I / 16) * w->w13_sf_pair_stride_bytes ||
+        w->w2_expert_stride_bytes < (int64_t)(H / 32) * w->w2_pair_stride_bytes ||
+        w->w2_sf_expert_stride_bytes < (int64_t)(H / 32) * w->w2_sf_pair_stride_bytes ||
+        (w->w13_expert_stride_bytes | w->w13_sf_expert_stride_bytes | w->w2_expert_stride_bytes |
+         w->w2_sf_expert_stride_bytes) % 16)
+        return fail(MOE_EINVAL, "%s: expert strides too small or not multiples of 16", name);
+    return MOE_OK;
+}
+
+static int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
 }  // namespace moe
 
 extern "C" {
@@ -69,6 +97,54 @@ int moe_meta_layout_get(int T, int K, int E_local, int tile_m, moe_meta_layout* 
                          tile_m);
     *out = moe::meta_layout(T, K, E_local, tile_m);
     return MOE_OK;
+}
+
+int moe_validate_weights(const moe_nvfp4_weights* w, int E_local, int H, int I, int tp) {
+    using namespace moe;
+    const char* name = "moe_validate_weights";
+    if (E_local < 1 || E_local > MOE_MAX_EXPERTS)
+        return fail(MOE_EINVAL, "%s: E_local=%d out of range", name, E_local);
+    if (H < 64 || H % 64 || I < 64 || I % 64 || H > MOE_MAX_HIDDEN || I > MOE_MAX_HIDDEN)
+        return fail(MOE_EUNSUPPORTED, "%s: H=%d and I=%d must be multiples of 64 up to %d", name, H, I,
+                    MOE_MAX_HIDDEN);
+    if (tp < 1) return fail(MOE_EINVAL, "%s: tp=%d must be at least 1", name, tp);
+    if (tp > 1) {
+        if (I % tp) return fail(MOE_EUNSUPPORTED, "%s: intermediate %d does not split %d ways", name, I, tp);
+        if ((I / tp) % 64 || H % 128)
+            return fail(MOE_EUNSUPPORTED, "%s: intermediate slice %d and hidden %d must be multiples of 64 and 128",
+                        name, I / tp, H);
+    }
+    return check_weights(w, H, I, true, name);
+}
+
+int64_t moe_workspace_bytes(int T, int K, int E_local, int H, int I, int tile_m, int tp,
+                            moe_workspace_layout* layout) {
+    using namespace moe;
+    const char* name = "moe_workspace_bytes";
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E_local < 1 || E_local > MOE_MAX_EXPERTS || tp < 1) {
+        fail(MOE_EINVAL, "%s: T=%d K=%d E_local=%d tp=%d out of range", name, T, K, E_local, tp);
+        return -1;
+    }
+    if (tile_m < 16 || tile_m > 256 || tile_m % 16 || H < 16 || H % 16 || I % tp || (I / tp) < 16 ||
+        (I / tp) % 16) {
+        fail(MOE_EUNSUPPORTED, "%s: tile_m=%d H=%d I=%d tp=%d not supported", name, tile_m, H, I, tp);
+        return -1;
+    }
+    const moe_meta_layout L = meta_layout(T, K, E_local, tile_m);
+    const int64_t R = (int64_t)T * K, Is = I / tp;
+    moe_workspace_layout w;
+    int64_t off = 0;
+    w.meta = off;         off += align256(4 * L.total_ints);
+    w.topk_ids = off;     off += align256(4 * R);
+    w.topk_weights = off; off += align256(4 * R);
+    w.a_codes = off;      off += align256((int64_t)T * (H / 2));
+    w.a_sf = off;         off += align256((int64_t)T * (H / 16));
+    w.inter_codes = off;  off += align256(L.rows_max * (Is / 2));
+    w.inter_sf = off;     off += align256(L.rows_max * (Is / 16));
+    w.rows = off;         off += align256((int64_t)tp * L.rows_max * H * 2);
+    w.total_bytes = off;
+    if (layout) *layout = w;
+    return off;
 }
 
 }  // extern "C"

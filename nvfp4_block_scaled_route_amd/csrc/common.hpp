@@ -21,12 +21,18 @@ int check_launch(const char* what);                // MOE_ELAUNCH on a pending l
 int moe_route_check(int T, int E, int K, int tile_m, int local_expert_offset, int local_num_experts,
                     int64_t logits_row_stride, const float* logits, const int32_t* topk_ids,
                     const float* topk_weights, const int32_t* meta, const char* name);
+// the converted-weight descriptor's pointers, alignment and strides for H x I
+// experts (g1_scale_c checked when need_scale_c): shared by the expert calls
+// and moe_validate_weights
+int check_weights(const moe_nvfp4_weights* w, int H, int I, bool need_scale_c, const char* name);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m);
 // int32 words between the sync counters of consecutive 16-row tiles in the
 // metadata (1 KB): tiles' counters on distinct cache lines and memory channels,
 // so that the polls of many workgroups do not all queue on one channel.
 constexpr int kSubSyncStride = 256;
+// converted weight layout: code and scale bytes per row pair and k-tile
+constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;
 
 // ------------------------------------------------------------------ codecs
 // e2m1: nearest value of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,

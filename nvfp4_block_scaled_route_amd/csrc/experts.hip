@@ -583,26 +583,13 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int3
         return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: tile_m=%d must be a multiple of 16 in [16, 256]", tile_m);
     if (!w || !meta) return fail(MOE_EINVAL, "moe_experts_fwd: NULL weights or meta");
     if (T == 0) return MOE_OK;
-    if (!a_codes || !a_sf || !inter_codes || !inter_sf || !rows || !w->w13 || !w->w13_sf ||
-        !w->w2 || !w->w2_sf || !w->g1_alphas || !w->g1_scale_c || !w->g2_alphas)
+    if (!a_codes || !a_sf || !inter_codes || !inter_sf || !rows)
         return fail(MOE_EINVAL, "moe_experts_fwd: NULL pointer");
-    const void* ptrs[] = {a_codes, a_sf, meta, inter_codes, inter_sf, rows, w->w13, w->w13_sf,
-                          w->w2, w->w2_sf, w->g1_alphas, w->g1_scale_c, w->g2_alphas};
+    const void* ptrs[] = {a_codes, a_sf, meta, inter_codes, inter_sf, rows};
     for (const void* ptr : ptrs)
         if (!aligned16(ptr)) return fail(MOE_EINVAL, "moe_experts_fwd: pointers must be 16-byte aligned");
+    if (int rc = check_weights(w, H, I, true, "moe_experts_fwd")) return rc;
     const int64_t kt1 = H / 64, kt2 = I / 64;
-    if (w->w13_pair_stride_bytes < kt1 * kSlotBytes || w->w13_sf_pair_stride_bytes < kt1 * kSlotSfBytes ||
-        w->w2_pair_stride_bytes < kt2 * kSlotBytes || w->w2_sf_pair_stride_bytes < kt2 * kSlotSfBytes ||
-        w->w13_pair_stride_bytes % 16 || w->w13_sf_pair_stride_bytes % 16 ||
-        w->w2_pair_stride_bytes % 16 || w->w2_sf_pair_stride_bytes % 16)
-        return fail(MOE_EINVAL, "moe_experts_fwd: pair strides too small or not multiples of 16");
-    if (w->w13_expert_stride_bytes < (int64_t)(I / 16) * w->w13_pair_stride_bytes ||
-        w->w13_sf_expert_stride_bytes < (int64_t)(I / 16) * w->w13_sf_pair_stride_bytes ||
-        w->w2_expert_stride_bytes < (int64_t)(H / 32) * w->w2_pair_stride_bytes ||
-        w->w2_sf_expert_stride_bytes < (int64_t)(H / 32) * w->w2_sf_pair_stride_bytes ||
-        w->w13_expert_stride_bytes % 16 || w->w13_sf_expert_stride_bytes % 16 ||
-        w->w2_expert_stride_bytes % 16 || w->w2_sf_expert_stride_bytes % 16)
-        return fail(MOE_EINVAL, "moe_experts_fwd: expert strides too small or not multiples of 16");
     if (rows_stride < H || rows_stride % 8)
         return fail(MOE_EINVAL, "moe_experts_fwd: rows_stride must be >= H and a multiple of 8");
     ExpArgs args;

@@ -21,8 +21,6 @@ struct ExpArgs {
     int32_t* status;     // meta's sync_status
 };
 
-constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;   // converted layout: per pair and k-tile
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediates (gfx9 encoding): at most n vector-memory loads in
@@ -57,17 +55,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // Direct-to-LDS load: lane l's 16 bytes at base + voff + soff land at LDS
 // address lds + 16 l. The compiler does not see it: a wait for it is the
-// caller's (vmcnt, which it shares with the loads issued around it).
+// caller's (vmcnt, which it shares with the loads issued around it). The LDS
+// address goes to the instruction in M0 as an input operand, so the compiler
+// writes M0 itself right before it and knows the register is taken (the
+// instruction only reads M0). Inline assembly rather than the compiler's
+// direct-to-LDS builtin: the compiler takes that builtin for an LDS write of
+// unknown extent and makes every later LDS read wait for it, which would
+// serialize the double-buffered stages of the tiled kernels.
 __device__ __forceinline__ void lds_copy16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
 }
 
 // The same load, agent-coherent (sc1): it returns what another XCD wrote with
 // agent-coherent stores, not a line its own L2 may still hold.
 __device__ __forceinline__ void lds_copy16_sc1(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc1 lds"
-                 :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen sc1 lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
 }
 
 // The unit's 16-row tile: expert (-1: no unit) and the lane's row token.

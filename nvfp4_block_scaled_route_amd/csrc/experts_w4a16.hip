@@ -461,22 +461,11 @@ extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, co
     if (rc) return rc;
     if (!w || !meta) return fail(MOE_EINVAL, "%s: NULL weights or meta", name);
     if (T == 0) return MOE_OK;
-    if (!x || !inter || !rows || !w->w13 || !w->w13_sf || !w->w2 || !w->w2_sf || !w->g1_alphas || !w->g2_alphas)
-        return fail(MOE_EINVAL, "%s: NULL pointer", name);
-    const void* ptrs[] = {x, meta, inter, rows, w->w13, w->w13_sf, w->w2, w->w2_sf, w->g1_alphas, w->g2_alphas};
+    if (!x || !inter || !rows) return fail(MOE_EINVAL, "%s: NULL pointer", name);
+    const void* ptrs[] = {x, meta, inter, rows};
     for (const void* ptr : ptrs)
         if (!aligned16(ptr)) return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
-    const int64_t kt1 = H / 64, kt2 = I / 64;
-    if (w->w13_pair_stride_bytes < kt1 * kSlotBytes || w->w13_sf_pair_stride_bytes < kt1 * kSlotSfBytes ||
-        w->w2_pair_stride_bytes < kt2 * kSlotBytes || w->w2_sf_pair_stride_bytes < kt2 * kSlotSfBytes ||
-        w->w13_expert_stride_bytes < (int64_t)(I / 16) * w->w13_pair_stride_bytes ||
-        w->w13_sf_expert_stride_bytes < (int64_t)(I / 16) * w->w13_sf_pair_stride_bytes ||
-        w->w2_expert_stride_bytes < (int64_t)(H / 32) * w->w2_pair_stride_bytes ||
-        w->w2_sf_expert_stride_bytes < (int64_t)(H / 32) * w->w2_sf_pair_stride_bytes ||
-        (w->w13_pair_stride_bytes | w->w13_sf_pair_stride_bytes | w->w2_pair_stride_bytes |
-         w->w2_sf_pair_stride_bytes | w->w13_expert_stride_bytes | w->w13_sf_expert_stride_bytes |
-         w->w2_expert_stride_bytes | w->w2_sf_expert_stride_bytes) % 16)
-        return fail(MOE_EINVAL, "%s: weight strides too small or not multiples of 16", name);
+    if (int rc = check_weights(w, H, I, false, name)) return rc;
     return w16_launch<false>(name, x, x_row_stride, meta, *w, T, K, E_local, H, I, tile_m, inter, rows,
                              rows_stride, (hipStream_t)stream);
 }

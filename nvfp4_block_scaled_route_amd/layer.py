@@ -70,23 +70,39 @@ class LayerShape:
 
 
 class Buffers:
-    """Every device buffer one layer call writes, sized once (nothing is
-    allocated per call, so the calls can be captured in a HIP graph)."""
+    """Every device buffer one layer call writes, sized once by moe_workspace_bytes
+    and carved from one allocation (nothing is allocated per call, so the calls
+    can be captured in a HIP graph)."""
 
     def __init__(self, shape: LayerShape, device="cuda"):
         s = self.shape = shape
         L = self.layout = N.moe_meta_layout_get(s.T, s.K, s.E, s.tile_m)
-        u8, i32, i16 = torch.uint8, torch.int32, torch.int16
-        self.a_codes = torch.empty((s.T, s.H // 2), dtype=u8, device=device)
-        self.a_sf = torch.empty((s.T, s.H // 16), dtype=u8, device=device)
-        self.ids = torch.empty((s.T, s.K), dtype=i32, device=device)
-        self.weights = torch.empty((s.T, s.K), dtype=torch.float32, device=device)
-        self.meta = torch.full((L.total_ints,), -1, dtype=i32, device=device)
-        I_slice = s.I // s.tp
-        self.inter_codes = torch.empty((max(L.rows_max, 1), I_slice // 2), dtype=u8, device=device)
-        self.inter_sf = torch.empty((max(L.rows_max, 1), I_slice // 16), dtype=u8, device=device)
-        self.rows = torch.empty((s.tp, max(L.rows_max, 1), s.H), dtype=i16, device=device)
-        self.out = torch.empty((s.T, s.H), dtype=i16, device=device)
+        W = self.ws_layout = N.moe_workspace_bytes(s.T, s.K, s.E, s.H, s.I, s.tile_m, s.tp)
+        self.workspace = torch.empty((W.total_bytes,), dtype=torch.uint8, device=device)
+        rm, I_slice = L.rows_max, s.I // s.tp
+
+        def part(off, dtype, dims):
+            n = 1
+            for d in dims:
+                n *= d
+            nbytes = n * torch.empty((), dtype=dtype).element_size()
+            return self.workspace[off:off + nbytes].view(dtype).view(dims)
+
+        self.meta = part(W.meta, torch.int32, (L.total_ints,))
+        self.meta.fill_(-1)
+        self.ids = part(W.topk_ids, torch.int32, (s.T, s.K))
+        self.weights = part(W.topk_weights, torch.float32, (s.T, s.K))
+        self.a_codes = part(W.a_codes, torch.uint8, (s.T, s.H // 2))
+        self.a_sf = part(W.a_sf, torch.uint8, (s.T, s.H // 16))
+        if rm > 0:
+            self.inter_codes = part(W.inter_codes, torch.uint8, (rm, I_slice // 2))
+            self.inter_sf = part(W.inter_sf, torch.uint8, (rm, I_slice // 16))
+            self.rows = part(W.rows, torch.int16, (s.tp, rm, s.H))
+        else:                       # no routed rows: placeholders the calls never touch
+            self.inter_codes = torch.empty((1, I_slice // 2), dtype=torch.uint8, device=device)
+            self.inter_sf = torch.empty((1, I_slice // 16), dtype=torch.uint8, device=device)
+            self.rows = torch.empty((s.tp, 1, s.H), dtype=torch.int16, device=device)
+        self.out = torch.empty((s.T, s.H), dtype=torch.int16, device=device)
 
     def field(self, name: str, length: int) -> torch.Tensor:
         off = getattr(self.layout, name)
@@ -100,13 +116,25 @@ class Buffers:
     def perm2tok(self) -> torch.Tensor:
         return self.field("perm2tok", self.layout.rows_max)
 
+    def check_sync(self) -> None:
+        """Raise if an expert step's bounded wait gave up (meta[sync_status] != 0:
+        its rows are not valid) or left a tile counter non-zero. Reads the
+        metadata back, so the caller synchronizes the stream first."""
+        L = self.layout
+        status = int(self.meta[L.sync_status].item())
+        counters = self.meta[L.sub_sync:L.sub_sync + 256 * L.subs_max].view(-1, 256)[:, :2]
+        if status != 0 or bool(counters.any().item()):
+            raise N.MoeError(f"expert step synchronization failed: sync_status={status}, "
+                             f"non-zero tile counters={int((counters != 0).sum().item())}; the rows are not valid")
+
 
 def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, weights: N.Weights,
               norm_weight, gain_center: float, eps: float, weight_before_norm: bool,
               route_scale: float = 1.0, slices: list[N.Weights] | None = None, stream=None,
-              fused_route_quant: bool = True) -> None:
+              fused_route_quant: bool = True, check: bool = False) -> None:
     """route -> quant -> experts (per TP slice) -> finalize, all enqueued on one stream
-    (route and quant in one launch unless fused_route_quant is False)."""
+    (route and quant in one launch unless fused_route_quant is False). With check,
+    waits for the stream and raises if an expert step's wait gave up."""
     s = bufs.shape
     if fused_route_quant:
         N.moe_route_quant(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
@@ -123,3 +151,9 @@ def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, we
                           s.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
     N.moe_finalize(bufs.rows, len(parts), bufs.rows.stride(0), bufs.exp2perm, bufs.weights,
                    norm_weight, gain_center, eps, weight_before_norm, s.T, s.K, s.H, bufs.out, stream)
+    if check:
+        if stream is None:
+            torch.cuda.current_stream().synchronize()
+        else:
+            stream.synchronize()
+        bufs.check_sync()

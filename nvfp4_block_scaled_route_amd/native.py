@@ -20,7 +20,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3
 EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout_get",
            "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
            "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant", "moe_router_logits",
-           "moe_router_route", "moe_experts_fwd_w4a16", "moe_experts_fwd_bf16")
+           "moe_router_route", "moe_experts_fwd_w4a16", "moe_experts_fwd_bf16",
+           "moe_validate_weights", "moe_workspace_bytes")
 
 
 class MoeMetaLayout(ctypes.Structure):
@@ -39,6 +40,12 @@ class MoeNvfp4Weights(ctypes.Structure):
                    "w2_sf_expert_stride_bytes", "w2_sf_pair_stride_bytes")] + \
                [("g1_alphas", ctypes.c_void_p), ("g1_scale_c", ctypes.c_void_p),
                 ("g2_alphas", ctypes.c_void_p)]
+
+
+class MoeWorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "meta", "topk_ids", "topk_weights", "a_codes", "a_sf", "inter_codes", "inter_sf", "rows",
+        "total_bytes")]
 
 
 class MoeError(RuntimeError):
@@ -77,6 +84,8 @@ def lib() -> ctypes.CDLL:
         "moe_experts_fwd": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
                                   i32, i32, i32, vp, vp, vp, i64, vp]),
         "moe_finalize": (i32, [vp, i64, i32, i64, vp, vp, vp, f32, f32, i32, i32, i32, i32, vp, vp]),
+        "moe_validate_weights": (i32, [ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32, i32]),
+        "moe_workspace_bytes": (i64, [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(MoeWorkspaceLayout)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -111,6 +120,15 @@ def _stream(stream) -> int | None:
 # ------------------------------------------------------------------ sizing
 def moe_rows_max(T: int, K: int, E_local: int, tile_m: int) -> int:
     return int(lib().moe_rows_max(T, K, E_local, tile_m))
+
+
+def moe_workspace_bytes(T: int, K: int, E_local: int, H: int, I: int, tile_m: int,
+                        tp: int = 1) -> MoeWorkspaceLayout:
+    out = MoeWorkspaceLayout()
+    n = lib().moe_workspace_bytes(T, K, E_local, H, I, tile_m, tp, ctypes.byref(out))
+    if n < 0:
+        _check(MOE_EINVAL, "moe_workspace_bytes")
+    return out
 
 
 def moe_meta_layout_get(T: int, K: int, E_local: int, tile_m: int) -> MoeMetaLayout:
@@ -211,6 +229,12 @@ class Weights:
             self.w13_sf_pair_stride, self.w2_expert_stride, self.w2_pair_stride,
             self.w2_sf_expert_stride, self.w2_sf_pair_stride,
             _ptr(self.g1_alphas), _ptr(self.g1_scale_c), _ptr(self.g2_alphas))
+
+
+def moe_validate_weights(weights: Weights, E_local: int, H: int, I: int, tp: int = 1) -> None:
+    """Host-only check of the descriptor (and of its cut into tp slices); raises MoeError."""
+    ws = weights.struct()
+    _check(lib().moe_validate_weights(ctypes.byref(ws), E_local, H, I, tp), "moe_validate_weights")
 
 
 def moe_experts_fwd(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, tile_m,

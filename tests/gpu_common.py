@@ -79,3 +79,97 @@ def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | Non
         inter_codes=host(bufs.inter_codes), inter_sf=host(bufs.inter_sf),
         rows=host(bufs.rows), out=host(bufs.out))
     return res
+
+
+# ------------------------------------------------------------------ requantized intermediate
+U32 = 2.0 ** -24      # fp32 unit roundoff
+
+
+def abs_gemm1(a_codes, a_sf, tokens, experts, w13_codes, w13_sf) -> np.ndarray:
+    """sum_h |a[t, h] w13[e, n, h]| per route and column: the oracle's exact GEMM1
+    on the magnitudes (sign bits cleared), the scale of an accumulation's error."""
+    from oracle import experts as ex
+    return ex.gemm1(a_codes & 0x77, a_sf & 0x7F, tokens, experts, w13_codes & 0x77, w13_sf & 0x7F)
+
+
+def h_error_bound(acc1, abs_acc1, experts, g1_alphas, g1_scale_c, h, K) -> np.ndarray:
+    """A bound on |h_kernel - h_oracle| per element of the gated activation.
+
+    The kernels accumulate exact f16 products in fp32 through a chain of at most
+    K/16 matrix instructions, each adding at most 32 terms, so the accumulator's
+    error is at most (K/16 + 32) u sum|a w| to first order (u = 2^-24, any
+    summation order of that depth). It propagates into h = silu(g) u through
+    |d h / d acc_gate| = |ga silu'(g) u| and |d h / d acc_up| = |uc silu(g)|,
+    silu'(g) = s (1 + g (1 - s)) with s the logistic of g, taken at g (the
+    accumulator's relative error is far below what moves it); the scalar
+    products, the exponential (about (|g| + 4) u relative for exp2 of a rounded
+    argument), the reciprocal or division and the final product add at most
+    (|g| + 12) u |h|. Doubled for safety."""
+    I = h.shape[1]
+    ga = np.asarray(g1_alphas, np.float64)[experts][:, None]
+    uc = np.asarray(g1_scale_c, np.float64)[experts][:, None]
+    g = acc1[:, :I] * ga
+    up = acc1[:, I:] * uc
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
+    depth = K / 16 + 32
+    eps_g = depth * U32 * abs_acc1[:, :I] * np.abs(ga)
+    eps_u = depth * U32 * abs_acc1[:, I:] * np.abs(uc)
+    hv = np.abs(h.astype(np.float64))
+    return 2.0 * (dsilu * np.abs(up) * eps_g + np.abs(silu) * eps_u + (np.abs(g) + 12.0) * U32 * hv) + 1e-38
+
+
+def check_requant(got_codes, got_sf, h, ref_codes, ref_sf, eb_of, name, max_frac=1e-3):
+    """The kernel's requantized intermediate (codes [R, I/2], scales [R, I/16])
+    against the oracle's, where several results are correct: every differing
+    scale byte is the adjacent e4m3 code, with the oracle's amax / 6 within
+    (the block's error bound) / 6 of the midpoint between the two; every code
+    that differs, after quantizing the oracle's h with the kernel's scale, is
+    the adjacent e2m1 value of the same sign (or a zero of the other sign),
+    with the oracle's h within its error bound of the boundary between the two.
+    At most max_frac of the codes and of the scales may differ. eb_of(routes)
+    gives the error bound [len(routes), I] of those routes' h (h_error_bound),
+    asked for only where something differs."""
+    from oracle import formats as F
+    R, nb = got_sf.shape
+    sf_diff = got_sf != ref_sf
+    code_diff = got_codes != ref_codes
+    say(f"{name}: requant scale diff {sf_diff.mean():.2e}, code byte diff {code_diff.mean():.2e}")
+    assert sf_diff.mean() <= max_frac and code_diff.mean() <= max_frac, name
+    bad = np.nonzero(sf_diff.any(axis=1) | code_diff.any(axis=1))[0]
+    if bad.size == 0:
+        return
+    eb = eb_of(bad)
+    hb = h[bad].astype(np.float32).reshape(bad.size, nb, 16)
+    ebb = eb.reshape(bad.size, nb, 16)
+    gsf, rsf = got_sf[bad], ref_sf[bad]
+    # scales: adjacent codes, amax / 6 at their midpoint within the bound
+    rr, bb = np.nonzero(gsf != rsf)
+    for r, b in zip(rr, bb):
+        g, o = int(gsf[r, b]), int(rsf[r, b])
+        assert abs(g - o) == 1 and max(g, o) < 0x7F, (name, bad[r], b, g, o)
+        mid = (F.E4M3[g] + F.E4M3[o]) / 2.0
+        amax = float(np.max(np.abs(hb[r, b]).astype(np.float64)))
+        assert abs(amax / 6.0 - mid) <= float(ebb[r, b].max()) / 6.0 + 2 * U32 * amax, (name, bad[r], b)
+    # codes, against the oracle's h quantized with the kernel's scale
+    gn = F.unpack_nibbles(got_codes[bad]).astype(np.int64)
+    d = F.decode_e4m3(gsf).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        recip = np.where(d == 0, np.float32(0), (np.float32(1) / d).astype(np.float32)).astype(np.float32)
+    want = F.encode_e2m1((hb * recip[..., None]).astype(np.float32)).reshape(bad.size, -1).astype(np.int64)
+    want = np.where(np.repeat(d == 0, 16, axis=1), 0, want)
+    rr, ii = np.nonzero(gn != want)
+    hv = h[bad].astype(np.float64)
+    for r, i in zip(rr, ii):
+        g, o = int(gn[r, i]), int(want[r, i])
+        dd = float(d[r, i // 16])
+        mg, mo = g & 7, o & 7
+        if mg == 0 and mo == 0:             # a zero of the other sign: h within the bound of 0
+            assert abs(hv[r, i]) <= eb[r, i], (name, bad[r], i)
+            continue
+        assert (g >> 3) == (o >> 3) or min(mg, mo) == 0, (name, bad[r], i, g, o)
+        assert abs(mg - mo) == 1, (name, bad[r], i, g, o)
+        mid = (abs(F.E2M1[g]) + abs(F.E2M1[o])) / 2.0 * dd * np.sign(hv[r, i])
+        assert abs(hv[r, i] - mid) <= eb[r, i] + 4 * U32 * abs(hv[r, i]), (name, bad[r], i, hv[r, i], mid)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
@@ -133,3 +133,90 @@ def test_zero_tokens_is_a_no_op_without_device():
     L = N.lib()
     assert L.nvfp4_quant(None, 64, None, 0, 64, None, None, None) == N.MOE_OK
     assert L.moe_finalize(None, 64, 1, 0, None, None, None, ctypes.c_float(1.0), ctypes.c_float(1e-6), 1, 0, 2, 64, None, None) == N.MOE_OK
+
+
+def _weights_struct(H, I, E, base=1 << 20, **override):
+    """A descriptor of full-width converted weights at fake, aligned addresses
+    (never dereferenced: moe_validate_weights reads no device memory)."""
+    w = N.MoeNvfp4Weights()
+    w.w13, w.w13_sf, w.w2, w.w2_sf = base, 2 * base, 3 * base, 4 * base
+    w.g1_alphas, w.g1_scale_c, w.g2_alphas = 5 * base, 6 * base, 7 * base
+    w.w13_pair_stride_bytes = (H // 64) * 1024
+    w.w13_sf_pair_stride_bytes = (H // 64) * 128
+    w.w13_expert_stride_bytes = (I // 16) * w.w13_pair_stride_bytes
+    w.w13_sf_expert_stride_bytes = (I // 16) * w.w13_sf_pair_stride_bytes
+    w.w2_pair_stride_bytes = (I // 64) * 1024
+    w.w2_sf_pair_stride_bytes = (I // 64) * 128
+    w.w2_expert_stride_bytes = (H // 32) * w.w2_pair_stride_bytes
+    w.w2_sf_expert_stride_bytes = (H // 32) * w.w2_sf_pair_stride_bytes
+    for k, v in override.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_validate_weights_accepts_the_workloads_and_their_tp_cuts():
+    L = N.lib()
+    for (H, I, E, tp) in [(256, 128, 8, 1), (2048, 768, 64, 1), (4096, 1536, 128, 1),
+                          (4096, 2048, 128, 8), (4096, 2048, 128, 2), (1024, 512, 4, 4)]:
+        w = _weights_struct(H, I, E)
+        assert L.moe_validate_weights(ctypes.byref(w), E, H, I, tp) == N.MOE_OK, L.moe_last_error()
+
+
+def test_validate_weights_refusals():
+    """The expert_tp page's "unsupported": tp must divide I, the slice I/tp be a
+    multiple of 64 and H of 128; and the descriptor's pointers and strides."""
+    L = N.lib()
+    H, I, E = 4096, 2048, 128
+    ok = _weights_struct(H, I, E)
+    cases = [
+        ((ok, E, H, I, 3), N.MOE_EUNSUPPORTED, b"split"),           # 2048 % 3
+        ((ok, E, H, I, 64), N.MOE_EUNSUPPORTED, b"multiples"),      # slice 32
+        ((_weights_struct(64 * 23, I, E), E, 64 * 23, I, 8), N.MOE_EUNSUPPORTED, b"multiples"),     # H % 128
+        ((ok, E, H, I, 0), N.MOE_EINVAL, b"tp"),
+        ((ok, 0, H, I, 1), N.MOE_EINVAL, b"E_local"),
+        ((ok, E, H + 32, I, 1), N.MOE_EUNSUPPORTED, b"multiples of 64"),
+        ((_weights_struct(H, I, E, w2=0), E, H, I, 1), N.MOE_EINVAL, b"NULL"),
+        ((_weights_struct(H, I, E, g1_scale_c=8), E, H, I, 1), N.MOE_EINVAL, b"aligned"),
+        ((_weights_struct(H, I, E, w13_pair_stride_bytes=1024), E, H, I, 1), N.MOE_EINVAL, b"pair strides"),
+        ((_weights_struct(H, I, E, w2_sf_pair_stride_bytes=(I // 64) * 128 + 8), E, H, I, 1), N.MOE_EINVAL,
+         b"pair strides"),
+        ((_weights_struct(H, I, E, w2_expert_stride_bytes=1024), E, H, I, 1), N.MOE_EINVAL, b"expert strides"),
+    ]
+    for (w, e, h, i, tp), want, msg in cases:
+        assert L.moe_validate_weights(ctypes.byref(w), e, h, i, tp) == want, (tp, L.moe_last_error())
+        assert msg in L.moe_last_error(), L.moe_last_error()
+    assert L.moe_validate_weights(None, E, H, I, 1) == N.MOE_EINVAL
+
+
+@pytest.mark.parametrize("T,K,E,H,I,m,tp", [(4, 2, 8, 256, 128, 16, 1), (8, 8, 64, 2048, 768, 16, 1),
+                                            (64, 8, 128, 4096, 1536, 16, 1),
+                                            (4096, 8, 128, 4096, 1536, 128, 1),
+                                            (32, 8, 128, 4096, 2048, 16, 8), (0, 8, 8, 64, 64, 16, 1)])
+def test_workspace_layout(T, K, E, H, I, m, tp):
+    """Every buffer of one layer call at a 256-byte aligned offset of one
+    allocation, none overlapping, each of the size its call needs."""
+    lay = N.moe_workspace_bytes(T, K, E, H, I, m, tp)
+    meta = N.moe_meta_layout_get(T, K, E, m)
+    rm = oracle_rows_max(T, K, E, m)
+    Is = I // tp
+    need = [("meta", 4 * meta.total_ints), ("topk_ids", 4 * T * K), ("topk_weights", 4 * T * K),
+            ("a_codes", T * H // 2), ("a_sf", T * H // 16), ("inter_codes", rm * Is // 2),
+            ("inter_sf", rm * Is // 16), ("rows", tp * rm * H * 2)]
+    spans = []
+    for name, nbytes in need:
+        off = getattr(lay, name)
+        assert off % 256 == 0, name
+        spans.append((off, off + nbytes))
+    spans.sort()
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert spans[-1][1] <= lay.total_bytes < spans[-1][1] + 256 * len(need)
+    assert N.lib().moe_workspace_bytes(T, K, E, H, I, m, tp, None) == lay.total_bytes
+
+
+def test_workspace_refusals():
+    L = N.lib()
+    assert L.moe_workspace_bytes(4, 0, 8, 256, 128, 16, 1, None) == -1
+    assert L.moe_workspace_bytes(4, 2, 8, 256, 128, 24, 1, None) == -1
+    assert L.moe_workspace_bytes(4, 2, 8, 256, 128, 16, 3, None) == -1       # 128 % 3
+    assert L.moe_last_error()

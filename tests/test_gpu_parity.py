@@ -21,7 +21,8 @@ from oracle.permute import permute as o_permute
 from oracle.quant import quantize_nvfp4
 from oracle.routing import route as o_route
 
-from .gpu_common import DEV, dev, host, run_layer, say, sync_counters, upload_weights
+from .gpu_common import (DEV, abs_gemm1, check_requant, dev, h_error_bound, host, run_layer, say,
+                         sync_counters, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -305,23 +306,46 @@ def _check_sync_words(res):
     assert not np.any(res["sub_sync"])
 
 
-def _compare_layer(res, ref, name):
+def _compare_requant(res, ref, inp, rows_got, tokens, experts, name, a_codes=None, a_sf=None):
+    """The kernel's intermediate at permuted rows rows_got against the oracle's
+    for the same routes in the same order (ref: h, acc1, h_codes, h_sf), by the
+    one-grid-step rule at rounding boundaries (the error bound is computed for
+    the routes that differ only)."""
+    if a_codes is None:
+        a_codes, a_sf = quantize_input(inp)
+
+    def eb_of(sel):
+        abs_acc1 = abs_gemm1(a_codes, a_sf, tokens[sel], experts[sel], inp.w13_codes, inp.w13_sf)
+        return h_error_bound(ref["acc1"][sel], abs_acc1, experts[sel], inp.g1_alphas, inp.g1_scale_c,
+                             ref["h"][sel], inp.wl.H)
+
+    check_requant(res["inter_codes"][rows_got], res["inter_sf"][rows_got], ref["h"], ref["h_codes"],
+                  ref["h_sf"], eb_of, name)
+
+
+def _compare_layer(res, ref, name, inp, tile_m=None):
     _check_sync_words(res)
     p = ref["rows_idx"]
+    m = inp.wl.tile_m if tile_m is None else tile_m
     # routing and metadata: bit-exact
     assert np.array_equal(res["ids"], ref["ids"])
     assert np.array_equal(res["weights"].view(np.uint32), ref["weights"].view(np.uint32))
     assert np.array_equal(res["exp2perm"], ref["meta"]["exp2perm"])
     assert np.array_equal(res["perm2tok"], ref["meta"]["perm2tok"])
     assert np.array_equal(res["a_codes"], ref["a_codes"]) and np.array_equal(res["a_sf"], ref["a_sf"])
-    # intermediate: agree except at rounding boundaries
-    sf_diff = np.mean(res["inter_sf"][p] != ref["h_sf"])
-    code_diff = np.mean(F.unpack_nibbles(res["inter_codes"][p]) != F.unpack_nibbles(ref["h_codes"]))
-    rows_rel = rel_l2(F.bf16_to_f64(res["rows"][0][p]), F.bf16_to_f64(ref["rows"][p]))
+    # intermediate: equal except one grid step at fp32 rounding boundaries
+    tokens = ref["meta"]["perm2tok"][p]
+    experts = ref["meta"]["tile_expert"][p // m]
+    _compare_requant(res, ref, inp, p, tokens, experts, name, ref["a_codes"], ref["a_sf"])
+    got_rows, want_rows = F.bf16_to_f64(res["rows"][0][p]), F.bf16_to_f64(ref["rows"][p])
+    rows_rel = rel_l2(got_rows, want_rows)
     out_rel = rel_l2(F.bf16_to_f64(res["out"]), F.bf16_to_f64(ref["out"]))
-    say(f"{name}: inter scale diff {sf_diff:.2e}, code diff {code_diff:.2e}, "
-        f"rows rel-L2 {rows_rel:.2e}, out rel-L2 {out_rel:.2e}")
-    assert sf_diff < 1e-2 and code_diff < 2e-2
+    # every block of up to 128 permuted rows (a tiled kernel's row block, a few
+    # streaming tiles) on its own, so that one wrong block cannot hide in the total
+    blk = p // 128
+    worst = max(rel_l2(got_rows[blk == b], want_rows[blk == b]) for b in np.unique(blk))
+    say(f"{name}: rows rel-L2 {rows_rel:.2e} (worst 128-row block {worst:.2e}), out rel-L2 {out_rel:.2e}")
+    assert worst < TOL
     assert rows_rel < TOL
     assert out_rel < TOL
     return out_rel
@@ -332,7 +356,7 @@ def test_layer_parity_full_oracle(inputs, name):
     inp = inputs(name)
     res = run_layer(inp)
     ref = o_layer(inp)
-    _compare_layer(res, ref, name)
+    _compare_layer(res, ref, name, inp)
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(256, 512, 256, 4, 2, 128), (200, 256, 512, 6, 3, 256),
@@ -350,7 +374,7 @@ def test_layer_parity_tiled_path(T, H, I, E, K, m):
     assert T * K >= 32 * E                      # the tiled path's dispatch condition
     res = run_layer(inp)
     ref = o_layer(inp)
-    _compare_layer(res, ref, wl.name)
+    _compare_layer(res, ref, wl.name, inp)
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 16),
@@ -372,7 +396,7 @@ def test_layer_parity_streaming_kernel_choices(T, H, I, E, K, m):
     inp = W.make_inputs(wl, a2_gscale=a2)
     res = run_layer(inp)
     ref = o_layer(inp)
-    _compare_layer(res, ref, wl.name)
+    _compare_layer(res, ref, wl.name, inp)
 
 
 @pytest.mark.parametrize("tile_m", [32, 64, 256])
@@ -380,7 +404,7 @@ def test_layer_parity_other_tiles(inputs, tile_m):
     inp = inputs("decode_b8")
     res = run_layer(inp, tile_m=tile_m)
     ref = o_layer(inp, tile_m=tile_m)
-    _compare_layer(res, ref, f"decode_b8 m={tile_m}")
+    _compare_layer(res, ref, f"decode_b8 m={tile_m}", inp, tile_m)
 
 
 def test_layer_parity_padding_tokens(inputs):
@@ -388,7 +412,7 @@ def test_layer_parity_padding_tokens(inputs):
     pad = np.array([False, True, False, False])
     res = run_layer(inp, is_padding=pad)
     ref = o_layer(inp, is_padding=pad)
-    _compare_layer(res, ref, "tiny padded")
+    _compare_layer(res, ref, "tiny padded", inp)
     assert np.all(res["ids"][1] == -1) and np.all(F.bf16_to_f64(res["out"][1]) == 0)
 
 
@@ -397,12 +421,14 @@ def test_layer_parity_decode_b64_zipf(inputs):
     inp = inputs("decode_b64_zipf")
     res = run_layer(inp)
     ref = o_layer(inp)
-    _compare_layer(res, ref, "decode_b64_zipf")
+    _compare_layer(res, ref, "decode_b64_zipf", inp)
     counts = res["counts"]
     say(f"decode_b64_zipf: {int((counts > 0).sum())} experts touched, hottest {int(counts.max())} routes")
 
 
 def _compare_sampled(res, inp, tokens, name):
+    """The HIP layer's rows, intermediate and outputs for the given tokens against
+    the oracle's sampled evaluation of the same tokens."""
     ref = layer_sampled(inp, tokens)
     e2p = res["exp2perm"][tokens]
     served = e2p >= 0
@@ -413,24 +439,23 @@ def _compare_sampled(res, inp, tokens, name):
     out_rel = rel_l2(F.bf16_to_f64(res["out"][tokens]), F.bf16_to_f64(ref["out"]))
     say(f"{name}: sampled {len(tokens)} tokens, rows rel-L2 {rows_rel:.2e}, out rel-L2 {out_rel:.2e}")
     assert rows_rel < TOL and out_rel < TOL
+    tt, kk = np.nonzero(served)
+    _compare_requant(res, ref, inp, e2p[tt, kk], np.asarray(tokens)[tt], ref["ids"][tt, kk], name)
     return ref
 
 
 @pytest.mark.slow
-def test_layer_parity_prefill_sampled(inputs):
+@pytest.mark.timeout(900)
+def test_layer_parity_prefill_all_tokens(inputs):
+    """prefill_t4096 against the oracle's whole layer over all 4096 tokens (32768
+    routes): routing, metadata and the quantizer bit-exact, the intermediate by
+    the one-step rule, the rows of every routed 128-row block and the outputs
+    within rel-L2 1e-2."""
     inp = inputs("prefill_t4096")
     res = run_layer(inp)
-    # routing, metadata and the quantizer over all tokens: bit-exact
-    a_codes, a_sf = quantize_input(inp)
-    assert np.array_equal(res["a_codes"], a_codes) and np.array_equal(res["a_sf"], a_sf)
-    oids, ow = o_route(inp.logits, inp.expert_bias, inp.wl.K)
-    assert np.array_equal(res["ids"], oids)
-    om = o_permute(oids, 0, inp.wl.E, inp.wl.tile_m)
-    assert np.array_equal(res["exp2perm"], om["exp2perm"])
-    assert np.array_equal(res["perm2tok"], om["perm2tok"])
-    tokens = np.random.default_rng(0).choice(inp.wl.T, 12, replace=False)
-    tokens = np.concatenate([tokens, [0, inp.wl.T - 1]])
-    _compare_sampled(res, inp, tokens, "prefill_t4096")
+    say("prefill_t4096: oracle layer over all tokens")
+    ref = o_layer(inp)
+    _compare_layer(res, ref, "prefill_t4096", inp)
 
 
 @pytest.mark.slow
@@ -438,12 +463,14 @@ def test_expert_tp_slices(inputs):
     """Expert TP on one GPU: 8 slices of all experts at I' = 256, each a byte view
     of the converted weights, give K-partial GEMM2 rows whose fp32 sum (one bf16
     rounding) matches the full-width rows; the finalize on the summed partials
-    matches the oracle."""
+    matches the oracle on all 32 tokens."""
     inp = inputs("expert_tp8_b32")
     wl = inp.wl
     w = upload_weights(inp)
     full = run_layer(inp, weights=w, tp=1)
     sliced = run_layer(inp, weights=w, tp=wl.tp)
+    _check_sync_words(full)
+    _check_sync_words(sliced)
     assert np.array_equal(full["exp2perm"], sliced["exp2perm"])
     p = np.nonzero(full["perm2tok"] >= 0)[0]
     part_sum = np.zeros((p.size, wl.H), np.float32)
@@ -454,11 +481,12 @@ def test_expert_tp_slices(inputs):
     out_rel = rel_l2(F.bf16_to_f64(sliced["out"]), F.bf16_to_f64(full["out"]))
     say(f"expert TP: slice-sum probe rel-L2 {probe:.2e}, finalize(partials) vs full {out_rel:.2e}")
     assert probe < TOL and out_rel < TOL
-    tokens = np.arange(0, wl.T, 4)
-    _compare_sampled(full, inp, tokens, "expert_tp8 full width")
-    ref = layer_sampled(inp, tokens)
+    tokens = np.arange(wl.T)
+    ref = _compare_sampled(full, inp, tokens, "expert_tp8 full width")
     got = F.bf16_to_f64(sliced["out"][tokens])
-    assert rel_l2(got, F.bf16_to_f64(ref["out"])) < TOL
+    sliced_rel = rel_l2(got, F.bf16_to_f64(ref["out"]))
+    say(f"expert TP: finalize(partials) vs oracle {sliced_rel:.2e}")
+    assert sliced_rel < TOL
 
 
 @pytest.mark.parametrize("name,tile_m", [("decode_b8", 16), ("decode_b8", 64), ("tiny", 16)])
