@@ -355,6 +355,30 @@ int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
                     int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
                     int64_t rows_stride, void* stream);
 
+/* ------------------------------------------------------------------ experts, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_experts_fwd with
+ * the requantized intermediate kept in the library's own static device memory
+ * instead of caller buffers -- the same kernels and the same rows, bit for bit.
+ * The caller passes inputs and outputs only (a_codes, a_sf, meta, w, rows as in
+ * moe_experts_fwd).
+ *   - The static intermediate holds at most MOE_NOALLOC_SCRATCH_BYTES: calls whose
+ *     rows_max * I/2 (rounded up to 256) + rows_max * I/16 bytes exceed it return
+ *     MOE_EUNSUPPORTED before any launch. Every GPU the library runs on holds
+ *     that much for the life of the process.
+ *   - All calls on one GPU share that memory and it keeps the last call's
+ *     contents (nothing in it needs to start at zero). Calls that overlap on one
+ *     GPU -- on different streams, or from different threads -- race; serialize
+ *     them (as calls sharing one meta buffer must be already).
+ *   - No hipMalloc, hipFree or allocating library routine is called. The first
+ *     call on a device looks the memory's address up once (hipGetSymbolAddress,
+ *     with that device current). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+int moe_experts_fwd_noalloc(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
+                            const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                            int tile_m, uint16_t* rows, int64_t rows_stride, void* stream);
+
 /* ------------------------------------------------------------------ experts, W4A16
  * The W4A16 variant of the routed experts: bf16 activations, not quantized,
  * against the same converted NVFP4 weights (the runner page,

@@ -39,6 +39,8 @@
 // requests only its 16-byte weight slot and 2 scale bytes from memory, not 16
 // rows x (8 code bytes + 1 scale byte) spread over 32 cache lines, which leaves
 // a CU's memory requests to the weights.
+#include <mutex>
+
 #include "experts.hpp"
 
 namespace moe {
@@ -566,32 +568,34 @@ static void launch_fused(int d1, int d2, bool two_pairs, dim3 grid, unsigned lds
 #undef MOE_FUSED
 }
 
-}  // namespace moe
-
-extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
-                               const moe_nvfp4_weights* w, int T, int K, int E_local, int H,
-                               int I, int tile_m, uint8_t* inter_codes, uint8_t* inter_sf,
-                               uint16_t* rows, int64_t rows_stride, void* stream) {
-    using namespace moe;
+static int experts_shape_check(const char* name, int T, int K, int E_local, int H, int I, int tile_m) {
     if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E_local < 1 || E_local > MOE_MAX_EXPERTS)
-        return fail(MOE_EINVAL, "moe_experts_fwd: T=%d K=%d E_local=%d out of range", T, K, E_local);
+        return fail(MOE_EINVAL, "%s: T=%d K=%d E_local=%d out of range", name, T, K, E_local);
     if (H < 64 || H % 64 || I < 64 || I % 64)
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: H=%d and I=%d must be multiples of 64", H, I);
+        return fail(MOE_EUNSUPPORTED, "%s: H=%d and I=%d must be multiples of 64", name, H, I);
     if (H > MOE_MAX_HIDDEN || I > MOE_MAX_HIDDEN)
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: H=%d or I=%d above %d", H, I, MOE_MAX_HIDDEN);
+        return fail(MOE_EUNSUPPORTED, "%s: H=%d or I=%d above %d", name, H, I, MOE_MAX_HIDDEN);
     if (tile_m < 16 || tile_m > 256 || tile_m % 16)
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: tile_m=%d must be a multiple of 16 in [16, 256]", tile_m);
-    if (!w || !meta) return fail(MOE_EINVAL, "moe_experts_fwd: NULL weights or meta");
+        return fail(MOE_EUNSUPPORTED, "%s: tile_m=%d must be a multiple of 16 in [16, 256]", name, tile_m);
+    return MOE_OK;
+}
+
+// moe_experts_fwd with its checks; the intermediate at inter_codes / inter_sf
+static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
+                       const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I, int tile_m,
+                       uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows, int64_t rows_stride,
+                       void* stream) {
+    if (int rc = experts_shape_check(name, T, K, E_local, H, I, tile_m)) return rc;
+    if (!w || !meta) return fail(MOE_EINVAL, "%s: NULL weights or meta", name);
     if (T == 0) return MOE_OK;
-    if (!a_codes || !a_sf || !inter_codes || !inter_sf || !rows)
-        return fail(MOE_EINVAL, "moe_experts_fwd: NULL pointer");
+    if (!a_codes || !a_sf || !inter_codes || !inter_sf || !rows) return fail(MOE_EINVAL, "%s: NULL pointer", name);
     const void* ptrs[] = {a_codes, a_sf, meta, inter_codes, inter_sf, rows};
     for (const void* ptr : ptrs)
-        if (!aligned16(ptr)) return fail(MOE_EINVAL, "moe_experts_fwd: pointers must be 16-byte aligned");
-    if (int rc = check_weights(w, H, I, true, "moe_experts_fwd")) return rc;
+        if (!aligned16(ptr)) return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
+    if (int rc = check_weights(w, H, I, true, name)) return rc;
     const int64_t kt1 = H / 64, kt2 = I / 64;
     if (rows_stride < H || rows_stride % 8)
-        return fail(MOE_EINVAL, "moe_experts_fwd: rows_stride must be >= H and a multiple of 8");
+        return fail(MOE_EINVAL, "%s: rows_stride must be >= H and a multiple of 8", name);
     ExpArgs args;
     args.a_codes = a_codes; args.a_sf = a_sf; args.meta = meta;
     args.L = meta_layout(T, K, E_local, tile_m);
@@ -606,7 +610,7 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int3
     const int64_t grid1 = (units1 + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t grid2 = (units2 + kWavesPerBlock - 1) / kWavesPerBlock;
     if (units1 > 0x7FFFFFFF || units2 > 0x7FFFFFFF)   // unit indices are 32-bit in the kernels
-        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many work units");
+        return fail(MOE_EUNSUPPORTED, "%s: too many work units", name);
     hipStream_t s = (hipStream_t)stream;
     // Many routes per expert (on average a quarter of a 128-row block or more):
     // the GEMMs are MFMA-bound and take the register-tiled kernels.
@@ -641,4 +645,70 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int3
     if (wg2) launch_gemm2_wg_kernel(wg_depth((int)kt2, kWgDepth2), dim3((unsigned)grid2), (unsigned)tile_lds_bytes(I), s, args);
     else launch_gemm2_kernel(d2, dim3((unsigned)grid2), 0, s, args);
     return check_launch("moe_experts_fwd (GEMM2)");
+}
+
+// ---------------------------------------------------------------- the intermediate in static memory
+// moe_experts_fwd_noalloc keeps the requantized intermediate (GEMM1's output,
+// GEMM2's input: nothing outside the call reads it) in this array instead of
+// caller memory, so that a caller that cannot allocate device memory needs
+// none beyond its inputs and outputs. Every GPU the library runs on holds its
+// own copy for the life of the process; calls on one GPU share it.
+constexpr int64_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_ptr[kMaxScratchDevices];   // device address of `scratch` on each GPU
+
+// The device address of the current GPU's scratch, looked up once per GPU
+// (with that GPU current) on its first call. The array's name is only a host
+// stand-in: kernels and copies take this address.
+static int scratch_base(const char* name, uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ELAUNCH, "%s: hipGetDevice failed: %s", name, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(MOE_EUNSUPPORTED, "%s: device %d beyond the %d this build tracks", name, dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ELAUNCH, "%s: hipGetSymbolAddress(scratch) failed: %s", name, hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
+                               const moe_nvfp4_weights* w, int T, int K, int E_local, int H,
+                               int I, int tile_m, uint8_t* inter_codes, uint8_t* inter_sf,
+                               uint16_t* rows, int64_t rows_stride, void* stream) {
+    return moe::experts_fwd("moe_experts_fwd", a_codes, a_sf, meta, w, T, K, E_local, H, I, tile_m,
+                            inter_codes, inter_sf, rows, rows_stride, stream);
+}
+
+extern "C" int moe_experts_fwd_noalloc(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
+                                       const moe_nvfp4_weights* w, int T, int K, int E_local, int H,
+                                       int I, int tile_m, uint16_t* rows, int64_t rows_stride,
+                                       void* stream) {
+    using namespace moe;
+    const char* name = "moe_experts_fwd_noalloc";
+    if (int rc = experts_shape_check(name, T, K, E_local, H, I, tile_m)) return rc;
+    const moe_meta_layout L = meta_layout(T, K, E_local, tile_m);
+    const int64_t codes_bytes = (L.rows_max * (I / 2) + 255) / 256 * 256;
+    const int64_t need = codes_bytes + L.rows_max * (I / 16);
+    if (need > kScratchBytes)
+        return fail(MOE_EUNSUPPORTED,
+                    "%s: the intermediate of %lld rows x %d needs %lld bytes, above the %lld of static scratch",
+                    name, (long long)L.rows_max, I, (long long)need, (long long)kScratchBytes);
+    if (!w || !meta) return fail(MOE_EINVAL, "%s: NULL weights or meta", name);
+    if (T == 0 || L.rows_max == 0) return MOE_OK;
+    uint8_t* base = nullptr;
+    if (int rc = scratch_base(name, &base)) return rc;
+    return experts_fwd(name, a_codes, a_sf, meta, w, T, K, E_local, H, I, tile_m, base, base + codes_bytes, rows,
+                       rows_stride, stream);
 }

@@ -21,7 +21,7 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout
            "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
            "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant", "moe_router_logits",
            "moe_router_route", "moe_experts_fwd_w4a16", "moe_experts_fwd_bf16",
-           "moe_validate_weights", "moe_workspace_bytes")
+           "moe_validate_weights", "moe_workspace_bytes", "moe_experts_fwd_noalloc")
 
 
 class MoeMetaLayout(ctypes.Structure):
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         "moe_experts_fwd": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
                                   i32, i32, i32, vp, vp, vp, i64, vp]),
         "moe_finalize": (i32, [vp, i64, i32, i64, vp, vp, vp, f32, f32, i32, i32, i32, i32, vp, vp]),
+        "moe_experts_fwd_noalloc": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
+                                          i32, i32, i32, vp, i64, vp]),
         "moe_validate_weights": (i32, [ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32, i32]),
         "moe_workspace_bytes": (i64, [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(MoeWorkspaceLayout)]),
     }
@@ -243,6 +245,14 @@ def moe_experts_fwd(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, 
     _check(lib().moe_experts_fwd(_ptr(a_codes), _ptr(a_sf), _ptr(meta), ctypes.byref(ws), T, K,
                                  E_local, H, I, tile_m, _ptr(inter_codes), _ptr(inter_sf),
                                  _ptr(rows), rows.stride(0), _stream(stream)), "moe_experts_fwd")
+
+
+def moe_experts_fwd_noalloc(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, tile_m,
+                            rows, stream=None) -> None:
+    ws = weights.struct()
+    _check(lib().moe_experts_fwd_noalloc(_ptr(a_codes), _ptr(a_sf), _ptr(meta), ctypes.byref(ws), T, K,
+                                         E_local, H, I, tile_m, _ptr(rows), rows.stride(0), _stream(stream)),
+           "moe_experts_fwd_noalloc")
 
 
 def moe_experts_fwd_w4a16(x, meta, weights: Weights, T, K, E_local, H, I, tile_m, inter, rows,

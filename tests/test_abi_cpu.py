@@ -220,3 +220,16 @@ def test_workspace_refusals():
     assert L.moe_workspace_bytes(4, 2, 8, 256, 128, 24, 1, None) == -1
     assert L.moe_workspace_bytes(4, 2, 8, 256, 128, 16, 3, None) == -1       # 128 % 3
     assert L.moe_last_error()
+
+
+def test_noalloc_refusals():
+    """moe_experts_fwd_noalloc refuses, before touching the device, an
+    intermediate larger than its static memory, and the usual bad shapes."""
+    L = N.lib()
+    w = N.MoeNvfp4Weights()
+    big = (None, None, None, ctypes.byref(w), 65536, 8, 128, 4096, 4096, 128, None, 4096, None)
+    assert L.moe_experts_fwd_noalloc(*big) == N.MOE_EUNSUPPORTED
+    assert b"static scratch" in L.moe_last_error()
+    assert L.moe_experts_fwd_noalloc(None, None, None, ctypes.byref(w), 4, 2, 8, 96, 128, 16, None, 96, None) \
+        == N.MOE_EUNSUPPORTED                                               # H % 64
+    assert L.moe_experts_fwd_noalloc(None, None, None, None, 4, 2, 8, 256, 128, 16, None, 256, None) == N.MOE_EINVAL
