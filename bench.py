@@ -7,7 +7,11 @@ that the 256 MB Infinity Cache cannot hold them between uses, so weight bytes
 come from HBM (the cold-cache timing the flashinfer_ops page's tuning
 configuration asks for). Inputs are resident in HBM before timing starts.
 
-Prints one JSON line. ``roofline`` is the dominant kernel (the experts step),
+Prints one JSON line. The headline workload is prefill_t4096 (the largest
+single-GPU configuration: T=4096, H=4096, I=1536, E=128, top-8); the same line
+carries a sub-record under ``workloads`` for each decode configuration
+(decode_b8, decode_b64_zipf, expert_tp8_b32), each measured the same way with
+its own roofline. ``roofline`` is the dominant kernel (the experts step),
 timed with HIP events on its own stream: ``kernel_ms`` over 16 consecutive
 steps replayed from one graph (back to back, as the layer runs them), and
 ``kernel_ms_isolated`` one step at a time behind a sleep kernel, which adds a
@@ -19,7 +23,8 @@ many (prefill, the register-tiled kernels) it is bound by the matrix cores:
 the routed rows' GEMM FLOPs over the duration, against the f16 MFMA peak. ``cpu_baseline`` is the CPU oracle timed on a bounded
 sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_b8]
+    python bench.py [--steps K] [--warmup W] [--workload prefill_t4096]
+                    [--sub-workloads decode_b8,decode_b64_zipf,expert_tp8_b32]
 """
 from __future__ import annotations
 
@@ -37,9 +42,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode_b8")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget of the oracle's CPU-baseline sample (0 disables)")
+    ap.add_argument("--workload", default="prefill_t4096")
+    ap.add_argument("--sub-workloads", default="decode_b8,decode_b64_zipf,expert_tp8_b32",
+                    help="comma-separated workloads measured into the line's 'workloads' record ('' for none)")
+    ap.add_argument("--sub-steps", type=int, default=400,
+                    help="timed layer replays of each sub-workload (at least --steps)")
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens of the headline workload in the oracle's CPU-baseline sample (0 disables)")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9)
     return ap.parse_args()
 
@@ -227,39 +236,38 @@ def time_bf16(N, W, wl, x, bufs, counts, n: int) -> dict:
             "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "bound": "hbm"}
 
 
-def cpu_baseline(inp, seconds: float) -> dict:
-    from threadpoolctl import threadpool_info
-    from oracle.layer import layer as o_layer
+def cpu_baseline(inp, n_tokens: int) -> dict:
+    """The CPU oracle (as it stands: numpy fp64, exact GEMMs) on the first
+    n_tokens tokens of the workload, the whole layer for those tokens (quantizer,
+    routing, both GEMMs, finalize), with numpy's BLAS on all the threads it uses
+    and again on one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle.layer import layer_sampled
     wl = inp.wl
+    tokens = np.arange(min(n_tokens, wl.T))
     t0 = time.perf_counter()
-    n = 0
-    while True:
-        o_layer(inp)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+    ref = layer_sampled(inp, tokens)
     dt = time.perf_counter() - t0
+    routes = int(ref["served"].sum())
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": wl.T * wl.K * n / dt, "unit": "routed rows/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n} whole-layer oracle evaluations of {wl.name} ({wl.T * wl.K} routes each), "
-                      f"{dt:.1f} s, numpy fp64 with BLAS on {threads} threads"}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        layer_sampled(inp, tokens)
+        dt1 = time.perf_counter() - t0
+    return {"value": routes / dt, "unit": "routed rows/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt, "single_thread": {"value": routes / dt1, "seconds": dt1, "cores": 1},
+            "sample": f"the whole layer of {wl.name} for its first {len(tokens)} tokens ({routes} routes): "
+                      f"{dt:.1f} s with numpy's BLAS on {threads} threads (the NVFP4 dequantization is "
+                      f"single-threaded numpy), {dt1:.1f} s on one thread"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
-              "multi-GPU path: expert TP is reproduced sequentially on one GPU.", file=sys.stderr)
-        sys.exit(2)
+def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, extras: bool) -> dict:
+    """One workload: the layer step replayed from graphs (steps timed), the expert
+    step timed by events with its roofline, the metadata's sync words checked
+    after the timed replays, and (extras) the neighbouring calls."""
     import torch
-    from nvfp4_block_scaled_route_amd import layer as LY
-    from nvfp4_block_scaled_route_amd import native as N
-    from nvfp4_block_scaled_route_amd import workloads as W
-
-    N.lib()
     dev = "cuda:0"
-    wl = W.WORKLOADS[args.workload]
+    wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl)
 
     def t(a):
@@ -269,14 +277,14 @@ def main():
     g1a, g1c, g2a = t(inp.g1_alphas), t(inp.g1_scale_c), t(inp.g2_alphas)
     logical = [t(inp.w13_codes), t(inp.w13_sf), t(inp.w2_codes), t(inp.w2_sf)]
     wbytes = sum(x.numel() for x in logical)
-    copies = max(4, int(np.ceil(args.rotate_bytes / wbytes)))
+    copies = max(4, int(np.ceil(rotate_bytes / wbytes)))
     weights = [LY.pack_weights(*logical, g1a, g1c, g2a) for _ in range(copies)]
     del logical
+    N.moe_validate_weights(weights[0], wl.E, wl.H, wl.I, wl.tp)
     x, gscale, logits = t(inp.x_bf16), t(inp.a1_gscale), t(inp.logits)
     norm_w = t(inp.norm_weight_bf16)
     shape = LY.LayerShape(wl.T, wl.H, wl.I, wl.E, wl.K, wl.tile_m, wl.tp)
     bufs = LY.Buffers(shape, dev)
-    slices = None
 
     def step(w, stream=None):
         sl = None if wl.tp == 1 else [LY.slice_weights(w, r, wl.tp, wl.H, wl.I) for r in range(wl.tp)]
@@ -287,6 +295,7 @@ def main():
     for i in range(3):
         step(weights[i % copies])
     torch.cuda.synchronize()
+    bufs.check_sync()
     cap = torch.cuda.Stream()
     graphs = []
     for w in weights:
@@ -295,23 +304,24 @@ def main():
             step(w)
         graphs.append(g)
     torch.cuda.synchronize()
-    for i in range(args.warmup):
+    for i in range(warmup):
         graphs[i % copies].replay()
     torch.cuda.synchronize()
 
-    # timed region: K whole-layer steps
+    # timed region: `steps` whole-layer steps
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         graphs[i % copies].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / steps
+    bufs.check_sync()            # no wait gave up: the timed steps computed valid rows
 
     # the dominant kernel, timed with HIP events on the stream it is launched on
     counts = bufs.meta[bufs.layout.expert_counts:bufs.layout.expert_counts + wl.E].cpu().numpy()
     ab = algorithmic_bytes(wl, counts)
     s = torch.cuda.current_stream()
-    n_k = min(args.steps, 400)
+    n_k = min(max(steps, 64), 400)
     I_part = wl.I // wl.tp
 
     def expert_step(i, stream):
@@ -351,49 +361,84 @@ def main():
         g_steps.replay()
         b.record(s)
     torch.cuda.synchronize()
+    bufs.check_sync()
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evg])) / group
     achieved = ab["total"] / (k_ms * 1e-3) / 1e9
 
     routes = wl.T * wl.K
-    out = {
-        "metric": "routed rows/s per MoE layer; HBM GB/s (decode) & MFMA util (prefill) vs peak",
-        "value": routes / (ms_per_step * 1e-3),
-        "unit": "routed rows/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic",
+    rec = {
+        "value": routes / (ms_per_step * 1e-3), "unit": "routed rows/s", "ms_per_step": ms_per_step,
+        "steps": steps, "warmup": warmup,
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
                    "tp": wl.tp, "tile_m": wl.tile_m, "weight_copies": copies},
     }
+    traffic = measured_traffic(wl.name)
+    unit_t = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     if mfma_bound(wl):
         flops = algorithmic_flops(wl, counts)
         tflops = flops / (k_ms * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma", "kernel": "moe_experts_fwd (tiled_kernel<1>: GEMM1+SwiGLU+requant, "
+        rec["roofline"] = {"bound": "mfma", "kernel": "moe_experts_fwd (tiled_kernel<1>: GEMM1+SwiGLU+requant, "
                                                       "tiled_kernel<2>: GEMM2)",
                            "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": measured_traffic(wl.name),
-                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                           "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": traffic, "traffic_unit": unit_t,
                            "algorithmic_flops": flops, "algorithmic_bytes": ab["total"], "hbm_gbs": achieved,
                            "kernel_ms": k_ms, "kernel_ms_isolated": k_ms_isolated}
     else:
-        out["roofline"] = {"bound": "hbm", "kernel": "moe_experts_fwd (experts_fused_kernel: GEMM1+SwiGLU+requant "
-                                                     "and GEMM2 in one launch)",
+        launches = "" if wl.tp == 1 else f"; {wl.tp} slice launches a step, figures per step"
+        rec["roofline"] = {"bound": "hbm", "kernel": "moe_experts_fwd (experts_fused_kernel: GEMM1+SwiGLU+requant "
+                                                     f"and GEMM2 in one launch{launches})",
                            "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name),
-                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                           "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_unit": unit_t,
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                            "experts_touched": ab["touched"], "kernel_ms": k_ms,
                            "kernel_ms_isolated": k_ms_isolated}
-    extra = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
-    if wl.tp == 1 and not mfma_bound(wl):          # on the layer's routing, before the router rewrites it
-        extra["moe_experts_fwd_w4a16"] = time_w4a16(N, wl, x, bufs, weights, ab, n_k)
-        if wl.E * 3 * wl.H * wl.I * 2 <= 1 << 30:   # bf16 weights of at most 1 GiB
-            extra["moe_experts_fwd_bf16"] = time_bf16(N, W, wl, x, bufs, counts, n_k)
-    extra.update(time_router(N, W, wl, bufs, n_k))
-    out["extra_kernels"] = extra
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if extras:
+        extra = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
+        if wl.tp == 1 and not mfma_bound(wl):      # on the layer's routing, before the router rewrites it
+            extra["moe_experts_fwd_w4a16"] = time_w4a16(N, wl, x, bufs, weights, ab, n_k)
+            if wl.E * 3 * wl.H * wl.I * 2 <= 1 << 30:   # bf16 weights of at most 1 GiB
+                extra["moe_experts_fwd_bf16"] = time_bf16(N, W, wl, x, bufs, counts, n_k)
+        extra.update(time_router(N, W, wl, bufs, n_k))
+        rec["extra_kernels"] = extra
+    del graphs, g_steps, weights, bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec, inp
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path: expert TP is reproduced sequentially on one GPU.", file=sys.stderr)
+        sys.exit(2)
+    from nvfp4_block_scaled_route_amd import layer as LY
+    from nvfp4_block_scaled_route_amd import native as N
+    from nvfp4_block_scaled_route_amd import workloads as W
+
+    N.lib()
+    head, inp = measure(N, LY, W, args.workload, args.steps, args.warmup, args.rotate_bytes, True)
+    out = {
+        "metric": "routed rows/s per MoE layer; HBM GB/s (decode) & MFMA util (prefill) vs peak",
+        "value": head["value"],
+        "unit": "routed rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "extra_kernels": head.get("extra_kernels", {}),
+    }
+    subs = [w for w in args.sub_workloads.split(",") if w and w != args.workload]
+    if subs:
+        out["workloads"] = {}
+        for name in subs:
+            rec, _ = measure(N, LY, W, name, max(args.steps, args.sub_steps), max(args.warmup, 20),
+                             args.rotate_bytes, name != "expert_tp8_b32")
+            out["workloads"][name] = rec
+    if args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 
