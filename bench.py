@@ -91,17 +91,21 @@ def algorithmic_flops(wl, counts) -> float:
     return 2.0 * routes * (2 * wl.I * wl.H + wl.H * wl.I)
 
 
-def algorithmic_bytes(wl, counts) -> dict:
-    """Bytes the experts step must move at least once per call."""
+def algorithmic_bytes(wl, counts, finalize: bool = False) -> dict:
+    """Bytes the experts step must move at least once per call (per layer step:
+    all expert-TP slices). finalize: the step also finalizes (moe_experts_finalize),
+    reading every slice's rows once more and writing the bf16 output."""
     touched = int((counts > 0).sum())
     H, I = wl.H, wl.I
     per_expert = 2 * I * H // 2 + 2 * I * H // 16 + H * I // 2 + H * I // 16   # 27/16 I H
     routes = int(counts.sum())
-    act = wl.T * (H // 2 + H // 16)                        # NVFP4 input, read once
+    act = wl.tp * wl.T * (H // 2 + H // 16)                # NVFP4 input, read once a slice
     inter = 2 * routes * (I // 2 + I // 16)                # NVFP4 intermediate, written and read
-    rows = routes * H * 2                                  # GEMM2 bf16 rows written
-    return dict(weights=touched * per_expert, touched=touched, other=act + inter + rows,
-                total=touched * per_expert + act + inter + rows)
+    rows = wl.tp * routes * H * 2                          # GEMM2 bf16 rows written, one partial a slice
+    fin = (wl.tp * routes * H * 2 + wl.T * H * 2) if finalize else 0   # rows read, output written
+    other = act + inter + rows + fin
+    return dict(weights=touched * per_expert, touched=touched, other=other,
+                total=touched * per_expert + other)
 
 
 def time_norm_quant(N, x, norm_w, gscale, wl, n: int) -> dict:
@@ -324,12 +328,20 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
     n_k = min(max(steps, 64), 400)
     I_part = wl.I // wl.tp
 
-    def expert_step(i, stream):
+    def expert_step(i, stream, finalize=False):
+        """The layer's expert launches: every slice's moe_experts_fwd; with finalize
+        the last one is moe_experts_finalize (the finalize in the same launch)."""
         w = weights[i % copies]
         sl = [w] if wl.tp == 1 else [LY.slice_weights(w, r, wl.tp, wl.H, wl.I) for r in range(wl.tp)]
         for r, ww in enumerate(sl):
-            N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H,
-                              I_part, wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
+            if finalize and r == len(sl) - 1:
+                N.moe_experts_finalize(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H, I_part,
+                                       wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows, len(sl),
+                                       bufs.rows.stride(0), bufs.weights, norm_w, wl.gain_center, wl.eps,
+                                       bool(wl.weight_before_norm), bufs.out, stream)
+            else:
+                N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, ww, wl.T, wl.K, wl.E, wl.H,
+                                  I_part, wl.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
 
     # (1) one step at a time, a sleep kernel ahead of each so that host enqueue
     # time stays out: the step's duration plus one launch's dispatch
@@ -392,6 +404,26 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                            "experts_touched": ab["touched"], "kernel_ms": k_ms,
                            "kernel_ms_isolated": k_ms_isolated}
+    if not mfma_bound(wl):
+        # the expert step with the finalize in its launch (moe_experts_finalize),
+        # against the expert step followed by moe_finalize, back to back
+        def with_fin(s_):
+            with_fin.i += 1
+            expert_step(with_fin.i, s_, finalize=True)
+        with_fin.i = 0
+
+        def then_fin(s_):
+            then_fin.i += 1
+            expert_step(then_fin.i, s_)
+            N.moe_finalize(bufs.rows, wl.tp, bufs.rows.stride(0), bufs.exp2perm, bufs.weights, norm_w,
+                           wl.gain_center, wl.eps, bool(wl.weight_before_norm), wl.T, wl.K, wl.H, bufs.out, s_)
+        then_fin.i = 0
+        us_f, iso_f = _event_us(with_fin, min(n_k, 128))
+        us_s, iso_s = _event_us(then_fin, min(n_k, 128))
+        bufs.check_sync()
+        rec["finalize_in_launch"] = {"moe_experts_finalize_us": us_f, "moe_experts_finalize_us_isolated": iso_f,
+                                     "moe_experts_fwd_then_moe_finalize_us": us_s,
+                                     "moe_experts_fwd_then_moe_finalize_us_isolated": iso_s}
     if extras:
         extra = {"nvfp4_norm_quant": time_norm_quant(N, x, norm_w, gscale, wl, n_k)}
         if wl.tp == 1 and not mfma_bound(wl):      # on the layer's routing, before the router rewrites it

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 5
+#define MOE_NVFP4_ABI_VERSION 6
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -90,6 +90,13 @@ int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
  *                                moe_route; moe_experts_fwd's one-launch form
  *                                uses them and leaves them at 0 again. The
  *                                other words are not used.
+ *   tok_sync        [32*T]       three counters per token t, at 32*t .. 32*t + 2
+ *                                (128 bytes apart), set to 0 by moe_route; the
+ *                                one-launch form of moe_experts_finalize uses them
+ *                                and leaves them at 0 again. The other words are
+ *                                not used.
+ *   fin_part        [128*T]      that form's working space: per token, the fp32
+ *                                partial sums of squares its workgroups exchange
  *   perm_counts     [ceil(T*K/512) * E_local]  moe_route's working space when it
  *                                routes more than 32 tokens: per chunk of 512
  *                                routes, the routes of each expert, then the
@@ -112,6 +119,8 @@ typedef struct moe_meta_layout {
     int64_t sub_sync;
     int64_t subs_max;
     int64_t perm_counts;
+    int64_t tok_sync;
+    int64_t fin_part;
 } moe_meta_layout;
 
 int moe_meta_layout_get(int T, int K, int E_local, int tile_m, moe_meta_layout* out);
@@ -354,6 +363,30 @@ int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
                     const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
                     int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
                     int64_t rows_stride, void* stream);
+
+/* ------------------------------------------------------------------ experts + finalize
+ * moe_experts_fwd followed by moe_finalize, with the same results bit for bit:
+ * the expert step writes its GEMM2 rows as partial n_partials - 1, at
+ *   rows + (n_partials - 1) * partial_stride
+ * (partials 0 .. n_partials - 2, the other expert-TP slices, were written by
+ * earlier calls), then every token's output is finalized from all n_partials
+ * partials as moe_finalize(rows, rows_stride, n_partials, partial_stride,
+ * meta + exp2perm, topk_weights, norm_weight, gain_center, eps,
+ * weight_before_norm, T, K, H, out) computes it (the runner page,
+ * "MusePostExpertFinalize"; the flashinfer_ops page's module docstring: the
+ * tail kernel finalizes).
+ * Where moe_experts_fwd runs in one launch, the finalize runs in that launch
+ * too: the workgroup that publishes a token's last route row finalizes the
+ * token, counting arrivals on meta's tok_sync (moe_route leaves them at 0 and
+ * the call returns them to 0; calls that share one meta buffer must not run
+ * concurrently). Otherwise moe_finalize is launched after the expert step.
+ * Arguments and checks are those of the two calls. */
+int moe_experts_finalize(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
+                         const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                         int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
+                         int64_t rows_stride, int n_partials, int64_t partial_stride,
+                         const float* topk_weights, const uint16_t* norm_weight, float gain_center,
+                         float eps, int weight_before_norm, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------------------ experts, no allocation
  * For callers that cannot allocate device memory (code under HIP graph capture,

@@ -41,6 +41,8 @@ moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m) {
     L.sync_status = 2;
     L.subs_max = L.rows_max / 16;
     L.sub_sync = off;       off += align64(kSubSyncStride * L.subs_max);
+    L.tok_sync = off;       off += align64(kTokSyncStride * (int64_t)T);
+    L.fin_part = off;       off += align64(kFinPartWords * (int64_t)T);
     L.perm_counts = off;    off += align64(((R + 511) / 512) * E_local);
     L.total_ints = off;
     return L;

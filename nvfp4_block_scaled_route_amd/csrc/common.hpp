@@ -31,6 +31,11 @@ moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m);
 // metadata (1 KB): tiles' counters on distinct cache lines and memory channels,
 // so that the polls of many workgroups do not all queue on one channel.
 constexpr int kSubSyncStride = 256;
+// int32 words between the arrival counters of consecutive tokens (128 bytes:
+// one counter a cache line) -- moe_experts_finalize's one-launch form
+constexpr int kTokSyncStride = 32;
+// words a token's finalize exchanges between its workgroups: 16 waves x 8 routes
+constexpr int kFinPartWords = 128;
 // converted weight layout: code and scale bytes per row pair and k-tile
 constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;
 

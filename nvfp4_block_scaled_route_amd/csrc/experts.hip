@@ -42,6 +42,7 @@
 #include <mutex>
 
 #include "experts.hpp"
+#include "finalize.hpp"
 
 namespace moe {
 
@@ -416,12 +417,175 @@ __device__ __forceinline__ void run_held(const Stage (&st)[D], const uint8_t* lc
     }
 }
 
-template <int D1, int D2, int P2>
-__global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint32_t g1_blocks) {
+// ---------------------------------------------------------------- the finalize in the launch
+// moe_experts_finalize's one-launch form (K <= 8). GEMM2 workgroups write their
+// rows with agent-coherent stores, wait until they have completed, and count
+// themselves on the arrival counter (word 0) of each token in their 16 rows.
+// The grid ends with F = fin_threads(H) / 256 finalizer workgroups per token:
+// finalizer f plays moe_finalize's threads [256 f, 256 f + 256) (finalize.hpp),
+// so the arithmetic and its order are moe_finalize's. It waits until every
+// GEMM2 workgroup of every tile holding one of the token's served routes has
+// arrived (served routes x the H >> (6 + P2) workgroups of a tile), reads its
+// columns of the routes' rows (agent-coherent loads) once and keeps them in
+// registers, and forms its waves' sums of squares. With F > 1 the token's
+// finalizers exchange those through meta's fin_part (agent-coherent stores,
+// then word 1 of the token's counters counts them), each runs the same
+// 16-lane tree on all of them, and the last to pass (word 2) returns the
+// token's counters to 0. A token with no served route gets zero rows at once.
+// Finalizers are dispatched after every GEMM workgroup, so what they wait for
+// is already running; their waits are bounded as GEMM2's are (sync_status 1
+// if one gives up).
+struct FinFuse {
+    FinArgs f;             // rows: partial 0 (this launch writes partial n_partials - 1)
+    int32_t* tok_sync;     // meta's tok_sync
+    int32_t* fin_part;     // meta's fin_part
+    uint32_t fin_block0;   // the first finalizer workgroup
+    int F;                 // finalizer workgroups per token
+};
+
+// LDS of a finalizer workgroup
+struct FinLds {
+    float s_part[kFinBatch][kFinMaxWaves];
+    float s_inv[MOE_MAX_TOPK];
+};
+
+// A GEMM2 workgroup's rows are complete: count it on each of its tokens.
+__device__ __forceinline__ void arrive(const FinFuse& fin, const RowTile& rt, int wave, int lane) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's rows have completed
+    __syncthreads();
+    if (wave == 0 && lane < 16 && ((rt.vmask >> lane) & 1u))
+        __hip_atomic_fetch_add(fin.tok_sync + (int64_t)rt.tok * kTokSyncStride, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int W, int P2>
+__device__ void finalizer(const ExpArgs& a, const FinFuse& fin, uint8_t* lds) {
+    FinLds& l = *reinterpret_cast<FinLds*>(lds);
+    const FinArgs& f = fin.f;
+    const uint32_t x = blockIdx.x - fin.fin_block0;
+    const int t = (int)(x / (uint32_t)fin.F), part = (int)(x - (uint32_t)t * fin.F);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nthreads_v = fin_threads(f.H), nwaves_v = nthreads_v >> 6, ngroups = f.H / W;
+    const int vt = part * kThreads + tid;              // moe_finalize's thread this one plays
+    const bool wave_on = (vt & ~63) < nthreads_v;      // uniform over the wave
+    int32_t* cnt = fin.tok_sync + (int64_t)t * kTokSyncStride;
+    // what does not depend on the GEMM2 rows is read before the wait
+    int perm[kFinBatch];
+    float wk[kFinBatch];
+    int served = 0;
+#pragma unroll
+    for (int kk = 0; kk < kFinBatch; ++kk) {
+        perm[kk] = kk < f.K ? f.exp2perm[(int64_t)t * f.K + kk] : -1;
+        wk[kk] = kk < f.K ? f.weights[(int64_t)t * f.K + kk] : 0.0f;
+        served += perm[kk] >= 0;
+    }
+    float g[W];
+    if (vt < ngroups) gamma_cols<W>(f, vt, g);
+    if (served == 0) {                                 // no served route: zero columns
+        if (vt < ngroups) {
+            Cols<W> z;
+#pragma unroll
+            for (int i = 0; i < W / 2; ++i) z.w[i] = 0u;
+            store_cols<W>(f.out + (int64_t)t * f.H + W * vt, z);
+        }
+        return;
+    }
+    if (tid == 0) {
+        wait_ready(cnt, served * (a.H >> (6 + P2)), a.status);
+        if (fin.F == 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    Cols<W> raw[kFinBatch];
+#pragma unroll
+    for (int kk = 0; kk < kFinBatch; ++kk) {
+#pragma unroll
+        for (int i = 0; i < W / 2; ++i) raw[kk].w[i] = 0u;
+        if (perm[kk] >= 0 && vt < ngroups) raw[kk] = load_row_coherent<W>(f, perm[kk], vt);
+    }
+    // sums of squares: the thread's W columns, then its wave
+    float ss[kFinBatch];
+#pragma unroll
+    for (int kk = 0; kk < kFinBatch; ++kk) {
+        ss[kk] = 0.0f;
+        if (vt < ngroups) {
+            float v[W];
+            unpack<W>(raw[kk], v);
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const float z = f.weight_before_norm ? __fmul_rn(g[i], v[i]) : v[i];
+                ss[kk] = __fadd_rn(ss[kk], __fmul_rn(z, z));
+            }
+        }
+        if (wave_on) ss[kk] = wave_sum(ss[kk]);
+    }
+    if (fin.F == 1) {
+        if (wave_on && lane == 0)
+#pragma unroll
+            for (int kk = 0; kk < kFinBatch; ++kk) l.s_part[kk][vt >> 6] = ss[kk];
+        __syncthreads();
+    } else {
+        int32_t* pp = fin.fin_part + (int64_t)t * kFinPartWords;
+        if (wave_on && lane == 0)
+#pragma unroll
+            for (int kk = 0; kk < kFinBatch; ++kk)
+                __hip_atomic_store(pp + (vt >> 6) * kFinBatch + kk, __float_as_int(ss[kk]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+            __hip_atomic_fetch_add(cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_ready(cnt + 1, fin.F, a.status);
+        }
+        __syncthreads();
+        if (tid < kFinBatch * kFinMaxWaves) {
+            const int k = tid >> 4, w = tid & 15;
+            l.s_part[k][w] = w < nwaves_v ? __int_as_float(__hip_atomic_load(pp + w * kFinBatch + k, __ATOMIC_RELAXED,
+                                                                              __HIP_MEMORY_SCOPE_AGENT))
+                                          : 0.0f;
+        }
+        __syncthreads();
+        if (tid == 0 &&
+            __hip_atomic_fetch_add(cnt + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fin.F - 1) {
+            __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cnt + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    fin_inv_tree(f, 0, tid, kThreads, nwaves_v, l.s_part, l.s_inv);
+    __syncthreads();
+    // weighted sum over the routes, k ascending, from the held rows
+    if (vt < ngroups) {
+        float acc[W];
+#pragma unroll
+        for (int i = 0; i < W; ++i) acc[i] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < kFinBatch; ++kk) {
+            if (kk >= f.K || perm[kk] < 0) continue;   // a missing row normalizes to zero
+            const float inv = l.s_inv[kk];
+            float v[W];
+            unpack<W>(raw[kk], v);
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const float y = f.weight_before_norm ? __fmul_rn(__fmul_rn(g[i], v[i]), inv)
+                                                     : __fmul_rn(g[i], __fmul_rn(v[i], inv));
+                acc[i] = __fadd_rn(acc[i], __fmul_rn(y, wk[kk]));
+            }
+        }
+        store_cols<W>(f.out + (int64_t)t * f.H + W * vt, pack<W>(acc));
+    }
+}
+
+template <int D1, int D2, int P2, bool kFin>
+__global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint32_t g1_blocks, FinFuse fin) {
     extern __shared__ __align__(16) uint8_t tile_lds[];
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* lc = tile_lds + ((q >> 1) * 16 + n) * 16 + (q & 1) * 8;
+    if (kFin && blockIdx.x >= fin.fin_block0) {
+        if (fin_w(a.H) == 2) finalizer<2, P2>(a, fin, tile_lds);
+        else finalizer<4, P2>(a, fin, tile_lds);        // the one-launch rule: H <= 4352
+        return;
+    }
     if (blockIdx.x < g1_blocks) {
         const uint32_t n1 = a.I >> 4;
         const uint32_t unit = blockIdx.x * kWavesPerBlock + wave;
@@ -476,15 +640,16 @@ __global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint
     floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
     if constexpr (P2 == 2) {
         run_held<D2>(st, lc, ls, acc0, acc1);
-        gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+        gemm2_epilogue<kFin>(a, rt, e, c, n, q, acc0, acc1);
         acc0 = floatx4{0, 0, 0, 0};
         acc1 = floatx4{0, 0, 0, 0};
         run_held<D2>(st1, lc, ls, acc0, acc1);
-        gemm2_epilogue(a, rt, e, c + 1, n, q, acc0, acc1);
+        gemm2_epilogue<kFin>(a, rt, e, c + 1, n, q, acc0, acc1);
     } else {
         stream_lds_run<D2>(st, p, lc, ls, a.I >> 6, acc0, acc1);
-        gemm2_epilogue(a, rt, e, c, n, q, acc0, acc1);
+        gemm2_epilogue<kFin>(a, rt, e, c, n, q, acc0, acc1);
     }
+    if constexpr (kFin) arrive(fin, rt, wave, lane);
 }
 
 // ---------------------------------------------------------------- launch
@@ -551,10 +716,11 @@ MOE_LAUNCH_WG(gemm2_wg_kernel)
 // a wave per SIMD and were slower, and 6 measured no better than 4.
 static int fused_depth2(int kt2) { return kt2 % 8 == 0 ? 8 : 4; }
 
+template <bool kFin>
 static void launch_fused(int d1, int d2, bool two_pairs, dim3 grid, unsigned lds, hipStream_t s,
-                         const ExpArgs& a, uint32_t g1_blocks) {
+                         const ExpArgs& a, uint32_t g1_blocks, const FinFuse& fin) {
 #define MOE_FUSED(D1, D2, P2) \
-    hipLaunchKernelGGL((experts_fused_kernel<D1, D2, P2>), grid, dim3(kThreads), lds, s, a, g1_blocks)
+    hipLaunchKernelGGL((experts_fused_kernel<D1, D2, P2, kFin>), grid, dim3(kThreads), lds, s, a, g1_blocks, fin)
     if (two_pairs) {
         if (d1 == 8) MOE_FUSED(8, 4, 2);
         else MOE_FUSED(4, 4, 2);
@@ -580,11 +746,13 @@ static int experts_shape_check(const char* name, int T, int K, int E_local, int 
     return MOE_OK;
 }
 
-// moe_experts_fwd with its checks; the intermediate at inter_codes / inter_sf
+// moe_experts_fwd with its checks; the intermediate at inter_codes / inter_sf.
+// fin (moe_experts_finalize): the finalize of the rows too -- in the same launch
+// where the one-launch form applies, else by moe_finalize after the GEMMs.
 static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
                        const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I, int tile_m,
                        uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows, int64_t rows_stride,
-                       void* stream) {
+                       void* stream, const FinArgs* fin = nullptr) {
     if (int rc = experts_shape_check(name, T, K, E_local, H, I, tile_m)) return rc;
     if (!w || !meta) return fail(MOE_EINVAL, "%s: NULL weights or meta", name);
     if (T == 0) return MOE_OK;
@@ -614,9 +782,15 @@ static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* 
     hipStream_t s = (hipStream_t)stream;
     // Many routes per expert (on average a quarter of a 128-row block or more):
     // the GEMMs are MFMA-bound and take the register-tiled kernels.
+    auto finalize_after = [&](int rc) {
+        if (rc || !fin) return rc;
+        return moe_finalize(fin->rows, fin->rows_stride, fin->n_partials, fin->partial_stride, fin->exp2perm,
+                            fin->weights, fin->norm_weight, fin->gain_center, fin->eps, fin->weight_before_norm,
+                            fin->T, fin->K, fin->H, fin->out, stream);
+    };
     if (tiled_shape_ok(T, H, I, tile_m) && (int64_t)T * K >= (int64_t)32 * E_local) {
         launch_tiled(args, s);
-        return check_launch("moe_experts_fwd (tiled)");
+        return finalize_after(check_launch("moe_experts_fwd (tiled)"));
     }
     // Workgroups of four units sharing one LDS copy of their tile's activation
     // where the shape allows: whole 16-byte scale chunks (K % 256 == 0), at
@@ -635,8 +809,20 @@ static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* 
         // I = 256: a GEMM2 wave holds all 4 k-tiles of two output pairs (H % 256 == 0)
         const bool two_pairs = kt2 == 4 && H % 256 == 0;
         const int64_t g2 = two_pairs ? grid2 / 2 : grid2;
-        launch_fused(f1, f2, two_pairs, dim3((unsigned)(grid1 + g2)), lds, s, args, (uint32_t)grid1);
-        return check_launch("moe_experts_fwd (GEMM1 + GEMM2)");
+        FinFuse ff{};
+        if (fin && K <= kFinBatch) {
+            ff.f = *fin;
+            ff.tok_sync = meta + args.L.tok_sync;
+            ff.fin_part = meta + args.L.fin_part;
+            ff.fin_block0 = (uint32_t)(grid1 + g2);
+            ff.F = (fin_threads(H) + kThreads - 1) / kThreads;
+            const unsigned lds_f = (unsigned)sizeof(FinLds) > lds ? (unsigned)sizeof(FinLds) : lds;
+            launch_fused<true>(f1, f2, two_pairs, dim3((unsigned)(grid1 + g2 + (int64_t)T * ff.F)), lds_f, s, args,
+                               (uint32_t)grid1, ff);
+            return check_launch("moe_experts_finalize (GEMM1 + GEMM2 + finalize)");
+        }
+        launch_fused<false>(f1, f2, two_pairs, dim3((unsigned)(grid1 + g2)), lds, s, args, (uint32_t)grid1, ff);
+        return finalize_after(check_launch("moe_experts_fwd (GEMM1 + GEMM2)"));
     }
     if (wg1) launch_gemm1_wg_kernel(wg_depth((int)kt1, kWgDepth1), dim3((unsigned)grid1), (unsigned)tile_lds_bytes(H), s, args);
     else launch_gemm1_kernel(d1, dim3((unsigned)grid1), 0, s, args);
@@ -644,7 +830,7 @@ static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* 
     if (rc) return rc;
     if (wg2) launch_gemm2_wg_kernel(wg_depth((int)kt2, kWgDepth2), dim3((unsigned)grid2), (unsigned)tile_lds_bytes(I), s, args);
     else launch_gemm2_kernel(d2, dim3((unsigned)grid2), 0, s, args);
-    return check_launch("moe_experts_fwd (GEMM2)");
+    return finalize_after(check_launch("moe_experts_fwd (GEMM2)"));
 }
 
 // ---------------------------------------------------------------- the intermediate in static memory
@@ -689,6 +875,33 @@ extern "C" int moe_experts_fwd(const uint8_t* a_codes, const uint8_t* a_sf, int3
                                uint16_t* rows, int64_t rows_stride, void* stream) {
     return moe::experts_fwd("moe_experts_fwd", a_codes, a_sf, meta, w, T, K, E_local, H, I, tile_m,
                             inter_codes, inter_sf, rows, rows_stride, stream);
+}
+
+extern "C" int moe_experts_finalize(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,
+                                    const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
+                                    int tile_m, uint8_t* inter_codes, uint8_t* inter_sf, uint16_t* rows,
+                                    int64_t rows_stride, int n_partials, int64_t partial_stride,
+                                    const float* topk_weights, const uint16_t* norm_weight, float gain_center,
+                                    float eps, int weight_before_norm, uint16_t* out, void* stream) {
+    using namespace moe;
+    const char* name = "moe_experts_finalize";
+    if (int rc = experts_shape_check(name, T, K, E_local, H, I, tile_m)) return rc;
+    if (n_partials < 1 || n_partials > 16)
+        return fail(MOE_EUNSUPPORTED, "%s: n_partials=%d outside [1, 16]", name, n_partials);
+    if (T == 0) return MOE_OK;
+    if (!rows || !topk_weights || !out || !meta) return fail(MOE_EINVAL, "%s: NULL pointer", name);
+    if (!aligned16(topk_weights) || !aligned16(out) || (norm_weight && !aligned16(norm_weight)))
+        return fail(MOE_EINVAL, "%s: pointers must be 16-byte aligned", name);
+    if (n_partials > 1 && (partial_stride % 8 || partial_stride < 0))
+        return fail(MOE_EINVAL, "%s: partial_stride must be a non-negative multiple of 8", name);
+    const moe_meta_layout L = meta_layout(T, K, E_local, tile_m);
+    FinArgs f;
+    f.rows = rows; f.rows_stride = rows_stride; f.n_partials = n_partials; f.partial_stride = partial_stride;
+    f.exp2perm = meta + L.exp2perm; f.weights = topk_weights; f.norm_weight = norm_weight;
+    f.gain_center = gain_center; f.eps = eps; f.weight_before_norm = weight_before_norm ? 1 : 0;
+    f.T = T; f.K = K; f.H = H; f.out = out;
+    return experts_fwd(name, a_codes, a_sf, meta, w, T, K, E_local, H, I, tile_m, inter_codes, inter_sf,
+                       rows + (int64_t)(n_partials - 1) * partial_stride, rows_stride, stream, &f);
 }
 
 extern "C" int moe_experts_fwd_noalloc(const uint8_t* a_codes, const uint8_t* a_sf, int32_t* meta,

@@ -100,6 +100,9 @@ __device__ __forceinline__ RowTile row_tile(const ExpArgs& a, int sub, int n) {
 }
 
 // GEMM2: lane (q, n) holds rows 4q + i of output columns 32c + n and 32c + 16 + n.
+// kPublish: the rows are read by other workgroups of the same launch (the
+// finalize in the launch), so they are written with agent-coherent stores.
+template <bool kPublish = false>
 __device__ __forceinline__ void gemm2_epilogue(const ExpArgs& a, const RowTile& rt, int e, int c, int n, int q,
                                                const floatx4& acc0, const floatx4& acc1) {
     const float alpha = a.w.g2_alphas[e];
@@ -108,8 +111,14 @@ __device__ __forceinline__ void gemm2_epilogue(const ExpArgs& a, const RowTile& 
         const int m = 4 * q + i;
         if ((rt.vmask >> m) & 1u) {
             uint16_t* out = a.rows + (int64_t)(rt.row0 + m) * a.rows_stride + c * 32 + n;
-            out[0] = (uint16_t)f32_to_bf16(acc0[i] * alpha);
-            out[16] = (uint16_t)f32_to_bf16(acc1[i] * alpha);
+            const uint16_t v0 = (uint16_t)f32_to_bf16(acc0[i] * alpha), v1 = (uint16_t)f32_to_bf16(acc1[i] * alpha);
+            if (kPublish) {
+                __hip_atomic_store(out, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(out + 16, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                out[0] = v0;
+                out[16] = v1;
+            }
         }
     }
 }

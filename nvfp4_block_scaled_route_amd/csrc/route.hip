@@ -233,6 +233,8 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e) {
 __device__ __forceinline__ void clear_sync(const RouteArgs& a, int i, int step) {
     int32_t* sync = a.meta + a.L.sub_sync;
     for (int64_t x = i; x < 2 * a.L.subs_max; x += step) sync[(x >> 1) * kSubSyncStride + (x & 1)] = 0;
+    int32_t* tok = a.meta + a.L.tok_sync;
+    for (int64_t x = i; x < 3 * a.T; x += step) tok[(x / 3) * kTokSyncStride + x % 3] = 0;
     if (i == 0) a.meta[a.L.sync_status] = 0;
 }
 
@@ -587,6 +589,13 @@ __global__ void __launch_bounds__(kRouteThreads) perm_scatter_kernel(RouteArgs a
     int32_t* sync = a.meta + a.L.sub_sync;
     for (int64_t x = blockIdx.x * wshare + tid; x < min(words, (blockIdx.x + 1) * wshare); x += kRouteThreads)
         sync[(x >> 1) * kSubSyncStride + (x & 1)] = 0;
+    const int64_t tshare = (a.T + gridDim.x - 1) / gridDim.x;
+    int32_t* tok = a.meta + a.L.tok_sync;
+    for (int64_t x = blockIdx.x * tshare + tid; x < min((int64_t)a.T, (blockIdx.x + 1) * tshare); x += kRouteThreads) {
+        tok[x * kTokSyncStride] = 0;
+        tok[x * kTokSyncStride + 1] = 0;
+        tok[x * kTokSyncStride + 2] = 0;
+    }
     if (blockIdx.x == 0 && tid == 0) a.meta[a.L.sync_status] = 0;
 }
 

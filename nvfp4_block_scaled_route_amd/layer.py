@@ -118,23 +118,29 @@ class Buffers:
 
     def check_sync(self) -> None:
         """Raise if an expert step's bounded wait gave up (meta[sync_status] != 0:
-        its rows are not valid) or left a tile counter non-zero. Reads the
+        its rows are not valid) or left a tile or token counter non-zero. Reads the
         metadata back, so the caller synchronizes the stream first."""
         L = self.layout
         status = int(self.meta[L.sync_status].item())
         counters = self.meta[L.sub_sync:L.sub_sync + 256 * L.subs_max].view(-1, 256)[:, :2]
-        if status != 0 or bool(counters.any().item()):
+        tok = self.meta[L.tok_sync:L.tok_sync + 32 * self.shape.T].view(-1, 32)[:, 0]
+        bad = int((counters != 0).sum().item()) + int((tok != 0).sum().item())
+        if status != 0 or bad:
             raise N.MoeError(f"expert step synchronization failed: sync_status={status}, "
-                             f"non-zero tile counters={int((counters != 0).sum().item())}; the rows are not valid")
+                             f"non-zero counters={bad}; the rows and outputs are not valid")
 
 
 def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, weights: N.Weights,
               norm_weight, gain_center: float, eps: float, weight_before_norm: bool,
               route_scale: float = 1.0, slices: list[N.Weights] | None = None, stream=None,
-              fused_route_quant: bool = True, check: bool = False) -> None:
-    """route -> quant -> experts (per TP slice) -> finalize, all enqueued on one stream
-    (route and quant in one launch unless fused_route_quant is False). With check,
-    waits for the stream and raises if an expert step's wait gave up."""
+              fused_route_quant: bool = True, fused_finalize: bool = False, check: bool = False) -> None:
+    """route -> quant -> experts (per TP slice) -> finalize, all enqueued on one stream.
+    Route and quant run in one launch unless fused_route_quant is False. With
+    fused_finalize the last (or only) slice's experts and the finalize run as one
+    call (moe_experts_finalize: one launch at decode shapes; one launch fewer,
+    which pays when launches are enqueued one by one, while replayed from a
+    graph the separate finalize is as fast or faster). With check, waits for the
+    stream and raises if an expert step's wait gave up."""
     s = bufs.shape
     if fused_route_quant:
         N.moe_route_quant(logits, expert_bias, is_padding, s.K, route_scale, s.tile_m, 0, s.E,
@@ -146,11 +152,18 @@ def run_layer(bufs: Buffers, x_bf16, gscale, logits, expert_bias, is_padding, we
         N.nvfp4_quant(x_bf16, gscale, bufs.a_codes, bufs.a_sf, stream)
     parts = slices if slices is not None else [weights]
     I_part = s.I // len(parts)
-    for r, w in enumerate(parts):
-        N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, w, s.T, s.K, s.E, s.H, I_part,
+    n_sep = len(parts) - 1 if fused_finalize else len(parts)
+    for r in range(n_sep):
+        N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, parts[r], s.T, s.K, s.E, s.H, I_part,
                           s.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows[r], stream)
-    N.moe_finalize(bufs.rows, len(parts), bufs.rows.stride(0), bufs.exp2perm, bufs.weights,
-                   norm_weight, gain_center, eps, weight_before_norm, s.T, s.K, s.H, bufs.out, stream)
+    if fused_finalize:
+        N.moe_experts_finalize(bufs.a_codes, bufs.a_sf, bufs.meta, parts[-1], s.T, s.K, s.E, s.H, I_part,
+                               s.tile_m, bufs.inter_codes, bufs.inter_sf, bufs.rows, len(parts),
+                               bufs.rows.stride(0), bufs.weights, norm_weight, gain_center, eps,
+                               weight_before_norm, bufs.out, stream)
+    else:
+        N.moe_finalize(bufs.rows, len(parts), bufs.rows.stride(0), bufs.exp2perm, bufs.weights,
+                       norm_weight, gain_center, eps, weight_before_norm, s.T, s.K, s.H, bufs.out, stream)
     if check:
         if stream is None:
             torch.cuda.current_stream().synchronize()

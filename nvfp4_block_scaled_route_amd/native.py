@@ -21,13 +21,15 @@ EXPORTS = ("moe_abi_version", "moe_last_error", "moe_rows_max", "moe_meta_layout
            "moe_route", "nvfp4_quant", "moe_route_quant", "moe_pack_w13", "moe_pack_w2",
            "moe_experts_fwd", "moe_finalize", "nvfp4_norm_quant", "moe_router_logits",
            "moe_router_route", "moe_experts_fwd_w4a16", "moe_experts_fwd_bf16",
-           "moe_validate_weights", "moe_workspace_bytes", "moe_experts_fwd_noalloc")
+           "moe_validate_weights", "moe_workspace_bytes", "moe_experts_fwd_noalloc",
+           "moe_experts_finalize")
 
 
 class MoeMetaLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_tiles", "total_rows", "expert_offsets", "expert_counts", "exp2perm", "perm2tok",
-        "tile_expert", "total_ints", "rows_max", "tiles_max", "sync_status", "sub_sync", "subs_max", "perm_counts")]
+        "tile_expert", "total_ints", "rows_max", "tiles_max", "sync_status", "sub_sync", "subs_max", "perm_counts",
+        "tok_sync", "fin_part")]
 
 
 class MoeNvfp4Weights(ctypes.Structure):
@@ -86,6 +88,8 @@ def lib() -> ctypes.CDLL:
         "moe_finalize": (i32, [vp, i64, i32, i64, vp, vp, vp, f32, f32, i32, i32, i32, i32, vp, vp]),
         "moe_experts_fwd_noalloc": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32,
                                           i32, i32, i32, vp, i64, vp]),
+        "moe_experts_finalize": (i32, [vp, vp, vp, ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32, i32, i32,
+                                       i32, vp, vp, vp, i64, i32, i64, vp, vp, f32, f32, i32, vp, vp]),
         "moe_validate_weights": (i32, [ctypes.POINTER(MoeNvfp4Weights), i32, i32, i32, i32]),
         "moe_workspace_bytes": (i64, [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(MoeWorkspaceLayout)]),
     }
@@ -245,6 +249,20 @@ def moe_experts_fwd(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, 
     _check(lib().moe_experts_fwd(_ptr(a_codes), _ptr(a_sf), _ptr(meta), ctypes.byref(ws), T, K,
                                  E_local, H, I, tile_m, _ptr(inter_codes), _ptr(inter_sf),
                                  _ptr(rows), rows.stride(0), _stream(stream)), "moe_experts_fwd")
+
+
+def moe_experts_finalize(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, tile_m,
+                         inter_codes, inter_sf, rows, n_partials, partial_stride, topk_weights, norm_weight,
+                         gain_center, eps, weight_before_norm, out, stream=None) -> None:
+    """rows: the partials' base (partial q at rows + q * partial_stride elements);
+    this call writes partial n_partials - 1 and finalizes into out."""
+    ws = weights.struct()
+    _check(lib().moe_experts_finalize(_ptr(a_codes), _ptr(a_sf), _ptr(meta), ctypes.byref(ws), T, K, E_local,
+                                      H, I, tile_m, _ptr(inter_codes), _ptr(inter_sf), _ptr(rows),
+                                      rows.stride(-2), n_partials, partial_stride, _ptr(topk_weights),
+                                      _ptr(norm_weight), float(gain_center), float(eps),
+                                      int(weight_before_norm), _ptr(out), _stream(stream)),
+           "moe_experts_finalize")
 
 
 def moe_experts_fwd_noalloc(a_codes, a_sf, meta, weights: Weights, T, K, E_local, H, I, tile_m,

@@ -36,6 +36,11 @@ def sync_counters(meta: np.ndarray, L) -> np.ndarray:
     return meta[L.sub_sync:L.sub_sync + 256 * L.subs_max].reshape(-1, 256)[:, :2]
 
 
+def token_counters(meta: np.ndarray, L, T: int) -> np.ndarray:
+    """The arrival counter of every token (moe_experts_finalize's one-launch form)."""
+    return meta[L.tok_sync:L.tok_sync + 32 * T].reshape(-1, 32)[:, 0]
+
+
 def upload_weights(inp: W.Inputs) -> N.Weights:
     w13c, w13s, w2c, w2s = dev(inp.w13_codes), dev(inp.w13_sf), dev(inp.w2_codes), dev(inp.w2_sf)
     w = LY.pack_weights(w13c, w13s, w2c, w2s, dev(inp.g1_alphas), dev(inp.g1_scale_c),
@@ -47,7 +52,7 @@ def upload_weights(inp: W.Inputs) -> N.Weights:
 
 def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | None = None,
               is_padding: np.ndarray | None = None, tp: int = 1, bias: np.ndarray | None = None,
-              fill_rows: int | None = None) -> dict:
+              fill_rows: int | None = None, fused_finalize: bool = False) -> dict:
     wl = inp.wl
     m = wl.tile_m if tile_m is None else tile_m
     if weights is None:
@@ -62,7 +67,7 @@ def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | Non
                  None if bias is None else dev(bias),
                  None if is_padding is None else dev(is_padding.astype(np.uint8)),
                  weights, dev(inp.norm_weight_bf16), wl.gain_center, wl.eps,
-                 bool(wl.weight_before_norm), slices=slices)
+                 bool(wl.weight_before_norm), slices=slices, fused_finalize=fused_finalize)
     torch.cuda.synchronize()
     L = bufs.layout
     meta = host(bufs.meta)
@@ -76,6 +81,7 @@ def run_layer(inp: W.Inputs, weights: N.Weights | None = None, tile_m: int | Non
         perm2tok=meta[L.perm2tok:L.perm2tok + L.rows_max],
         tile_expert=meta[L.tile_expert:L.tile_expert + L.tiles_max],
         sync_status=int(meta[L.sync_status]), sub_sync=sync_counters(meta, L),
+        tok_sync=token_counters(meta, L, wl.T),
         inter_codes=host(bufs.inter_codes), inter_sf=host(bufs.inter_sf),
         rows=host(bufs.rows), out=host(bufs.out))
     return res

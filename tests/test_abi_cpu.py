@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
@@ -42,8 +42,8 @@ def test_rows_max_matches_oracle(T, K, E, m):
     assert lay.rows_max == oracle_rows_max(T, K, E, m) and lay.tiles_max * m == lay.rows_max
     assert lay.subs_max * 16 == lay.rows_max
     fields = [lay.expert_offsets, lay.expert_counts, lay.exp2perm, lay.perm2tok, lay.tile_expert,
-              lay.sub_sync, lay.perm_counts]
-    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max, 256 * lay.subs_max, -(-T * K // 512) * E]
+              lay.sub_sync, lay.tok_sync, lay.perm_counts]
+    sizes = [E + 1, E, T * K, lay.rows_max, lay.tiles_max, 256 * lay.subs_max, 32 * T, -(-T * K // 512) * E]
     assert all(f % 64 == 0 for f in fields)
     for (f, n), nxt in zip(zip(fields, sizes), fields[1:] + [lay.total_ints]):
         assert f + n <= nxt
@@ -233,3 +233,25 @@ def test_noalloc_refusals():
     assert L.moe_experts_fwd_noalloc(None, None, None, ctypes.byref(w), 4, 2, 8, 96, 128, 16, None, 96, None) \
         == N.MOE_EUNSUPPORTED                                               # H % 64
     assert L.moe_experts_fwd_noalloc(None, None, None, None, 4, 2, 8, 256, 128, 16, None, 256, None) == N.MOE_EINVAL
+
+
+def test_experts_finalize_refusals():
+    """moe_experts_finalize: the expert step's checks and the finalize's, before
+    any launch."""
+    L = N.lib()
+    w = N.MoeNvfp4Weights()
+    f = ctypes.c_float
+
+    def call(H=256, I=128, m=16, nparts=1, pstride=0, rows=16, tw=16, out=16, meta=16):
+        return L.moe_experts_finalize(16, 16, meta, ctypes.byref(w), 4, 2, 8, H, I, m, 16, 16, rows, H, nparts,
+                                      pstride, tw, None, f(1.0), f(1e-6), 1, out, None)
+    assert call(H=96) == N.MOE_EUNSUPPORTED
+    assert call(m=24) == N.MOE_EUNSUPPORTED
+    assert call(nparts=17) == N.MOE_EUNSUPPORTED
+    assert call(nparts=0) == N.MOE_EUNSUPPORTED
+    assert call(out=0) == N.MOE_EINVAL
+    assert call(tw=0) == N.MOE_EINVAL
+    assert call(tw=8) == N.MOE_EINVAL                  # alignment
+    assert call(nparts=2, pstride=12) == N.MOE_EINVAL   # partial stride % 8
+    assert call() == N.MOE_EINVAL                      # NULL weight pointers (checked with the expert step)
+    assert L.moe_last_error()

@@ -39,6 +39,24 @@ def test_weight_bytes_per_expert():
     assert ab["other"] == other and ab["total"] == ab["weights"] + other
 
 
+def test_bytes_with_the_finalize_and_slices():
+    """With the finalize in the step, every slice's rows are read once more and
+    the output written; with tp slices the input is read and rows written once
+    a slice, the weights and the intermediate once in total."""
+    wl = W.WORKLOADS["expert_tp8_b32"]
+    counts = np.zeros(wl.E, np.int64)
+    counts[:96] = 2
+    counts[96:112] = 4
+    routes = int(counts.sum())
+    assert routes == wl.T * wl.K
+    a = bench.algorithmic_bytes(wl, counts)
+    f = bench.algorithmic_bytes(wl, counts, finalize=True)
+    assert a["weights"] == f["weights"] == 112 * 27 * wl.I * wl.H // 16
+    assert f["total"] - a["total"] == wl.tp * routes * wl.H * 2 + wl.T * wl.H * 2
+    assert a["other"] == (wl.tp * wl.T * 9 * wl.H // 16 + 2 * routes * 9 * wl.I // 16
+                          + wl.tp * routes * wl.H * 2)
+
+
 def test_matrix_flops_of_the_routed_rows():
     """GEMM1 (2I x H) and GEMM2 (H x I) per route, 2 flops a multiply-add:
     6 R H I; prefill_t4096's 32768 routes give 1.237 TFLOP."""

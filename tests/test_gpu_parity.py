@@ -304,6 +304,7 @@ def _check_sync_words(res):
     are back at zero (the next call on this metadata starts from them)."""
     assert res["sync_status"] == 0
     assert not np.any(res["sub_sync"])
+    assert not np.any(res["tok_sync"])
 
 
 def _compare_requant(res, ref, inp, rows_got, tokens, experts, name, a_codes=None, a_sf=None):
