@@ -390,18 +390,6 @@ __global__ void __launch_bounds__(kThreads) gemm2_wg_kernel(ExpArgs a) {
 // Reset: after its copy each GEMM2 workgroup counts itself on the tile's done
 // counter; the last of the tile's H/128 returns both counters to 0, so the next
 // call on the same metadata starts from 0.
-constexpr uint32_t kSpinMax = 1u << 20;
-
-__device__ __forceinline__ void wait_ready(int32_t* ready, int target, int32_t* status) {
-    for (uint32_t it = 0;; ++it) {
-        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
-        if (it >= kSpinMax) {
-            __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return;
-        }
-        __builtin_amdgcn_s_sleep(8);
-    }
-}
 
 // A GEMM2 unit whose D = KT weight k-tiles are all held in st (I = 256: two
 // output pairs a wave, run one after the other, share the wave's metadata

@@ -74,6 +74,22 @@ __device__ __forceinline__ void lds_copy16_sc1(u32x4 rsrc, uint32_t lds, uint32_
                  :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
 }
 
+// A bounded wait for a counter another workgroup of the same launch adds to
+// (agent-coherent polls, a sleep between them): after kSpinMax polls it gives
+// up and sets the status word to 1, so no wait can hang the launch.
+constexpr uint32_t kSpinMax = 1u << 20;
+
+__device__ __forceinline__ void wait_ready(int32_t* ready, int target, int32_t* status) {
+    for (uint32_t it = 0;; ++it) {
+        if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+        if (it >= kSpinMax) {
+            __hip_atomic_store(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
 // The unit's 16-row tile: expert (-1: no unit) and the lane's row token.
 struct RowTile {
     int e;
@@ -127,6 +143,8 @@ __device__ __forceinline__ void gemm2_epilogue(const ExpArgs& a, const RowTile& 
 // 4-k-tile stages (H % 256 == 0, I % 256 == 0), activation code offsets below
 // 2^31 bytes.
 bool tiled_shape_ok(int T, int H, int I, int tile_m);
+// Both GEMMs in one launch, GEMM2's items waiting on per-block counters (meta's
+// sub_sync) for GEMM1's.
 void launch_tiled(const ExpArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -180,15 +180,22 @@ struct ASrc {
 };
 
 
+// kCoherent: agent-coherent copies (an intermediate other workgroups of the
+// same launch published).
+template <bool kCoherent>
 __device__ __forceinline__ void a_stage_load(ALds& lds, const ASrc& p, int wave, int g) {
     const int buf = g & 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        lds_copy16(p.a, __builtin_amdgcn_readfirstlane(lds_addr(&lds.codes[buf][(32 * q + 8 * wave) * kARowBytes])),
-                   p.a_off[q], (uint32_t)(g * kARowBytes));
-    if (wave < 2)
-        lds_copy16(p.as, __builtin_amdgcn_readfirstlane(lds_addr(&lds.sf[buf][64 * wave * kASfBytes])), p.as_off,
-                   (uint32_t)(g * kASfBytes));
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(&lds.codes[buf][(32 * q + 8 * wave) * kARowBytes]));
+        if (kCoherent) lds_copy16_sc1(p.a, l, p.a_off[q], (uint32_t)(g * kARowBytes));
+        else lds_copy16(p.a, l, p.a_off[q], (uint32_t)(g * kARowBytes));
+    }
+    if (wave < 2) {
+        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(&lds.sf[buf][64 * wave * kASfBytes]));
+        if (kCoherent) lds_copy16_sc1(p.as, l, p.as_off, (uint32_t)(g * kASfBytes));
+        else lds_copy16(p.as, l, p.as_off, (uint32_t)(g * kASfBytes));
+    }
 }
 
 // A fragments of k-tile c of a stage: lane (nn, h) of row tile i reads the 16
@@ -317,6 +324,7 @@ __device__ __forceinline__ float silu_fast(float g) {
 // intermediates col0 + [0, 32)): SwiGLU lane-local in the MFMA layout, then
 // per lane one block: amax, e4m3 scale, 16 codes, 8 code bytes and the scale
 // byte stored when its row has a route (bit r of vmask).
+template <bool kPub>
 __device__ __forceinline__ void swiglu_quant_tile(const floatx16& gacc, const floatx16& uacc, float ga, float uc,
                                                   int lane, uint32_t vmask, const ExpArgs& a, int m0, int col0,
                                                   float* slab) {
@@ -341,8 +349,16 @@ __device__ __forceinline__ void swiglu_quant_tile(const floatx16& gacc, const fl
     if ((vmask >> r) & 1u) {
         const int64_t row = m0 + r;
         const int col = col0 + 16 * (lane & 1);
-        *reinterpret_cast<uint2*>(a.inter_codes + row * (a.I >> 1) + (col >> 1)) = make_uint2(w0, w1);
-        a.inter_sf[row * (a.I >> 4) + (col >> 4)] = (uint8_t)bs.byte;
+        uint8_t* cp = a.inter_codes + row * (a.I >> 1) + (col >> 1);
+        uint8_t* sp = a.inter_sf + row * (a.I >> 4) + (col >> 4);
+        if (kPub) {        // read by GEMM2 workgroups of the same launch: agent-coherent stores
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(cp), (uint64_t)w0 | ((uint64_t)w1 << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sp, (uint8_t)bs.byte, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
+            *sp = (uint8_t)bs.byte;
+        }
     }
 }
 
@@ -371,7 +387,7 @@ __device__ __forceinline__ void bf16_tile(const floatx16& acc, float alpha, int 
 // One wave's block: rows [row0, row0 + 32 RT) of expert e, column block cb
 // (computed but not stored when store is false: a column group past the end).
 // vmask[i]: bit r is set when row 32 i + r of the block has a route.
-template <int MODE, int RT>
+template <int MODE, int RT, bool kPub>
 __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASrc& ap, int e, int row0, int cb,
                                           bool store, int wave, int lane, const uint32_t (&vmask)[4]) {
     const int h = lane >> 5, nn = lane & 31, n = lane & 15, hh = (lane >> 4) & 1;
@@ -432,8 +448,8 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
     // worth
     constexpr int kAfterCopy = 4 * BRaw<MODE>::kLoads < 63 ? 4 * BRaw<MODE>::kLoads : 63;
 
-    a_stage_load(lds, ap, wave, 0);
-    a_stage_load(lds, ap, wave, min(1, NS - 1));
+    a_stage_load<kPub && MODE == 2>(lds, ap, wave, 0);
+    a_stage_load<kPub && MODE == 2>(lds, ap, wave, min(1, NS - 1));
     BRaw<MODE> ring[2];
     b_load(ring[0], p, 0);
     b_load(ring[1], p, min(1, KT - 1));
@@ -487,7 +503,7 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
                 // barrier) issues with the weight loads it will be waited for
                 // with: vmcnt drains in order, so a copy issued earlier would
                 // hold up the next wait for the weights by a full memory latency
-                if (cc == 2) a_stage_load(lds, ap, wave, min(g + 2, NS - 1));
+                if (cc == 2) a_stage_load<kPub && MODE == 2>(lds, ap, wave, min(g + 2, NS - 1));
                 b_load_half<MODE, 1>(ring[d], p, cn);
                 a_read(ar[d], lds, (cn / kStage) & 1, cn % kStage, nn, h);
                 step_mfma(f[1], acc);
@@ -506,8 +522,8 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
     if (MODE == 1) {
         const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
 #define MOE_EPI1(i, t)                                                                          \
-    if (RT > i) swiglu_quant_tile(acc[RT > i ? i : 0][2 * t], acc[RT > i ? i : 0][2 * t + 1], ga, uc, lane, \
-                                  vmask[i], a, row0 + 32 * i, 64 * cb + 32 * t, lds.slab[wave][t])
+    if (RT > i) swiglu_quant_tile<kPub>(acc[RT > i ? i : 0][2 * t], acc[RT > i ? i : 0][2 * t + 1], ga, uc, lane, \
+                                        vmask[i], a, row0 + 32 * i, 64 * cb + 32 * t, lds.slab[wave][t])
         MOE_EPI1(0, 0); MOE_EPI1(0, 1); MOE_EPI1(1, 0); MOE_EPI1(1, 1);
         MOE_EPI1(2, 0); MOE_EPI1(2, 1); MOE_EPI1(3, 0); MOE_EPI1(3, 1);
 #undef MOE_EPI1
@@ -524,9 +540,15 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
     }
 }
 
-template <int MODE>   // 1: GEMM1 + SwiGLU + requant, 2: GEMM2
-__global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, int ncb) {
-    __shared__ ALds lds;
+// One work item of GEMM MODE (1: GEMM1 + SwiGLU + requant, 2: GEMM2) for
+// workgroup `bid` of that GEMM's grid. kPub: both GEMMs run in one launch
+// (tiled_fused_kernel): GEMM1 publishes its part of a row block's intermediate
+// with agent-coherent stores and counts itself on the block's ready counter;
+// GEMM2 waits for all GEMM1 items of its block, copies the intermediate with
+// agent-coherent loads, and the block's last GEMM2 item returns the counters
+// to 0.
+template <int MODE, bool kPub>
+__device__ __forceinline__ void tiled_item(const ExpArgs& a, ALds& lds, uint32_t bid, int ncg, int ncb, int ncg1) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -534,9 +556,9 @@ __global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, 
     // equal contiguous chunks, chunk x on XCD x
     const int items = a.meta[a.L.num_tiles] * (a.tile_m / kBlockRows) * ncg;
     const int per_xcd = (items + kXcds - 1) / kXcds;
-    const int slot = (int)(blockIdx.x / kXcds);
+    const int slot = (int)(bid / kXcds);
     if (slot >= per_xcd) return;
-    const int item = (int)(blockIdx.x % kXcds) * per_xcd + slot;
+    const int item = (int)(bid % kXcds) * per_xcd + slot;
     if (item >= items) return;
     const int bx = item / ncg, cg = item % ncg;
     const int row0 = bx * kBlockRows;
@@ -586,13 +608,43 @@ __global__ void __launch_bounds__(64 * kWaves) tiled_kernel(ExpArgs a, int ncg, 
         }
     }
 
-    switch (rt) {
-        case 1: run_block<MODE, 1>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        case 2: run_block<MODE, 2>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        case 3: run_block<MODE, 3>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        case 4: run_block<MODE, 4>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        default: break;
+    if (rt == 0) return;                                  // uniform: a block of padding only
+    // the block's two counters: meta's sub_sync of its first 16-row tile
+    if (kPub && MODE == 2) {
+        if (threadIdx.x == 0) wait_ready(a.sync + (int64_t)kSubSyncStride * (bx * (kBlockRows / 16)), ncg1, a.status);
+        __syncthreads();
     }
+    switch (rt) {
+        case 1: run_block<MODE, 1, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 2: run_block<MODE, 2, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 3: run_block<MODE, 3, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        default: run_block<MODE, 4, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+    }
+    if (kPub) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores (GEMM1) or copies (GEMM2) are done
+        __syncthreads();
+        int32_t* cnt = a.sync + (int64_t)kSubSyncStride * (__builtin_amdgcn_readfirstlane(bx) * (kBlockRows / 16));
+        if (threadIdx.x == 0) {
+            if (MODE == 1) {
+                __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else if (__hip_atomic_fetch_add(cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ncg - 1) {
+                __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// Both GEMMs in one launch: GEMM1's workgroups [0, g1_blocks) (a multiple of
+// 8, so that GEMM2's item mapping keeps its XCD), then GEMM2's. Workgroups are
+// dispatched in order on each XCD, so a GEMM2 item only waits for GEMM1 items
+// that were dispatched before it; GEMM2 items of the first blocks start while
+// GEMM1's last items run.
+__global__ void __launch_bounds__(64 * kWaves) tiled_fused_kernel(ExpArgs a, int ncg1, int ncb1, int ncg2, int ncb2,
+                                                                  uint32_t g1_blocks) {
+    __shared__ ALds lds;
+    if (blockIdx.x < g1_blocks) tiled_item<1, true>(a, lds, blockIdx.x, ncg1, ncb1, ncg1);
+    else tiled_item<2, true>(a, lds, blockIdx.x - g1_blocks, ncg2, ncb2, ncg1);
 }
 
 bool tiled_shape_ok(int T, int H, int I, int tile_m) {
@@ -606,11 +658,12 @@ void launch_tiled(const ExpArgs& a, hipStream_t s) {
     // grids cover every row block that routing can fill; the kernels take the
     // routed ones from the metadata
     const int nx = (int)(a.L.rows_max / kBlockRows);
-    const int ncb1 = a.I / 64, ncb2 = a.H / 128;
+    const int ncb1 = a.I / 64, ncb2 = a.H / 128;   // column blocks of one wave
     const int ncg1 = (ncb1 + kWaves - 1) / kWaves, ncg2 = (ncb2 + kWaves - 1) / kWaves;
-    auto grid = [](int64_t items) { return dim3((unsigned)((items + kXcds - 1) / kXcds * kXcds)); };
-    hipLaunchKernelGGL(tiled_kernel<1>, grid((int64_t)nx * ncg1), dim3(64 * kWaves), 0, s, a, ncg1, ncb1);
-    hipLaunchKernelGGL(tiled_kernel<2>, grid((int64_t)nx * ncg2), dim3(64 * kWaves), 0, s, a, ncg2, ncb2);
+    auto grid = [](int64_t items) { return (items + kXcds - 1) / kXcds * kXcds; };
+    const int64_t g1 = grid((int64_t)nx * ncg1), g2 = grid((int64_t)nx * ncg2);
+    hipLaunchKernelGGL(tiled_fused_kernel, dim3((unsigned)(g1 + g2)), dim3(64 * kWaves), 0, s, a, ncg1, ncb1, ncg2,
+                       ncb2, (uint32_t)g1);
 }
 
 }  // namespace moe
