@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the headline workload in the oracle's CPU-baseline sample (0 disables)")
     ap.add_argument("--rotate-bytes", type=float, default=1.0e9)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the layer step and the expert step, none of the neighbouring calls "
+                         "(for counter runs, whose per-dispatch figures then hold only the step's kernels)")
     return ap.parse_args()
 
 
@@ -389,8 +392,8 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
     if mfma_bound(wl):
         flops = algorithmic_flops(wl, counts)
         tflops = flops / (k_ms * 1e-3) / 1e12
-        rec["roofline"] = {"bound": "mfma", "kernel": "moe_experts_fwd (tiled_kernel<1>: GEMM1+SwiGLU+requant, "
-                                                      "tiled_kernel<2>: GEMM2)",
+        rec["roofline"] = {"bound": "mfma", "kernel": "moe_experts_fwd (tiled_fused_kernel: GEMM1+SwiGLU+requant "
+                                                      "and GEMM2 in one launch)",
                            "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": tflops / MFMA_F16_PEAK_TFLOPS, "traffic": traffic, "traffic_unit": unit_t,
                            "algorithmic_flops": flops, "algorithmic_bytes": ab["total"], "hbm_gbs": achieved,
@@ -404,7 +407,7 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
                            "algorithmic_bytes": ab["total"], "weight_bytes": ab["weights"],
                            "experts_touched": ab["touched"], "kernel_ms": k_ms,
                            "kernel_ms_isolated": k_ms_isolated}
-    if not mfma_bound(wl):
+    if extras and not mfma_bound(wl):
         # the expert step with the finalize in its launch (moe_experts_finalize),
         # against the expert step followed by moe_finalize, back to back
         def with_fin(s_):
@@ -449,7 +452,7 @@ def main():
     from nvfp4_block_scaled_route_amd import workloads as W
 
     N.lib()
-    head, inp = measure(N, LY, W, args.workload, args.steps, args.warmup, args.rotate_bytes, True)
+    head, inp = measure(N, LY, W, args.workload, args.steps, args.warmup, args.rotate_bytes, not args.no_extras)
     out = {
         "metric": "routed rows/s per MoE layer; HBM GB/s (decode) & MFMA util (prefill) vs peak",
         "value": head["value"],
@@ -467,7 +470,7 @@ def main():
         out["workloads"] = {}
         for name in subs:
             rec, _ = measure(N, LY, W, name, max(args.steps, args.sub_steps), max(args.warmup, 20),
-                             args.rotate_bytes, name != "expert_tp8_b32")
+                             args.rotate_bytes, name != "expert_tp8_b32" and not args.no_extras)
             out["workloads"][name] = rec
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

@@ -4,16 +4,18 @@ Reads four counter collections (rocprofv3 --pmc ... --output-format csv), each
 counter in a run of its own:
 
     <dir>/FETCH_SIZE, <dir>/WRITE_SIZE              python bench.py --workload W ...
-    <dir>/copy_FETCH_SIZE, <dir>/copy_WRITE_SIZE    copy_calibration.py --mib M --reps R
+    <copy dir>/copy_FETCH_SIZE, <copy dir>/copy_WRITE_SIZE
+                                                    copy_calibration.py --mib M --reps R
 
 scales the expert kernels' per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) by what
-the same counters read for a device copy of known size, and writes
+the same counters read for a device copy of known size (times the launches of
+one layer step: the expert-TP slices each launch the step), and writes
 profiles/experts_<W>_traffic.json (with the SHA-256 of the kernel sources, so
 that bench.py reports the figure only while they are unchanged) and prints a
 markdown table.
 
     python -m nvfp4_block_scaled_route_amd.traffic_summary --dir <rocprofv3 output dir> \\
-        --workload prefill_t4096 --copy-mib 256
+        --workload prefill_t4096 --copy-mib 256 [--copy-dir <dir>] [--launches-per-step 8]
 """
 from __future__ import annotations
 
@@ -29,11 +31,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = ["nvfp4_block_scaled_route_amd/csrc/experts.hip",
            "nvfp4_block_scaled_route_amd/csrc/experts_tiled.hip",
            "nvfp4_block_scaled_route_amd/csrc/experts.hpp",
+           "nvfp4_block_scaled_route_amd/csrc/finalize.hpp",
            "nvfp4_block_scaled_route_amd/csrc/common.hpp"]
 # the kernels moe_experts_fwd launches (the other expert variants the bench
 # times beside it, W4A16 and BF16, are not part of the step)
 EXPERT_KERNELS = ("gemm1_kernel", "gemm2_kernel", "gemm1_wg_kernel", "gemm2_wg_kernel", "experts_fused_kernel",
-                  "tiled_kernel")
+                  "tiled_fused_kernel")
 
 
 def is_expert_kernel(name: str) -> bool:
@@ -61,12 +64,17 @@ def main():
     ap.add_argument("--dir", required=True)
     ap.add_argument("--workload", required=True)
     ap.add_argument("--copy-mib", type=float, required=True)
+    ap.add_argument("--copy-dir", default=None,
+                    help="where copy_FETCH_SIZE and copy_WRITE_SIZE are (default: --dir)")
+    ap.add_argument("--launches-per-step", type=int, default=1,
+                    help="expert-step launches per layer step (the expert-TP slices)")
     args = ap.parse_args()
 
     fetch = per_dispatch(os.path.join(args.dir, "FETCH_SIZE"), "FETCH_SIZE")
     write = per_dispatch(os.path.join(args.dir, "WRITE_SIZE"), "WRITE_SIZE")
-    cfetch = per_dispatch(os.path.join(args.dir, "copy_FETCH_SIZE"), "FETCH_SIZE")
-    cwrite = per_dispatch(os.path.join(args.dir, "copy_WRITE_SIZE"), "WRITE_SIZE")
+    cdir = args.copy_dir or args.dir
+    cfetch = per_dispatch(os.path.join(cdir, "copy_FETCH_SIZE"), "FETCH_SIZE")
+    cwrite = per_dispatch(os.path.join(cdir, "copy_WRITE_SIZE"), "WRITE_SIZE")
     copy_kib = args.copy_mib * 1024.0
     # the copy kernel is the one whose counters are largest
     fetch_factor = max(cfetch.values()) / copy_kib
@@ -75,7 +83,7 @@ def main():
     kernels = sorted(k for k in fetch if is_expert_kernel(k))
     rows, total = [], 0.0
     rec = {"workload": args.workload, "kernels": kernels, "fetch_factor": fetch_factor,
-           "write_factor": write_factor}
+           "write_factor": write_factor, "launches_per_step": args.launches_per_step}
     for k in kernels:
         rb = fetch[k] / fetch_factor * 1024.0
         wb = write.get(k, 0.0) / write_factor * 1024.0
@@ -83,7 +91,8 @@ def main():
         total += rb + wb
     rec["per_kernel"] = [{"kernel": k, "fetch_kib": f, "write_kib": w, "read_mb": r, "write_mb": x}
                          for k, f, w, r, x in rows]
-    rec["traffic_bytes"] = total
+    rec["traffic_bytes_per_launch"] = total
+    rec["traffic_bytes"] = total * args.launches_per_step
     h = hashlib.sha256()
     for src in SOURCES:
         with open(os.path.join(ROOT, src), "rb") as f:
@@ -99,7 +108,8 @@ def main():
     print("|---|---|---|---|---|")
     for k, f, w, r, x in rows:
         print(f"| `{k}` | {f:.1f} | {w:.1f} | {r:.2f} | {x:.3f} |")
-    print(f"traffic per expert step: {total / 1e6:.2f} MB -> {out}")
+    print(f"traffic per launch: {total / 1e6:.2f} MB; per step ({args.launches_per_step} launches): "
+          f"{total * args.launches_per_step / 1e6:.2f} MB -> {out}")
 
 
 if __name__ == "__main__":
