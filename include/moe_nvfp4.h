@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 6
+#define MOE_NVFP4_ABI_VERSION 7
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -101,6 +101,10 @@ int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
  *                                routes more than 32 tokens: per chunk of 512
  *                                routes, the routes of each expert, then the
  *                                chunk's first row in each expert
+ *   queue           [16]         (inside the first 64 words) the work queues of
+ *                                moe_experts_fwd's register-tiled form: 8 per-XCD
+ *                                item counters and an exit counter, set to 0 by
+ *                                moe_route; that form leaves them at 0 again
  * Order (the counting-sort reading of the flashinfer_ops page's metadata,
  * "FlashInferOps.slot"): experts ascending, routes of one expert in ascending
  * t*K+k, each expert's rows padded to a multiple of m. */
@@ -121,6 +125,7 @@ typedef struct moe_meta_layout {
     int64_t perm_counts;
     int64_t tok_sync;
     int64_t fin_part;
+    int64_t queue;
 } moe_meta_layout;
 
 int moe_meta_layout_get(int T, int K, int E_local, int tile_m, moe_meta_layout* out);

@@ -39,6 +39,7 @@ moe_meta_layout meta_layout(int T, int K, int E_local, int tile_m) {
     L.perm2tok = off;       off += align64(L.rows_max);
     L.tile_expert = off;    off += align64(L.tiles_max);
     L.sync_status = 2;
+    L.queue = kQueueOffset;
     L.subs_max = L.rows_max / 16;
     L.sub_sync = off;       off += align64(kSubSyncStride * L.subs_max);
     L.tok_sync = off;       off += align64(kTokSyncStride * (int64_t)T);

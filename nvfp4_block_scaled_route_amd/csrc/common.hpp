@@ -36,6 +36,11 @@ constexpr int kSubSyncStride = 256;
 constexpr int kTokSyncStride = 32;
 // words a token's finalize exchanges between its workgroups: 16 waves x 8 routes
 constexpr int kFinPartWords = 128;
+// the tiled expert step's work queues in the metadata header: words
+// [kQueueOffset, kQueueOffset + kXcds) count the items taken from each XCD's
+// queue, word kQueueOffset + kXcds the workgroups that have finished
+constexpr int kQueueOffset = 16;
+constexpr int kQueueWords = 16;
 // converted weight layout: code and scale bytes per row pair and k-tile
 constexpr int kSlotBytes = 1024, kSlotSfBytes = 128;
 

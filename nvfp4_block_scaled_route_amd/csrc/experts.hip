@@ -760,6 +760,7 @@ static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* 
     args.rows_stride = rows_stride;
     args.sync = meta + args.L.sub_sync;
     args.status = meta + args.L.sync_status;
+    args.queue = meta + args.L.queue;
     if (args.L.rows_max == 0) return MOE_OK;
     const int64_t subs = args.L.rows_max / 16;             // 16-row tiles, routed or not
     const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
@@ -777,7 +778,7 @@ static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* 
                             fin->T, fin->K, fin->H, fin->out, stream);
     };
     if (tiled_shape_ok(T, H, I, tile_m) && (int64_t)T * K >= (int64_t)32 * E_local) {
-        launch_tiled(args, s);
+        if (int rc = launch_tiled(args, s)) return rc;
         return finalize_after(check_launch("moe_experts_fwd (tiled)"));
     }
     // Workgroups of four units sharing one LDS copy of their tile's activation

@@ -19,6 +19,7 @@ struct ExpArgs {
     int64_t rows_stride;
     int32_t* sync;       // meta's sub_sync: per 16-row tile (kSubSyncStride apart), GEMM1 workgroups done, GEMM2 copies done
     int32_t* status;     // meta's sync_status
+    int32_t* queue;      // meta's queue words (the register-tiled form's work queues)
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -143,8 +144,9 @@ __device__ __forceinline__ void gemm2_epilogue(const ExpArgs& a, const RowTile& 
 // 4-k-tile stages (H % 256 == 0, I % 256 == 0), activation code offsets below
 // 2^31 bytes.
 bool tiled_shape_ok(int T, int H, int I, int tile_m);
-// Both GEMMs in one launch, GEMM2's items waiting on per-block counters (meta's
-// sub_sync) for GEMM1's.
-void launch_tiled(const ExpArgs& a, hipStream_t s);
+// Both GEMMs in one launch of persistent workgroups taking work items from
+// per-XCD queues (meta's queue words), GEMM2's items waiting on per-block
+// counters (meta's sub_sync) for GEMM1's. Returns MOE_OK or an error code.
+int launch_tiled(const ExpArgs& a, hipStream_t s);
 
 }  // namespace moe

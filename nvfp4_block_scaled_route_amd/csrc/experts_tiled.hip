@@ -34,11 +34,16 @@
 //     k-tile could use the rest.)
 //   * row tiles with no route are skipped (an expert's rows are padded to the
 //     block size): a block runs with 1 to 4 row tiles.
-// Workgroups are mapped to the routed row blocks only (their count is read from
-// the routing metadata), split into 8 equal contiguous chunks, one per XCD
-// (workgroups are dealt to the 8 XCDs round robin), row block major: the
-// column groups of a row block, and the row blocks of one expert, run on the
-// same XCD at about the same time and share the A rows and the weights in its L2.
+// One persistent workgroup per CU takes work items -- (routed row block,
+// column group) of GEMM1, then of GEMM2 -- from 8 queues, one per XCD: the
+// routed row blocks (their count is read from the routing metadata) are split
+// into 8 equal contiguous chunks, and queue x holds chunk x's GEMM1 items, row
+// block major, then its GEMM2 items. A workgroup takes from its own XCD's queue
+// (workgroups are dealt to the 8 XCDs round robin), so the column groups of a
+// row block, and the row blocks of one expert, run on the same XCD at about
+// the same time and share the A rows and the weights in its L2; when that queue
+// is empty it takes from the others, so that no XCD idles while another still
+// has work (items differ in length: a block runs 1 to 4 row tiles).
 //
 // GEMM1's columns are arranged so that a lane holds the gate and the up value of
 // the same intermediate in two accumulators (column tiles 2t and 2t + 1 take the
@@ -540,30 +545,80 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
     }
 }
 
-// One work item of GEMM MODE (1: GEMM1 + SwiGLU + requant, 2: GEMM2) for
-// workgroup `bid` of that GEMM's grid. kPub: both GEMMs run in one launch
-// (tiled_fused_kernel): GEMM1 publishes its part of a row block's intermediate
-// with agent-coherent stores and counts itself on the block's ready counter;
-// GEMM2 waits for all GEMM1 items of its block, copies the intermediate with
-// agent-coherent loads, and the block's last GEMM2 item returns the counters
-// to 0.
-template <int MODE, bool kPub>
-__device__ __forceinline__ void tiled_item(const ExpArgs& a, ALds& lds, uint32_t bid, int ncg, int ncb, int ncg1) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// The work queues (meta's queue words): queue x holds the GEMM1 items of the
+// row blocks [x bpx, (x + 1) bpx), ncg1 a block, then their GEMM2 items.
+struct Queues {
+    int32_t* q;             // items taken from each queue; q[kXcds]: workgroups finished
+    int nblocks, bpx, ncg1, ncg2, home;
+};
 
-    // work items: (routed row block, column group), row block major, in 8
-    // equal contiguous chunks, chunk x on XCD x
-    const int items = a.meta[a.L.num_tiles] * (a.tile_m / kBlockRows) * ncg;
-    const int per_xcd = (items + kXcds - 1) / kXcds;
-    const int slot = (int)(bid / kXcds);
-    if (slot >= per_xcd) return;
-    const int item = (int)(bid % kXcds) * per_xcd + slot;
-    if (item >= items) return;
-    const int bx = item / ncg, cg = item % ncg;
+__device__ __forceinline__ int queue_blocks(const Queues& Q, int x) {
+    return min(max(Q.nblocks - x * Q.bpx, 0), Q.bpx);
+}
+
+// Thread 0: the next item, x << 24 | its position in queue x; -1 when every
+// queue is empty. From the home queue while it lasts; then from the queue
+// with the most items left, by one read of all the counters (8 loads in
+// flight at once) and an increment of the chosen one, again while a chosen
+// queue turns out to be empty. *done (in LDS, so that no register stays live
+// across items) holds the queues this workgroup found empty. A counter passes
+// its item count by at most one per workgroup; the last workgroup out resets
+// them.
+__device__ __forceinline__ int take_item(const Queues& Q, uint32_t* done) {
+    uint32_t d = *done;
+    int item = -1;
+    const int ni = Q.ncg1 + Q.ncg2;
+    if (!((d >> Q.home) & 1u)) {
+        const int v = __hip_atomic_fetch_add(Q.q + Q.home, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v < queue_blocks(Q, Q.home) * ni) item = (Q.home << 24) | v;
+        else d |= 1u << Q.home;
+    }
+    while (item < 0 && d != (1u << kXcds) - 1) {
+        int left[kXcds];
+#pragma unroll
+        for (int x = 0; x < kXcds; ++x)
+            left[x] = ((d >> x) & 1u) ? 0
+                      : queue_blocks(Q, x) * ni - __hip_atomic_load(Q.q + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int best = -1, most = 0;
+#pragma unroll
+        for (int x = 0; x < kXcds; ++x) {
+            if (left[x] > most) { most = left[x]; best = x; }
+            if (left[x] <= 0) d |= 1u << x;
+        }
+        if (best < 0) break;
+        const int v = __hip_atomic_fetch_add(Q.q + best, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v < queue_blocks(Q, best) * ni) item = (best << 24) | v;
+        else d |= 1u << best;
+    }
+    *done = d;
+    return item;
+}
+
+// One work item of GEMM MODE (1: GEMM1 + SwiGLU + requant, 2: GEMM2): row
+// block bx, column group cg. GEMM1 publishes its part of a row block's
+// intermediate with agent-coherent stores and counts itself on the block's
+// ready counter; GEMM2 waits for all GEMM1 items of its block, copies the
+// intermediate with agent-coherent loads, and the block's last GEMM2 item
+// returns the counters to 0. Thread 0 takes the workgroup's next item into
+// *s_next as soon as this one waits for nothing more (a GEMM1 item at once, a
+// GEMM2 item once its block's intermediate is ready): a workgroup then never
+// holds an item that another one waits for while it waits itself.
+template <int MODE>
+__device__ __forceinline__ void tiled_item(const ExpArgs& a, ALds& lds, int bx, int cg, int ncg, int ncb, int ncg1,
+                                           const Queues& Q, uint32_t* done, int* s_next) {
+    // the lane index through an empty asm: the per-lane offsets derived from it
+    // are recomputed for every item rather than kept live across the item loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (MODE == 1 && threadIdx.x == 0) *s_next = take_item(Q, done);
+
     const int row0 = bx * kBlockRows;
     const int e = a.meta[a.L.tile_expert + row0 / a.tile_m];
-    if (e < 0 || e >= a.E_local) return;                     // uniform over the workgroup
+    if (e < 0 || e >= a.E_local) {                            // uniform over the workgroup
+        if (MODE == 2 && threadIdx.x == 0) *s_next = take_item(Q, done);
+        return;
+    }
     int cb = cg * kWaves + wave;
     const bool store = cb < ncb;
     cb = min(cb, ncb - 1);
@@ -608,43 +663,85 @@ __device__ __forceinline__ void tiled_item(const ExpArgs& a, ALds& lds, uint32_t
         }
     }
 
-    if (rt == 0) return;                                  // uniform: a block of padding only
+    if (rt == 0) {                                        // uniform: a block of padding only
+        if (MODE == 2 && threadIdx.x == 0) *s_next = take_item(Q, done);
+        return;
+    }
     // the block's two counters: meta's sub_sync of its first 16-row tile
-    if (kPub && MODE == 2) {
-        if (threadIdx.x == 0) wait_ready(a.sync + (int64_t)kSubSyncStride * (bx * (kBlockRows / 16)), ncg1, a.status);
+    if (MODE == 2) {
+        if (threadIdx.x == 0) {
+            wait_ready(a.sync + (int64_t)kSubSyncStride * (bx * (kBlockRows / 16)), ncg1, a.status);
+            *s_next = take_item(Q, done);
+        }
         __syncthreads();
     }
     switch (rt) {
-        case 1: run_block<MODE, 1, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        case 2: run_block<MODE, 2, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        case 3: run_block<MODE, 3, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
-        default: run_block<MODE, 4, kPub>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 1: run_block<MODE, 1, true>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 2: run_block<MODE, 2, true>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        case 3: run_block<MODE, 3, true>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
+        default: run_block<MODE, 4, true>(a, lds, ap, e, row0, cb, store, wave, lane, vmask); break;
     }
-    if (kPub) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores (GEMM1) or copies (GEMM2) are done
-        __syncthreads();
-        int32_t* cnt = a.sync + (int64_t)kSubSyncStride * (__builtin_amdgcn_readfirstlane(bx) * (kBlockRows / 16));
-        if (threadIdx.x == 0) {
-            if (MODE == 1) {
-                __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else if (__hip_atomic_fetch_add(cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ncg - 1) {
-                __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores (GEMM1) or copies (GEMM2) are done
+    __syncthreads();
+    int32_t* cnt = a.sync + (int64_t)kSubSyncStride * (bx * (kBlockRows / 16));
+    if (threadIdx.x == 0) {
+        if (MODE == 1) {
+            __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (__hip_atomic_fetch_add(cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ncg - 1) {
+            __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-// Both GEMMs in one launch: GEMM1's workgroups [0, g1_blocks) (a multiple of
-// 8, so that GEMM2's item mapping keeps its XCD), then GEMM2's. Workgroups are
-// dispatched in order on each XCD, so a GEMM2 item only waits for GEMM1 items
-// that were dispatched before it; GEMM2 items of the first blocks start while
-// GEMM1's last items run.
-__global__ void __launch_bounds__(64 * kWaves) tiled_fused_kernel(ExpArgs a, int ncg1, int ncb1, int ncg2, int ncb2,
-                                                                  uint32_t g1_blocks) {
+// A pointer into the kernel argument segment (constant address space: its
+// loads are scalar).
+template <typename T>
+using KernArg = const T __attribute__((address_space(4)))*;
+
+// Both GEMMs in one launch, one persistent workgroup per CU looping over the
+// queues' items. A GEMM2 item only waits for GEMM1 items that running
+// workgroups have taken (a queue yields all its GEMM1 items before any GEMM2
+// item, and a workgroup holds a taken item only while its current one waits
+// for nothing), so every wait ends. The last workgroup out returns the queue
+// counters to 0 for the next call on the same routing.
+__global__ void __launch_bounds__(64 * kWaves) tiled_fused_kernel(ExpArgs a, int ncg1, int ncb1, int ncg2, int ncb2) {
     __shared__ ALds lds;
-    if (blockIdx.x < g1_blocks) tiled_item<1, true>(a, lds, blockIdx.x, ncg1, ncb1, ncg1);
-    else tiled_item<2, true>(a, lds, blockIdx.x - g1_blocks, ncg2, ncb2, ncg1);
+    __shared__ int s_next;
+    __shared__ uint32_t s_done;
+    Queues Q;
+    Q.q = a.queue;
+    Q.nblocks = __builtin_amdgcn_readfirstlane(a.meta[a.L.num_tiles]) * (a.tile_m / kBlockRows);
+    Q.bpx = (Q.nblocks + kXcds - 1) / kXcds;
+    Q.ncg1 = ncg1;
+    Q.ncg2 = ncg2;
+    Q.home = (int)(blockIdx.x & (kXcds - 1));
+    if (threadIdx.x == 0) {
+        s_done = 0;
+        s_next = take_item(Q, &s_done);
+    }
+    __syncthreads();
+    int it = __builtin_amdgcn_readfirstlane(s_next);
+    while (it >= 0) {
+        __syncthreads();                                  // every thread has read s_next
+        // the arguments are read again from the kernel argument segment for
+        // every item (an empty asm hides the pointer's value): left to
+        // itself the compiler keeps every field live in registers across the
+        // loop, which spills the k-loop's registers
+        KernArg<ExpArgs> pa = (KernArg<ExpArgs>)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(pa));
+        const ExpArgs& ai = *(const ExpArgs*)pa;
+        const int x = it >> 24, v = it & 0xFFFFFF;
+        const int n1 = queue_blocks(Q, x) * ncg1, b0 = x * Q.bpx;
+        if (v < n1) tiled_item<1>(ai, lds, b0 + v / ncg1, v % ncg1, ncg1, ncb1, ncg1, Q, &s_done, &s_next);
+        else tiled_item<2>(ai, lds, b0 + (v - n1) / ncg2, (v - n1) % ncg2, ncg2, ncb2, ncg1, Q, &s_done, &s_next);
+        __syncthreads();
+        it = __builtin_amdgcn_readfirstlane(s_next);
+    }
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(Q.q + kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+        for (int y = 0; y <= kXcds; ++y) __hip_atomic_store(Q.q + y, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 bool tiled_shape_ok(int T, int H, int I, int tile_m) {
@@ -654,16 +751,23 @@ bool tiled_shape_ok(int T, int H, int I, int tile_m) {
            (int64_t)T * (H / 2) < ((int64_t)1 << 31);
 }
 
-void launch_tiled(const ExpArgs& a, hipStream_t s) {
-    // grids cover every row block that routing can fill; the kernels take the
-    // routed ones from the metadata
+int launch_tiled(const ExpArgs& a, hipStream_t s) {
+    // the routed row blocks are read from the metadata on the device; the
+    // queues' item indices are 24-bit
     const int nx = (int)(a.L.rows_max / kBlockRows);
     const int ncb1 = a.I / 64, ncb2 = a.H / 128;   // column blocks of one wave
     const int ncg1 = (ncb1 + kWaves - 1) / kWaves, ncg2 = (ncb2 + kWaves - 1) / kWaves;
-    auto grid = [](int64_t items) { return (items + kXcds - 1) / kXcds * kXcds; };
-    const int64_t g1 = grid((int64_t)nx * ncg1), g2 = grid((int64_t)nx * ncg2);
-    hipLaunchKernelGGL(tiled_fused_kernel, dim3((unsigned)(g1 + g2)), dim3(64 * kWaves), 0, s, a, ncg1, ncb1, ncg2,
-                       ncb2, (uint32_t)g1);
+    if ((int64_t)((nx + kXcds - 1) / kXcds) * (ncg1 + ncg2) >= (1 << 24))
+        return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many row blocks for the work queues");
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(MOE_ELAUNCH, "moe_experts_fwd: cannot read the device's compute unit count");
+    // one workgroup per CU (a workgroup takes a whole CU's registers), a
+    // multiple of the 8 XCDs
+    const int grid = (cus + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(tiled_fused_kernel, dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a, ncg1, ncb1, ncg2, ncb2);
+    return MOE_OK;
 }
 
 }  // namespace moe

@@ -228,14 +228,16 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e) {
 }
 
 
-// The expert step's sync words start at zero: its status and the two counters
-// of every 16-row tile (moe_experts_fwd's one-launch form).
+// The expert step's sync words start at zero: its status, the two counters
+// of every 16-row tile (moe_experts_fwd's one-launch form), the tiled form's
+// work queues and the per-token counters of the finalize in the launch.
 __device__ __forceinline__ void clear_sync(const RouteArgs& a, int i, int step) {
     int32_t* sync = a.meta + a.L.sub_sync;
     for (int64_t x = i; x < 2 * a.L.subs_max; x += step) sync[(x >> 1) * kSubSyncStride + (x & 1)] = 0;
     int32_t* tok = a.meta + a.L.tok_sync;
     for (int64_t x = i; x < 3 * a.T; x += step) tok[(x / 3) * kTokSyncStride + x % 3] = 0;
     if (i == 0) a.meta[a.L.sync_status] = 0;
+    if (i < kQueueWords) a.meta[a.L.queue + i] = 0;
 }
 
 // The permutation metadata for up to 512 routes, by one workgroup. Wave 0
@@ -597,6 +599,7 @@ __global__ void __launch_bounds__(kRouteThreads) perm_scatter_kernel(RouteArgs a
         tok[x * kTokSyncStride + 2] = 0;
     }
     if (blockIdx.x == 0 && tid == 0) a.meta[a.L.sync_status] = 0;
+    if (blockIdx.x == 0 && tid < kQueueWords) a.meta[a.L.queue + tid] = 0;
 }
 
 static size_t topk_lds_bytes(int E, int K) {

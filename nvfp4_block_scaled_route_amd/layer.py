@@ -118,13 +118,15 @@ class Buffers:
 
     def check_sync(self) -> None:
         """Raise if an expert step's bounded wait gave up (meta[sync_status] != 0:
-        its rows are not valid) or left a tile or token counter non-zero. Reads the
-        metadata back, so the caller synchronizes the stream first."""
+        its rows are not valid) or left a tile, token or work-queue counter
+        non-zero. Reads the metadata back, so the caller synchronizes the stream
+        first."""
         L = self.layout
         status = int(self.meta[L.sync_status].item())
         counters = self.meta[L.sub_sync:L.sub_sync + 256 * L.subs_max].view(-1, 256)[:, :2]
         tok = self.meta[L.tok_sync:L.tok_sync + 32 * self.shape.T].view(-1, 32)[:, 0]
-        bad = int((counters != 0).sum().item()) + int((tok != 0).sum().item())
+        queue = self.meta[L.queue:L.queue + 16]
+        bad = int((counters != 0).sum().item()) + int((tok != 0).sum().item()) + int((queue != 0).sum().item())
         if status != 0 or bad:
             raise N.MoeError(f"expert step synchronization failed: sync_status={status}, "
                              f"non-zero counters={bad}; the rows and outputs are not valid")

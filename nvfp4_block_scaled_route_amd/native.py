@@ -29,7 +29,7 @@ class MoeMetaLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_tiles", "total_rows", "expert_offsets", "expert_counts", "exp2perm", "perm2tok",
         "tile_expert", "total_ints", "rows_max", "tiles_max", "sync_status", "sub_sync", "subs_max", "perm_counts",
-        "tok_sync", "fin_part")]
+        "tok_sync", "fin_part", "queue")]
 
 
 class MoeNvfp4Weights(ctypes.Structure):

@@ -36,6 +36,11 @@ def sync_counters(meta: np.ndarray, L) -> np.ndarray:
     return meta[L.sub_sync:L.sub_sync + 256 * L.subs_max].reshape(-1, 256)[:, :2]
 
 
+def queue_words(meta: np.ndarray, L) -> np.ndarray:
+    """The register-tiled expert step's work-queue counters (zero between calls)."""
+    return meta[L.queue:L.queue + 16]
+
+
 def token_counters(meta: np.ndarray, L, T: int) -> np.ndarray:
     """The arrival counter of every token (moe_experts_finalize's one-launch form)."""
     return meta[L.tok_sync:L.tok_sync + 32 * T].reshape(-1, 32)[:, 0]

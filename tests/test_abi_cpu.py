@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),
@@ -49,6 +49,8 @@ def test_rows_max_matches_oracle(T, K, E, m):
         assert f + n <= nxt
     header = {lay.num_tiles, lay.total_rows, lay.sync_status}
     assert len(header) == 3 and max(header) < 64
+    # the 16 work-queue words sit in the header too, clear of its other words
+    assert max(header) < lay.queue and lay.queue + 16 <= 64
 
 
 def test_invalid_sizes_are_refused():

@@ -9,7 +9,7 @@ import torch
 from nvfp4_block_scaled_route_amd import layer as LY
 from nvfp4_block_scaled_route_amd import workloads as W
 
-from .gpu_common import DEV, dev, host, say, sync_counters, upload_weights
+from .gpu_common import DEV, dev, host, queue_words, say, sync_counters, upload_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,7 @@ def test_graph_replays_equal_eager(name):
     eager = snapshot()
     L = bufs.layout
     assert eager["meta"][L.sync_status] == 0 and not np.any(sync_counters(eager["meta"], L))
+    assert not np.any(queue_words(eager["meta"], L))
     cap = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):

@@ -21,7 +21,7 @@ from oracle.permute import permute as o_permute
 from oracle.quant import quantize_nvfp4
 from oracle.routing import route as o_route
 
-from .gpu_common import (DEV, abs_gemm1, check_requant, dev, h_error_bound, host, run_layer, say,
+from .gpu_common import (DEV, abs_gemm1, check_requant, dev, h_error_bound, host, queue_words, run_layer, say,
                          sync_counters, upload_weights)
 
 pytestmark = pytest.mark.gpu
@@ -142,6 +142,7 @@ def _check_route(logits, bias, K, tile_m, offset=0, local=None, padding=None, ro
     assert np.array_equal(meta[L.perm2tok:L.perm2tok + L.rows_max], om["perm2tok"])
     assert np.array_equal(meta[L.tile_expert:L.tile_expert + L.tiles_max], om["tile_expert"])
     assert meta[L.sync_status] == 0 and not np.any(sync_counters(meta, L))
+    assert not np.any(queue_words(meta, L))
     assert np.all(meta[L.total_ints:] == -777)                   # nothing written past the buffer
     return ids, w, meta
 
@@ -490,14 +491,25 @@ def test_expert_tp_slices(inputs):
     assert sliced_rel < TOL
 
 
-@pytest.mark.parametrize("name,tile_m", [("decode_b8", 16), ("decode_b8", 64), ("tiny", 16)])
+def _tiled_inputs():
+    """Many routes per expert (the register-tiled form): T=256, H=512, I=256,
+    E=4, top-2, 128-row tiles, the intermediate's global scale set from its amax."""
+    from oracle.layer import intermediate_amax
+    wl = W.Workload("tiled_256", T=256, H=512, I=256, E=4, K=2, tile_m=128, seed=3)
+    probe = W.make_inputs(wl, a2_gscale=1.0)
+    return W.make_inputs(wl, a2_gscale=float(np.float32(2688.0 / intermediate_amax(probe))))
+
+
+@pytest.mark.parametrize("name,tile_m", [("decode_b8", 16), ("decode_b8", 64), ("tiny", 16), ("tiled_256", 128)])
 def test_experts_repeated_calls_on_one_metadata(inputs, name, tile_m):
     """moe_experts_fwd called again and again on one routing (as a graph replay
     or the expert TP slices do), its intermediate and rows cleared in between:
     identical rows every time (decode_b8: the workgroup kernels with the LDS
     copy of the activation for both GEMMs; tiny: GEMM2 on the one-wave kernel,
-    I/16 = 8 scale bytes per row)."""
-    inp = inputs(name)
+    I/16 = 8 scale bytes per row; tiled_256: the persistent register-tiled
+    kernel, whose work queues in the metadata must be back at 0 after every
+    call)."""
+    inp = _tiled_inputs() if name == "tiled_256" else inputs(name)
     wl = inp.wl
     w = upload_weights(inp)
     first = run_layer(inp, weights=w, tile_m=tile_m)
@@ -518,6 +530,7 @@ def test_experts_repeated_calls_on_one_metadata(inputs, name, tile_m):
         assert np.array_equal(host(bufs.rows)[0][valid], first["rows"][0][valid]), it
         meta = host(bufs.meta)
         assert meta[L.sync_status] == 0 and not np.any(sync_counters(meta, L)), it
+        assert not np.any(queue_words(meta, L)), it
 
 
 def test_layer_leaves_padding_rows_untouched_and_is_deterministic(inputs):
