@@ -409,7 +409,7 @@ __device__ __forceinline__ void run_held(const Stage (&st)[D], const uint8_t* lc
 // moe_experts_finalize's one-launch form (K <= 8). GEMM2 workgroups write their
 // rows with agent-coherent stores, wait until they have completed, and count
 // themselves on the arrival counter (word 0) of each token in their 16 rows.
-// The grid ends with F = fin_threads(H) / 256 finalizer workgroups per token:
+// The grid ends with F = fin_threads(H, T, n_partials) / 256 finalizer workgroups per token:
 // finalizer f plays moe_finalize's threads [256 f, 256 f + 256) (finalize.hpp),
 // so the arithmetic and its order are moe_finalize's. It waits until every
 // GEMM2 workgroup of every tile holding one of the token's served routes has
@@ -453,7 +453,7 @@ __device__ void finalizer(const ExpArgs& a, const FinFuse& fin, uint8_t* lds) {
     const uint32_t x = blockIdx.x - fin.fin_block0;
     const int t = (int)(x / (uint32_t)fin.F), part = (int)(x - (uint32_t)t * fin.F);
     const int tid = threadIdx.x, lane = tid & 63;
-    const int nthreads_v = fin_threads(f.H), nwaves_v = nthreads_v >> 6, ngroups = f.H / W;
+    const int nthreads_v = fin_threads(f.H, f.T, f.n_partials), nwaves_v = nthreads_v >> 6, ngroups = f.H / W;
     const int vt = part * kThreads + tid;              // moe_finalize's thread this one plays
     const bool wave_on = (vt & ~63) < nthreads_v;      // uniform over the wave
     int32_t* cnt = fin.tok_sync + (int64_t)t * kTokSyncStride;
@@ -570,8 +570,8 @@ __global__ void __launch_bounds__(kThreads) experts_fused_kernel(ExpArgs a, uint
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* lc = tile_lds + ((q >> 1) * 16 + n) * 16 + (q & 1) * 8;
     if (kFin && blockIdx.x >= fin.fin_block0) {
-        if (fin_w(a.H) == 2) finalizer<2, P2>(a, fin, tile_lds);
-        else finalizer<4, P2>(a, fin, tile_lds);        // the one-launch rule: H <= 4352
+        if (fin_w(fin.f.H, fin.f.T, fin.f.n_partials) == 2) finalizer<2, P2>(a, fin, tile_lds);
+        else finalizer<4, P2>(a, fin, tile_lds);        // W = 8 launches no finalizer workgroups
         return;
     }
     if (blockIdx.x < g1_blocks) {
@@ -799,12 +799,12 @@ static int experts_fwd(const char* name, const uint8_t* a_codes, const uint8_t* 
         const bool two_pairs = kt2 == 4 && H % 256 == 0;
         const int64_t g2 = two_pairs ? grid2 / 2 : grid2;
         FinFuse ff{};
-        if (fin && K <= kFinBatch) {
+        if (fin && K <= kFinBatch && fin_w(H, T, fin->n_partials) <= 4) {
             ff.f = *fin;
             ff.tok_sync = meta + args.L.tok_sync;
             ff.fin_part = meta + args.L.fin_part;
             ff.fin_block0 = (uint32_t)(grid1 + g2);
-            ff.F = (fin_threads(H) + kThreads - 1) / kThreads;
+            ff.F = (fin_threads(H, T, fin->n_partials) + kThreads - 1) / kThreads;
             const unsigned lds_f = (unsigned)sizeof(FinLds) > lds ? (unsigned)sizeof(FinLds) : lds;
             launch_fused<true>(f1, f2, two_pairs, dim3((unsigned)(grid1 + g2 + (int64_t)T * ff.F)), lds_f, s, args,
                                (uint32_t)grid1, ff);

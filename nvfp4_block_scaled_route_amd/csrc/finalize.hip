@@ -5,9 +5,9 @@
 // rounded once to bf16 before the norm (the expert_tp page, "probe_rel_l2").
 //
 // One workgroup of up to 1024 threads per token, a thread owning W consecutive
-// columns (W = 2, 4 or 8: the smallest that fits; C = 2 column groups per
-// thread only above 8192 columns), so that little serial work falls on any
-// one wave. Routes go in batches of 8 whose row loads issue together: the sum
+// columns (W = 2, 4 or 8 by H, T and the partial count: fin_w; C = 2 column
+// groups per thread only above 8192 columns), so that little serial work falls
+// on any one wave. Routes go in batches of 8 whose row loads issue together: the sum
 // of squares of each route (a DPP wave reduction in fixed order, then the
 // waves' partials in a fixed-order 16-lane reduction), then sum_k w_k * y_k in
 // fp32, k ascending, from the rows still in registers (batches past the first
@@ -140,7 +140,7 @@ extern "C" int moe_finalize(const uint16_t* rows, int64_t rows_stride, int n_par
     a.partial_stride = partial_stride; a.exp2perm = exp2perm; a.weights = topk_weights;
     a.norm_weight = norm_weight; a.gain_center = gain_center; a.eps = eps;
     a.weight_before_norm = weight_before_norm ? 1 : 0; a.T = T; a.K = K; a.H = H; a.out = out;
-    const int W = fin_w(H), C = fin_c(H), threads = fin_threads(H);
+    const int W = fin_w(H, T, n_partials), C = fin_c(H, T, n_partials), threads = fin_threads(H, T, n_partials);
     hipStream_t s = (hipStream_t)stream;
     if (W == 2)
         hipLaunchKernelGGL((finalize_kernel<2, 1>), dim3(T), dim3(threads), 0, s, a);

@@ -137,13 +137,25 @@ __device__ __forceinline__ void fin_inv_tree(const FinArgs& a, int k0, int tid, 
     }
 }
 
-// Columns per thread and column groups of the finalize of H columns: the
-// fewest that fit 1024 threads (two groups of 8 above 8192 columns), and the
-// (virtual) thread count.
-__host__ __device__ constexpr int fin_w(int H) { return H <= 2048 ? 2 : H <= 4096 ? 4 : 8; }
-__host__ __device__ constexpr int fin_c(int H) { return H / fin_w(H) > kFinMaxThreads ? 2 : 1; }
-__host__ __device__ constexpr int fin_threads(int H) {
-    return ((H / fin_w(H) + fin_c(H) - 1) / fin_c(H) + 63) / 64 * 64;
+// Columns per thread and column groups of the finalize of T tokens x H
+// columns with n_partials partial rows per route, and the (virtual) thread
+// count. Wider threads issue fewer, larger loads (16 bytes at W = 8): measured
+// on prefill_t4096 (T = 4096, H = 4096) 61 µs at W = 8 against 68 at W = 4,
+// decode_b8 (H = 2048) 5.0 µs at W = 4 against 5.6 at W = 2. Where few tokens
+// spread over few workgroups (or several partials are summed per route) the
+// narrower form keeps more loads in flight per token (expert_tp8_b32: 16.1 µs
+// at W = 4, 16.9 at W = 8), and the finalize inside the expert launch takes W
+// up to 4 only (its registers are the GEMM workgroups' too). Two groups of 8
+// columns a thread above 8192 columns.
+__host__ __device__ constexpr int fin_w(int H, int T, int n_partials) {
+    return H <= 1024 ? 2 : H <= 2048 ? 4 : (H > 4096 || (n_partials == 1 && T >= 512)) ? 8 : 4;
+}
+__host__ __device__ constexpr int fin_c(int H, int T, int n_partials) {
+    return H / fin_w(H, T, n_partials) > kFinMaxThreads ? 2 : 1;
+}
+__host__ __device__ constexpr int fin_threads(int H, int T, int n_partials) {
+    const int w = fin_w(H, T, n_partials), c = fin_c(H, T, n_partials);
+    return ((H / w + c - 1) / c + 63) / 64 * 64;
 }
 
 // A route row's W columns at column group grp, with several partials summed
@@ -191,14 +203,14 @@ __device__ __forceinline__ Cols<W> load_row_coherent(const FinArgs& a, int p, in
 
 // Token t's output row by the workgroup's nreal threads (a multiple of 64),
 // as moe_finalize computes it: real thread tid plays virtual threads
-// tid + j nreal below fin_threads(H), whole waves at a time. s_part
+// tid + j nreal below fin_threads(H, T, n_partials), whole waves at a time. s_part
 // [kFinBatch][kFinMaxWaves] and s_inv [MOE_MAX_TOPK] are the workgroup's LDS.
 // Row loads are agent-coherent. Ends with a barrier.
 template <int W, int C>
 __device__ void finalize_token(const FinArgs& a, int t, int tid, int nreal, float (*s_part)[kFinMaxWaves],
                                float* s_inv) {
     const int lane = tid & 63;
-    const int nthreads_v = fin_threads(a.H), nwaves_v = nthreads_v >> 6;
+    const int nthreads_v = fin_threads(a.H, a.T, a.n_partials), nwaves_v = nthreads_v >> 6;
     const int V = (nthreads_v + nreal - 1) / nreal;
     const int ngroups = a.H / W;
     // sums of squares, batch by batch

@@ -111,7 +111,11 @@ class _Case:
                                         ("fin_two_pairs", (6, 512, 256, 8, 2, 16)),
                                         ("fin_one_pair", (9, 1024, 512, 16, 4, 16)),
                                         ("fin_h4096", (5, 4096, 768, 16, 4, 32)),
-                                        ("fin_two_launch", (7, 320, 192, 8, 2, 16))])
+                                        ("fin_two_launch", (7, 320, 192, 8, 2, 16)),
+                                        # 512 tokens at H = 3072, one partial: the finalize takes 8
+                                        # columns a thread, which the finalizer in the expert launch
+                                        # does not, so the call runs the expert step, then moe_finalize
+                                        ("fin_wide", (512, 3072, 256, 64, 2, 16))])
 def test_experts_finalize_equals_two_calls(name, shape):
     c = _Case(_inputs(name, shape))
     c.check(c.two_calls(), c.fused(), name)
