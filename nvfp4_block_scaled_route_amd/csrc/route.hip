@@ -7,12 +7,12 @@
 //
 // Top-k, one 64-wide wave per token. Selection keys are totally ordered by
 // (key descending, expert index ascending), so every expert's place in the
-// ranking is unique: for E <= 256 each lane counts, against the wave's keys in
+// ranking is unique: for E <= 64 each lane counts, against the wave's keys in
 // LDS (one 64-bit comparison per key), the experts that beat its own, and the
 // experts with rank < K land in slot `rank` -- the K choices in key order with
-// no serial rounds. Larger E
-// takes K rounds of a wave-wide arg-max. The renormalizing sum then runs over
-// the K slots in order.
+// no serial rounds. Larger E takes K rounds of a wave-wide maximum of the
+// 64-bit composite keys by DPP (registers only). The renormalizing sum then
+// runs over the K choices in order.
 // Permutation: routes per expert are counted, the padded offsets scanned, and
 // a second pass gives every route its rank among the earlier routes of its
 // expert (ballot matching over the expert index bits within a wave: a stable
@@ -32,7 +32,7 @@ namespace moe {
 constexpr int kRouteThreads = 512;                 // 8 waves
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;  // 16
-constexpr int kRankMaxExperts = 256;               // rank-count top-k up to here
+constexpr int kRankMaxExperts = 64;                // rank-count top-k up to here; the wave maximum beyond
 constexpr int kFusedMaxTokens = 32;                // one workgroup routes up to here
 
 enum RouteMode { kTopkOnly = 0, kPermuteOnly = 1, kFused = 2 };
@@ -87,7 +87,7 @@ __device__ __forceinline__ void emit(const RouteArgs& a, int t, int lane, int id
     if (s_ids) s_ids[t * a.K + lane] = id;
 }
 
-// Rank-count top-k of token t by wave w (E <= kRankMaxExperts). Called by every
+// Rank-count top-k of token t by wave w (E <= kRankMaxExperts: one key a lane). Called by every
 // thread of the workgroup (it holds two barriers); `active` is false for waves
 // without a token this round. An expert's composite key is its ordered key in
 // the high word and the complement of its index in the low word, so that one
@@ -152,45 +152,79 @@ __device__ void topk_rank(const RouteArgs& a, int t, bool active, int lane, int 
     }
 }
 
-// K rounds of a wave-wide arg-max (any E), one wave, no barrier.
-__device__ void topk_rounds(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
+// A 64-bit value of lane i ^ m (quad xor 1 and 2) or of the mirrored lane
+// (half-row, row) by DPP, both halves with the same control.
+template <int ctrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
+
+// The largest 64-bit value over the wave, uniform: the maximum over each row
+// of 16 lanes by DPP, then over the four rows' lane 0, 16, 32, 48.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
+    v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
+    v = max_u64(v, dpp_u64<kDppRowHalfMirror>(v));
+    v = max_u64(v, dpp_u64<kDppRowMirror>(v));
+    uint64_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+        m = max_u64(m, ((uint64_t)hi << 32) | lo);
+    }
+    return m;
+}
+
+// Top-k of token t by one wave, any E up to 64 kPer: K rounds of a wave-wide
+// maximum of the composite keys (the ordered key in the high word, the
+// complement of the expert index in the low word: one 64-bit comparison
+// decides key descending, index ascending), taking the winner out of its lane
+// after each round. The K choices come out by key descending and the
+// renormalizing sum runs over them in that order, as in the rank-count form.
+// Registers and DPP only: no LDS, no barrier.
+template <int kPer>
+__device__ void topk_max(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
     if (a.is_padding && a.is_padding[t]) {
         if (lane < a.K) emit(a, t, lane, -1, 0.0f, s_ids);
         return;
     }
     const float* row = a.logits + (int64_t)t * a.logits_row_stride;
-    float key[kMaxPerLane], sc[kMaxPerLane];
-    uint32_t alive = 0;
+    uint64_t kk[kPer];
+    float sc[kPer];
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < kPer; ++j) {
         const int e = lane + 64 * j;
-        key[j] = -__builtin_inff();
+        kk[j] = 0u;                                // below every real composite (its high word is non-zero)
         sc[j] = 0.0f;
         if (e < a.E) {
             sc[j] = sigmoid32(row[e]);
-            key[j] = a.bias ? __fadd_rn(sc[j], a.bias[e]) : sc[j];
-            alive |= 1u << j;
+            const uint32_t ok = order_key(a.bias ? __fadd_rn(sc[j], a.bias[e]) : sc[j]);
+            kk[j] = ((uint64_t)ok << 32) | (uint32_t)~(uint32_t)e;
         }
     }
     float total = 0.0f, my_s = 0.0f;
     int my_id = -1;
     for (int k = 0; k < a.K; ++k) {
-        float bk = -__builtin_inff(), bs = 0.0f;
-        int bi = 0x7FFFFFFF;
+        uint64_t best = kk[0];
 #pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-            const int e = lane + 64 * j;
-            if (((alive >> j) & 1u) && better(key[j], e, bk, bi)) { bk = key[j]; bi = e; bs = sc[j]; }
-        }
+        for (int j = 1; j < kPer; ++j) best = max_u64(best, kk[j]);
+        best = wave_max_u64(best);
+        const int e = (int)~(uint32_t)best;       // uniform
+        const int owner = e & 63, slot = e >> 6;
+        float s_own = sc[0];
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ok = __shfl_xor(bk, off);
-            const int oi = __shfl_xor(bi, off);
-            const float os = __shfl_xor(bs, off);
-            if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bs = os; }
-        }
-        if ((bi & 63) == lane) alive &= ~(1u << (bi >> 6));
-        if (lane == k) { my_id = bi; my_s = bs; }
+        for (int j = 1; j < kPer; ++j)
+            if (j == slot) s_own = sc[j];
+        const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_own), owner));
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (j == slot && lane == owner) kk[j] = 0u;
+        if (lane == k) { my_id = e; my_s = bs; }
         total = __fadd_rn(total, bs);
     }
     if (lane < a.K)
@@ -198,15 +232,25 @@ __device__ void topk_rounds(const RouteArgs& a, int t, int lane, int32_t* s_ids)
              __fmul_rn(__fdiv_rn(my_s, __fadd_rn(total, 1e-15f)), a.route_scale), s_ids);
 }
 
-// Top-k of tokens [first, T) with stride `step`, eight per round (every thread
-// of the workgroup takes part in every round: the rank path holds barriers).
+// Top-k of tokens [first, T) with stride `step`, one token per wave: the
+// rank count up to 64 experts (every thread of the workgroup takes part in
+// every round: it holds barriers), the K-round wave maximum beyond (measured,
+// moe_route_quant back to back: decode_b8 (E = 64) 6.4 µs by rank count, 6.7
+// by rounds; E = 128: expert_tp8_b32 (32 tokens, one workgroup) 26.2 -> 17.5
+// µs, decode_b64_zipf 17.5 -> 15.3, prefill_t4096 32.6 -> 29.2).
 __device__ void topk_tokens(const RouteArgs& a, int first, int step, int32_t* lds_topk,
                             int32_t* s_ids) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int base = first; base < a.T; base += step) {
         const int t = base + w;
-        if (a.E <= kRankMaxExperts) topk_rank(a, t, t < a.T, lane, w, lds_topk, s_ids);
-        else if (t < a.T) topk_rounds(a, t, lane, s_ids);
+        if (a.E <= kRankMaxExperts) {
+            topk_rank(a, t, t < a.T, lane, w, lds_topk, s_ids);
+            continue;
+        }
+        if (t >= a.T) continue;                    // uniform over the wave
+        if (a.E <= 128) topk_max<2>(a, t, lane, s_ids);
+        else if (a.E <= 256) topk_max<4>(a, t, lane, s_ids);
+        else topk_max<kMaxPerLane>(a, t, lane, s_ids);
     }
 }
 
