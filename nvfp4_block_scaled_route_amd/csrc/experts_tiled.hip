@@ -52,9 +52,13 @@
 // one whole 16-wide block of one row: the requantization (amax, e4m3 scale,
 // codes) and the bf16 packing are lane-local and the stores are 8 or 32
 // contiguous bytes. Rows without a route are not written.
+#include <atomic>
+
 #include "experts.hpp"
 
 namespace moe {
+
+constexpr int kMaxDevices = 64;             // devices whose CU count is cached
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -759,10 +763,18 @@ int launch_tiled(const ExpArgs& a, hipStream_t s) {
     const int ncg1 = (ncb1 + kWaves - 1) / kWaves, ncg2 = (ncb2 + kWaves - 1) / kWaves;
     if ((int64_t)((nx + kXcds - 1) / kXcds) * (ncg1 + ncg2) >= (1 << 24))
         return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many row blocks for the work queues");
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        return fail(MOE_ELAUNCH, "moe_experts_fwd: cannot read the device's compute unit count");
+    // the device's compute-unit count, read once per device (racing first
+    // calls store the same value)
+    static std::atomic<int> s_cus[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(MOE_ELAUNCH, "moe_experts_fwd: no current device");
+    int cus = dev < kMaxDevices ? s_cus[dev].load(std::memory_order_relaxed) : 0;
+    if (cus < 1) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            return fail(MOE_ELAUNCH, "moe_experts_fwd: cannot read the device's compute unit count");
+        if (dev < kMaxDevices) s_cus[dev].store(cus, std::memory_order_relaxed);
+    }
     // one workgroup per CU (a workgroup takes a whole CU's registers), a
     // multiple of the 8 XCDs
     const int grid = (cus + kXcds - 1) / kXcds * kXcds;
