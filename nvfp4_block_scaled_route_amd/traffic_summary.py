@@ -59,6 +59,42 @@ def per_dispatch(run_dir: str, counter: str) -> dict:
     return {k: sum(v.values()) / len(v) for k, v in per.items()}
 
 
+def summarize(run_dir: str, copy_dir: str, copy_mib: float, workload: str, launches_per_step: int = 1):
+    """The traffic record of one workload and its table rows: each expert
+    kernel's mean FETCH_SIZE and WRITE_SIZE per dispatch, divided by what the
+    counters read per KiB of the calibration copy, summed over the kernels of
+    one launch and multiplied by the launches of a step."""
+    fetch = per_dispatch(os.path.join(run_dir, "FETCH_SIZE"), "FETCH_SIZE")
+    write = per_dispatch(os.path.join(run_dir, "WRITE_SIZE"), "WRITE_SIZE")
+    cfetch = per_dispatch(os.path.join(copy_dir, "copy_FETCH_SIZE"), "FETCH_SIZE")
+    cwrite = per_dispatch(os.path.join(copy_dir, "copy_WRITE_SIZE"), "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    # the copy kernel is the one whose counters are largest
+    fetch_factor = max(cfetch.values()) / copy_kib
+    write_factor = max(cwrite.values()) / copy_kib
+
+    kernels = sorted(k for k in fetch if is_expert_kernel(k))
+    rows, total = [], 0.0
+    rec = {"workload": workload, "kernels": kernels, "fetch_factor": fetch_factor,
+           "write_factor": write_factor, "launches_per_step": launches_per_step}
+    for k in kernels:
+        rb = fetch[k] / fetch_factor * 1024.0
+        wb = write.get(k, 0.0) / write_factor * 1024.0
+        rows.append((k, fetch[k], write.get(k, 0.0), rb / 1e6, wb / 1e6))
+        total += rb + wb
+    rec["per_kernel"] = [{"kernel": k, "fetch_kib": f, "write_kib": w, "read_mb": r, "write_mb": x}
+                         for k, f, w, r, x in rows]
+    rec["traffic_bytes_per_launch"] = total
+    rec["traffic_bytes"] = total * launches_per_step
+    h = hashlib.sha256()
+    for src in SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    rec["sources"] = SOURCES
+    rec["sources_sha256"] = h.hexdigest()
+    return rec, rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--dir", required=True)
@@ -70,46 +106,20 @@ def main():
                     help="expert-step launches per layer step (the expert-TP slices)")
     args = ap.parse_args()
 
-    fetch = per_dispatch(os.path.join(args.dir, "FETCH_SIZE"), "FETCH_SIZE")
-    write = per_dispatch(os.path.join(args.dir, "WRITE_SIZE"), "WRITE_SIZE")
-    cdir = args.copy_dir or args.dir
-    cfetch = per_dispatch(os.path.join(cdir, "copy_FETCH_SIZE"), "FETCH_SIZE")
-    cwrite = per_dispatch(os.path.join(cdir, "copy_WRITE_SIZE"), "WRITE_SIZE")
-    copy_kib = args.copy_mib * 1024.0
-    # the copy kernel is the one whose counters are largest
-    fetch_factor = max(cfetch.values()) / copy_kib
-    write_factor = max(cwrite.values()) / copy_kib
-
-    kernels = sorted(k for k in fetch if is_expert_kernel(k))
-    rows, total = [], 0.0
-    rec = {"workload": args.workload, "kernels": kernels, "fetch_factor": fetch_factor,
-           "write_factor": write_factor, "launches_per_step": args.launches_per_step}
-    for k in kernels:
-        rb = fetch[k] / fetch_factor * 1024.0
-        wb = write.get(k, 0.0) / write_factor * 1024.0
-        rows.append((k, fetch[k], write.get(k, 0.0), rb / 1e6, wb / 1e6))
-        total += rb + wb
-    rec["per_kernel"] = [{"kernel": k, "fetch_kib": f, "write_kib": w, "read_mb": r, "write_mb": x}
-                         for k, f, w, r, x in rows]
-    rec["traffic_bytes_per_launch"] = total
-    rec["traffic_bytes"] = total * args.launches_per_step
-    h = hashlib.sha256()
-    for src in SOURCES:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    rec["sources"] = SOURCES
-    rec["sources_sha256"] = h.hexdigest()
+    rec, rows = summarize(args.dir, args.copy_dir or args.dir, args.copy_mib, args.workload,
+                          args.launches_per_step)
     out = os.path.join(ROOT, "profiles", f"experts_{args.workload}_traffic.json")
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
-    print(f"calibration: copy of {args.copy_mib:g} MiB reads FETCH_SIZE x{fetch_factor:.4f}, "
-          f"WRITE_SIZE x{write_factor:.4f} per KiB moved")
+    print(f"calibration: copy of {args.copy_mib:g} MiB reads FETCH_SIZE x{rec['fetch_factor']:.4f}, "
+          f"WRITE_SIZE x{rec['write_factor']:.4f} per KiB moved")
     print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |")
     print("|---|---|---|---|---|")
     for k, f, w, r, x in rows:
         print(f"| `{k}` | {f:.1f} | {w:.1f} | {r:.2f} | {x:.3f} |")
+    total = rec["traffic_bytes_per_launch"]
     print(f"traffic per launch: {total / 1e6:.2f} MB; per step ({args.launches_per_step} launches): "
-          f"{total * args.launches_per_step / 1e6:.2f} MB -> {out}")
+          f"{rec['traffic_bytes'] / 1e6:.2f} MB -> {out}")
 
 
 if __name__ == "__main__":

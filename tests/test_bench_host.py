@@ -107,3 +107,49 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def _counter_csv(path, counter, rows):
+    """rocprofv3's counter_collection.csv columns the summary reads: one row a
+    counter instance, (kernel, dispatch id, value)."""
+    os.makedirs(path)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for k, d, v in rows:
+            f.write(f'{d},"{k}",{counter},{v}\n')
+
+
+def test_traffic_summary_scales_by_the_copy_and_the_launches(tmp_path):
+    """FETCH_SIZE and WRITE_SIZE of a dispatch are summed over its instances
+    and averaged over dispatches, divided by what the same counter reads per KiB
+    of a copy of known size, summed over the step's expert kernels (a kernel the
+    step does not launch left out) and multiplied by the launches of a step."""
+    from nvfp4_block_scaled_route_amd import traffic_summary as ts
+    step = "void moe::experts_fused_kernel<8, 4, 2, false>(moe::ExpArgs, unsigned int, moe::FinFuse)"
+    tiled = "moe::tiled_fused_kernel(moe::ExpArgs, int, int, int, int)"
+    other = "void moe::w16_gemm1_kernel<4>(moe::W16Args)"
+    for name in (step, tiled):
+        assert ts.is_expert_kernel(name)
+    assert not ts.is_expert_kernel(other) and not ts.is_expert_kernel("moe::finalize_kernel<2>(moe::Fin)")
+    run = tmp_path / "run"
+    # two dispatches of the step kernel, two counter instances each: 600 and 400 KiB fetched
+    _counter_csv(run / "FETCH_SIZE", "FETCH_SIZE",
+                 [(step, 1, 250.0), (step, 1, 350.0), (step, 2, 100.0), (step, 2, 300.0), (other, 3, 9e9)])
+    _counter_csv(run / "WRITE_SIZE", "WRITE_SIZE", [(step, 1, 20.0), (step, 2, 30.0), (other, 3, 9e9)])
+    # a 1 MiB copy whose FETCH_SIZE reads half the KiB moved and WRITE_SIZE all of them
+    _counter_csv(run / "copy_FETCH_SIZE", "FETCH_SIZE", [("copy", 1, 512.0), ("fill", 2, 8.0)])
+    _counter_csv(run / "copy_WRITE_SIZE", "WRITE_SIZE", [("copy", 1, 1024.0)])
+    rec, rows = ts.summarize(str(run), str(run), 1.0, "w", launches_per_step=8)
+    assert rec["kernels"] == [step] and len(rows) == 1
+    assert rec["fetch_factor"] == 0.5 and rec["write_factor"] == 1.0
+    per_launch = (500.0 / 0.5 + 25.0) * 1024.0
+    assert rec["traffic_bytes_per_launch"] == per_launch
+    assert rec["traffic_bytes"] == 8 * per_launch
+    assert rec["sources"] == ts.SOURCES and len(rec["sources_sha256"]) == 64
+    # the committed records were written the same way: per step = launches x per launch
+    for fn in os.listdir(os.path.join(ROOT, "profiles")):
+        if fn.startswith("experts_") and fn.endswith("_traffic.json"):
+            with open(os.path.join(ROOT, "profiles", fn)) as f:
+                r = json.load(f)
+            assert abs(r["traffic_bytes"] - r["launches_per_step"] * r["traffic_bytes_per_launch"]) \
+                <= 1e-9 * r["traffic_bytes"], fn
