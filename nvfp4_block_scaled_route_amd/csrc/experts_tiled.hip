@@ -7,47 +7,47 @@
 // not by the weight stream. gfx950 has no MFMA for 16-element blocks under e4m3
 // scales, so both operands are decoded to exact f16 (one VALU instruction per
 // element) and multiplied with v_mfma_f32_32x32x16_f16. The decode is the cost
-// to amortize: every decoded element must feed as many MFMAs as possible.
+// to amortize, and the matrix pipe has to be kept busy while it runs.
 //
-// A workgroup takes one 128-row block of one expert and 4 column blocks of 128;
-// each of its 4 waves computes one 128 x 128 output block over K in 64-wide
-// k-tiles with 4 x 4 accumulators (the 256 accumulators fill the AGPR file: one
-// wave per SIMD):
+// Two workgroups share a CU (two waves per SIMD: while one waits at a barrier,
+// on memory or in its epilogue, the other issues MFMAs). A workgroup takes one
+// 128-row block of one expert and 4 column blocks; each of its 4 waves computes
+// one 128 x 64 output block over K in 64-wide k-tiles with 4 x 2 accumulators
+// (128 accumulator registers, half of a wave's share at two waves a SIMD):
 //   * the MFMA K index is permuted on both operands so that over the 4 K-steps
 //     of a k-tile a lane (r, h) of a 32 x 32 x 16 MFMA holds two whole NVFP4
 //     blocks of its row (column), blocks 2h and 2h + 1, each under one scale;
-//     a decoded A fragment then feeds 4 MFMAs and a decoded B fragment 4:
-//     4 VALU instructions per 32-cycle MFMA, which run beside the matrix pipe;
 //   * the weights (B) go straight from global memory to registers in MFMA lane
 //     order (whole pair tiles of the converted layout: full cache lines), two
-//     k-tiles ahead;
-//   * the activation rows (A) are shared by the 4 waves: the workgroup copies 4
-//     k-tiles of its 128 rows at a time (128 bytes of codes per row: whole cache
-//     lines) with direct global-to-LDS loads into a double-buffered LDS stage,
-//     one barrier per stage, and each wave reads its fragments from there. A
-//     row's 16-byte chunks are stored XOR-swizzled (chunk_swizzle), so that
-//     the 16-byte fragment reads of 16 consecutive rows -- one LDS cycle on
-//     gfx950, 64 banks -- hit 16 different bank groups (measured: the
-//     3-bit XOR alone left 4 conflict cycles per read).
-//     (Gathered straight into registers, every A load touched 32 cache lines
-//     for 32 bytes each, and the weight stream evicted them before the next
-//     k-tile could use the rest.)
+//     k-tiles ahead; each wave decodes its own columns (2 fragments a K-step,
+//     each feeding RT MFMAs);
+//   * the activation rows (A): the workgroup copies 4 k-tiles of its routed
+//     rows at a time (128 bytes of codes per row: whole cache lines) with
+//     direct global-to-LDS loads into a double-buffered raw stage (one row's
+//     16-byte chunks XOR-swizzled, chunk_swizzle). In blocks of 3 or 4 routed
+//     row tiles A is decoded once per workgroup: during k-tile c every thread
+//     decodes its share of k-tile c + 1 into a double-buffered f16 tile in MFMA
+//     fragment order, from which each wave reads its A fragments with 16-byte
+//     LDS reads (64 lanes, 1 KB contiguous: no bank conflicts); one barrier per
+//     k-tile publishes the decoded tile. In blocks of 1 or 2, each wave decodes
+//     its own A fragments from the raw stage (one barrier per stage);
 //   * row tiles with no route are skipped (an expert's rows are padded to the
-//     block size): a block runs with 1 to 4 row tiles.
-// One persistent workgroup per CU takes work items -- (routed row block,
+//     block size): a block runs with 1 to 4 row tiles and copies and decodes
+//     only those.
+// One persistent workgroup per half CU takes work items -- (routed row block,
 // column group) of GEMM1, then of GEMM2 -- from 8 queues, one per XCD: the
 // routed row blocks (their count is read from the routing metadata) are split
 // into 8 equal contiguous chunks, and queue x holds chunk x's GEMM1 items, row
 // block major, then its GEMM2 items. A workgroup takes from its own XCD's queue
 // (workgroups are dealt to the 8 XCDs round robin), so the column groups of a
 // row block, and the row blocks of one expert, run on the same XCD at about
-// the same time and share the A rows and the weights in its L2; when that queue
-// is empty it takes from the others, so that no XCD idles while another still
-// has work (items differ in length: a block runs 1 to 4 row tiles).
+// the same time; when that queue is empty it takes from the others, so that no
+// XCD idles while another still has work (items differ in length: a block runs
+// 1 to 4 row tiles).
 //
 // GEMM1's columns are arranged so that a lane holds the gate and the up value of
-// the same intermediate in two accumulators (column tiles 2t and 2t + 1 take the
-// gate and the up halves of the same two pairs), so SwiGLU is lane-local. The
+// the same intermediate in two accumulators (column tiles 0 and 1 take the gate
+// and the up halves of the same two pairs), so SwiGLU is lane-local. The
 // epilogues then transpose each 32 x 32 tile through LDS so that a lane holds
 // one whole 16-wide block of one row: the requantization (amax, e4m3 scale,
 // codes) and the bf16 packing are lane-local and the stores are 8 or 32
@@ -63,26 +63,34 @@ constexpr int kMaxDevices = 64;             // devices whose CU count is cached
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kCT = 4;                      // 32-column MFMA tiles per wave
+constexpr int kCT = 2;                      // 32-column MFMA tiles per wave
 constexpr int kBlockRows = 128;             // rows per block (4 row tiles of 32)
 constexpr int kWaves = 4;                   // waves (column blocks) per workgroup
-constexpr int kStage = 4;                   // k-tiles per A stage in LDS
-constexpr int kAhead = 2;                   // weight k-tiles loaded ahead in registers
+constexpr int kWgPerCu = 2;                 // workgroups a CU holds at once
+constexpr int kStage = 4;                   // k-tiles per raw A stage in LDS
 constexpr int kXcds = 8;
 constexpr int kARowBytes = 32 * kStage;     // codes of one row in a stage
 constexpr int kASfBytes = 4 * kStage;       // block scales of one row in a stage
-
+constexpr int kSlabStride = 36;             // floats per row of an epilogue slab
+constexpr int kAhBytes = 4 * 4 * 64 * 16;   // decoded A of one k-tile: [row tile][K-step][lane] 16 bytes
 
 // The LDS position (16-byte unit within its 128-byte row) of chunk k of row r:
 // rows r and r + 1 fall in different halves of the 64 banks, so the 8
 // positions of the rows r % 2 == const must differ over 16 consecutive rows.
 __device__ __forceinline__ int chunk_swizzle(int k, int r) { return k ^ (r & 7) ^ ((r >> 3) & 1); }
 
-// LDS: two A stages (codes, swizzled; block scales)
+// LDS of a workgroup (68 KB: two fit a CU): the raw A stages (codes, swizzled;
+// block scales), which the epilogue's tile transposes reuse once the k-loop is
+// done, and the two decoded f16 A k-tiles.
 struct ALds {
-    uint8_t codes[2][kBlockRows * kARowBytes];
-    uint8_t sf[2][kBlockRows * kASfBytes];
-    float slab[4][2][32 * 36];  // per wave, two: the epilogue's tile transposes (32 rows of 36)
+    union {
+        struct {
+            alignas(16) uint8_t codes[2][kBlockRows * kARowBytes];
+            alignas(16) uint8_t sf[2][kBlockRows * kASfBytes];
+        } raw;
+        float slab[kWaves][2][32 * kSlabStride];   // per wave, two: the epilogue's tile transposes
+    } u;
+    alignas(16) uint8_t ah[2][kAhBytes];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
@@ -92,22 +100,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) 
 
 // One lane's raw weight operands of one k-tile: blocks 2h and 2h + 1 of each
 // column tile's column (8 bytes each, 256 bytes apart in the pair tile) and the
-// u32 words holding their scales. In GEMM1 column tiles 2t and 2t + 1 are the
-// two halves of the same pairs, whose scale bytes share words: kSW word pairs.
+// u32 words holding their scales. In GEMM1 column tiles 0 and 1 are the two
+// halves of the same pairs, whose scale bytes share words: kSW word pairs.
 template <int MODE>
 struct BRaw {
     static constexpr int kSW = MODE == 1 ? kCT / 2 : kCT;
     static constexpr int kLoads = 2 * kCT + 2 * kSW;
     uint2 b[kCT][2];
     uint32_t bsf[kSW][2];
-};
-
-// One lane's raw activation operands of one k-tile: the 32 codes (blocks 2h,
-// 2h + 1) of each row tile's row and the row's 4 block scales of the k-tile.
-template <int RT>
-struct ARaw {
-    uint4 a[RT];
-    uint32_t asf[RT];
 };
 
 struct BSrc {
@@ -171,11 +171,12 @@ __device__ __forceinline__ void b_load(BRaw<MODE>& r, const BSrc& p, int c) {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The workgroup's copy of A stage g into LDS buffer g & 1. Codes: wave w's
-// load q covers rows 32q + 8w + [0, 8) (1 KB, lane l at byte 16 l): lane l
-// fetches the chunk of row 32q + 8w + l / 8 whose swizzled position is l % 8
-// (the swizzle is an involution). Scales: waves 0
-// and 1, lane l fetches the 16 scale bytes of row 64w + l.
+// The workgroup's copy of raw A stage g into LDS buffer g & 1, the rows of
+// its RT routed row tiles only. Codes: wave w's load q covers rows
+// 32q + 8w + [0, 8) (1 KB, lane l at byte 16 l): lane l fetches the chunk of
+// row 32q + 8w + l / 8 whose swizzled position is l % 8 (the swizzle is an
+// involution). Scales: waves 0 and 1, lane l fetches the 16 scale bytes of
+// row 64w + l.
 //
 // The copies are written as inline assembly on purpose: the compiler treats
 // its own direct-to-LDS loads as LDS writes of unknown extent and waits for
@@ -188,67 +189,80 @@ struct ASrc {
     uint32_t as_off;                // per lane: row start (waves 0, 1)
 };
 
-
 // kCoherent: agent-coherent copies (an intermediate other workgroups of the
 // same launch published).
-template <bool kCoherent>
+template <int RT, bool kCoherent>
 __device__ __forceinline__ void a_stage_load(ALds& lds, const ASrc& p, int wave, int g) {
     const int buf = g & 1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(&lds.codes[buf][(32 * q + 8 * wave) * kARowBytes]));
+    for (int q = 0; q < RT; ++q) {
+        const uint32_t l =
+            __builtin_amdgcn_readfirstlane(lds_addr(&lds.u.raw.codes[buf][(32 * q + 8 * wave) * kARowBytes]));
         if (kCoherent) lds_copy16_sc1(p.a, l, p.a_off[q], (uint32_t)(g * kARowBytes));
         else lds_copy16(p.a, l, p.a_off[q], (uint32_t)(g * kARowBytes));
     }
-    if (wave < 2) {
-        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(&lds.sf[buf][64 * wave * kASfBytes]));
+    if (wave < (RT + 1) / 2) {
+        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_addr(&lds.u.raw.sf[buf][64 * wave * kASfBytes]));
         if (kCoherent) lds_copy16_sc1(p.as, l, p.as_off, (uint32_t)(g * kASfBytes));
         else lds_copy16(p.as, l, p.as_off, (uint32_t)(g * kASfBytes));
     }
 }
 
-// A fragments of k-tile c of a stage: lane (nn, h) of row tile i reads the 16
-// bytes of chunk 2c + h of row 32 i + nn (swizzled), and its 4 block scales.
+// The workgroup's decode of A k-tile c (from raw stage c / 4) into the f16 tile
+// ah[c % 2]: thread (wave w, lane l = 32 h + nn) makes the fragments (row tile
+// i, K-step w, lane l) for i < RT -- u32 word w of chunk 2 (c % 4) + h of row
+// 32 i + nn (8 codes: elements 32 h + 8 w + [0, 8) of the k-tile) under the
+// scale of block 2h + w / 2 -- and stores each at ((4 i + w) 64 + l) 16: the
+// 16 bytes lane l of a wave reads for K-step w of row tile i.
 template <int RT>
-__device__ __forceinline__ void a_read(ARaw<RT>& r, const ALds& lds, int buf, int c, int nn, int h) {
-    const int pos = chunk_swizzle(2 * c + h, nn) * 16;       // rows 32 i + nn: same low bits
+struct ADec {
+    uint32_t w[RT];
+    uint32_t sf[RT];
+};
+
+template <int RT>
+__device__ __forceinline__ void adec_read(ADec<RT>& r, const ALds& lds, int c, int wave, int nn, int h) {
+    const int buf = (c / kStage) & 1, cc = c % kStage;
+    const int pos = chunk_swizzle(2 * cc + h, nn) * 16 + 4 * wave;   // rows 32 i + nn: same low bits
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-        r.a[i] = *reinterpret_cast<const uint4*>(&lds.codes[buf][(32 * i + nn) * kARowBytes + pos]);
-        r.asf[i] = *reinterpret_cast<const uint32_t*>(&lds.sf[buf][(32 * i + nn) * kASfBytes + 4 * c]);
+        const int row = 32 * i + nn;
+        r.w[i] = *reinterpret_cast<const uint32_t*>(&lds.u.raw.codes[buf][row * kARowBytes + pos]);
+        r.sf[i] = lds.u.raw.sf[buf][row * kASfBytes + 4 * cc + 2 * h + (wave >> 1)];
     }
 }
 
-// The MFMAs of one k-tile. K-step s takes, in lane (r, h), the elements
-// 32 h + 8 s + [0, 8) of the k-tile: u32 word s of the lane's 16 code bytes,
-// under the scale of block 2h + s / 2. The fragments of step s + 1 are decoded
-// while the MFMAs of step s run: one MFMA, then 4 or 5 VALU instructions.
-template <int RT>
-struct Frags {
-    half8 a[RT], b[kCT];
-};
-
-template <int MODE, int RT>
-__device__ __forceinline__ void decode_step(const ARaw<RT>& ar, const BRaw<MODE>& br, const half2v (&sa)[RT],
-                                            const half2v (&sb)[kCT], int s, Frags<RT>& f) {
+template <int RT, int I0, int I1>
+__device__ __forceinline__ void adec_write(const ADec<RT>& r, ALds& lds, int c, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-        const uint32_t w = s == 0 ? ar.a[i].x : s == 1 ? ar.a[i].y : s == 2 ? ar.a[i].z : ar.a[i].w;
-        f.a[i] = nvfp4x8_to_f16(w, s < 2 ? splat_lo(sa[i]) : splat_hi(sa[i]));
+    for (int i = I0; i < (I1 < RT ? I1 : RT); ++i) {
+        const half8 v = nvfp4x8_to_f16(r.w[i], splat_lo(e4m3x2_to_f16(r.sf[i])));
+        *reinterpret_cast<half8*>(&lds.ah[c & 1][((4 * i + wave) * 64 + lane) * 16]) = v;
     }
+}
+
+// A fragments of K-step s of k-tile c, one 16-byte read per row tile.
+template <int RT>
+__device__ __forceinline__ void a_frags(half8 (&fa)[RT], const ALds& lds, int c, int s, int lane) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) fa[i] = *reinterpret_cast<const half8*>(&lds.ah[c & 1][((4 * i + s) * 64 + lane) * 16]);
+}
+
+// B fragments of K-step s: lane (r, h) takes u32 word s of its 16 code bytes
+// (elements 32 h + 8 s + [0, 8) of the k-tile) under the scale of block
+// 2h + s / 2.
+template <int MODE>
+__device__ __forceinline__ void b_frags(half8 (&fb)[kCT], const BRaw<MODE>& br, const half2v (&sb)[kCT], int s) {
 #pragma unroll
     for (int j = 0; j < kCT; ++j) {
         const uint32_t w = s == 0 ? br.b[j][0].x : s == 1 ? br.b[j][0].y : s == 2 ? br.b[j][1].x : br.b[j][1].y;
-        f.b[j] = nvfp4x8_to_f16(w, s < 2 ? splat_lo(sb[j]) : splat_hi(sb[j]));
+        fb[j] = nvfp4x8_to_f16(w, s < 2 ? splat_lo(sb[j]) : splat_hi(sb[j]));
     }
 }
 
-// The block scales of one k-tile as f16 pairs (block 2h, block 2h + 1).
-template <int MODE, int RT>
-__device__ __forceinline__ void tile_scales(const ARaw<RT>& ar, const BRaw<MODE>& br, int h,
-                                            const uint32_t (&sel)[2], half2v (&sa)[RT], half2v (&sb)[kCT]) {
-#pragma unroll
-    for (int i = 0; i < RT; ++i) sa[i] = e4m3x2_to_f16(ar.asf[i] >> (16 * h));
+// The weight block scales of one k-tile as f16 pairs (block 2h, block 2h + 1).
+template <int MODE>
+__device__ __forceinline__ void b_scales(const BRaw<MODE>& br, const uint32_t (&sel)[2], half2v (&sb)[kCT]) {
 #pragma unroll
     for (int j = 0; j < kCT; ++j) {
         const int t = MODE == 1 ? j >> 1 : j;
@@ -256,37 +270,37 @@ __device__ __forceinline__ void tile_scales(const ARaw<RT>& ar, const BRaw<MODE>
     }
 }
 
-// Keeps the decode of a step's fragments in the region where it is written:
-// without it the compiler sinks the VALU work next to its first use, into the
-// following region, where it no longer overlaps the MFMAs.
-template <int RT>
-__device__ __forceinline__ void pin(Frags<RT>& f) {
+// Keeps a step's B decode in the region where it is written: without it the
+// compiler sinks the VALU work next to its first use, into the following
+// region, where it no longer overlaps the MFMAs. (The A fragments' LDS reads
+// stay in their region by the region's scheduling barrier; their wait falls
+// at the first MFMA that uses them.)
+__device__ __forceinline__ void pin(half8 (&fb)[kCT]) {
 #pragma unroll
-    for (int i = 0; i < RT; ++i) asm volatile("" : "+v"(f.a[i]));
-#pragma unroll
-    for (int j = 0; j < kCT; ++j) asm volatile("" : "+v"(f.b[j]));
+    for (int j = 0; j < kCT; ++j) asm volatile("" : "+v"(fb[j]));
 }
 
 template <int RT>
-__device__ __forceinline__ void step_mfma(const Frags<RT>& f, floatx16 (&acc)[RT][kCT]) {
+__device__ __forceinline__ void step_mfma(const half8 (&fa)[RT], const half8 (&fb)[kCT], floatx16 (&acc)[RT][kCT]) {
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int j = 0; j < kCT; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling of one step region: each MFMA followed by its share of the VALU
-// decode work (and of the memory instructions, nmem of them in the region).
-template <int RT>
-__device__ __forceinline__ void interleave(int nmem) {
+// Scheduling of one K-step region: each of its RT x kCT MFMAs followed by its
+// share of the region's VALU work (NV instructions) and memory instructions
+// (NM: vector-memory and LDS reads and writes).
+template <int RT, int NV, int NM>
+__device__ __forceinline__ void interleave() {
     constexpr int kM = RT * kCT;
-    constexpr int kV = (8 * (RT + kCT) + 2 * (RT + kCT) + kM - 1) / kM;   // decode + scale work, rounded up
+    constexpr int kV = (NV + kM - 1) / kM, kMem = (NM + kM - 1) / kM;
 #pragma unroll
     for (int k = 0; k < kM; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);     // VALU
-        if (k < nmem) __builtin_amdgcn_sched_group_barrier(0x020 | 0x100, 1, 0);   // VMEM or DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);                 // VALU
+        if (kMem > 0) __builtin_amdgcn_sched_group_barrier(0x020 | 0x100 | 0x200, kMem, 0);   // VMEM, DS
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -296,8 +310,6 @@ __device__ __forceinline__ void interleave(int nmem) {
 // in 8 different bank groups), so that lane L then holds the 16 consecutive
 // columns 16 (L % 2) + [0, 16) of row L / 2: one whole NVFP4 block (GEMM1) or
 // 32 contiguous bytes of a bf16 row (GEMM2), with all arithmetic lane-local.
-constexpr int kSlabStride = 36;
-
 // A wave's LDS instructions execute in order, so its later reads see its
 // earlier writes (those of other lanes included) without a wait; this only
 // keeps the compiler from reordering them. The two slabs of a wave alternate
@@ -393,6 +405,228 @@ __device__ __forceinline__ void bf16_tile(const floatx16& acc, float alpha, int 
     }
 }
 
+// A wave's k-loop state.
+template <int MODE, int RT>
+struct KState {
+    floatx16 acc[RT][kCT];
+    BRaw<MODE> ring[2];             // weight k-tile c in slot c % 2
+    half8 fa[2][RT], fb[2][kCT];    // fragments of the current and the next K-step
+    half2v sb[kCT];                 // the current k-tile's weight block scales
+};
+
+struct KPos {
+    int KT, NS;                     // k-tiles, raw stages
+    int wave, lane, nn, h;
+};
+
+// One k-tile c (position CC in its raw stage g; weight ring slot c % 2): 4
+// K-step regions of RT x 2 MFMAs. While the MFMAs of step s run, the fragments
+// of step s + 1 are read and decoded (in the last region those of step 0 of
+// k-tile c + 1), the workgroup decodes the A of k-tile c + 1 (regions 0 to 2)
+// and the weights of k-tile c + 2 load into the slot k-tile c has finished
+// with. The barrier after region 2 publishes the A of k-tile c + 1 (and frees
+// ah[c % 2], whose last reads were issued before it); once a stage (CC == 2)
+// it also waits for raw stage g + 1, copied during k-tile 4g - 2, and frees raw
+// buffer g % 2 for stage g + 2 (raw stage g was last read by the decode of
+// k-tile 4g + 3). Past the end the copies repeat the last stage and the weight
+// loads the last k-tile.
+template <int MODE, int RT, bool kCoh, int CC>
+__device__ __forceinline__ void ktile(KState<MODE, RT>& st, ALds& lds, const ASrc& ap, const BSrc& p,
+                                      const uint32_t (&sel)[2], const KPos& k, int c) {
+    constexpr int SLOT = CC & 1, NXT = SLOT ^ 1;
+    // weight loads issued between one stage copy (k-tile 4g - 2, region 3) and
+    // the barrier that waits for it (k-tile 4g + 2, after region 2): 4 k-tiles'
+    // worth
+    constexpr int kAfterCopy = 4 * BRaw<MODE>::kLoads;
+    static_assert(kAfterCopy <= 63, "vmcnt range");
+    constexpr int kVB = 8 * kCT;                                    // VALU of one step's B fragments
+    constexpr int kVA = 9;                                          // VALU of one decoded A fragment
+    const int cn = min(c + 2, k.KT - 1);
+    ADec<RT> ad;
+    // region 0: the raw A of k-tile c + 1 read; the weight scales of k-tile
+    // c + 2 load into slot SLOT
+    a_frags(st.fa[1], lds, c, 1, k.lane);
+    b_frags(st.fb[1], st.ring[SLOT], st.sb, 1);
+    b_load_sf(st.ring[SLOT], p, cn);
+    adec_read(ad, lds, c + 1, k.wave, k.nn, k.h);
+    step_mfma(st.fa[0], st.fb[0], st.acc);
+    pin(st.fb[1]);
+    interleave<RT, kVB, RT + 2 * BRaw<MODE>::kSW + 2 * RT>();
+    // region 1: half of it decoded; blocks 2h of k-tile c + 2 load
+    a_frags(st.fa[0], lds, c, 2, k.lane);
+    b_frags(st.fb[0], st.ring[SLOT], st.sb, 2);
+    b_load_half<MODE, 0>(st.ring[SLOT], p, cn);
+    adec_write<RT, 0, (RT + 1) / 2>(ad, lds, c + 1, k.wave, k.lane);
+    step_mfma(st.fa[1], st.fb[1], st.acc);
+    pin(st.fb[0]);
+    interleave<RT, kVB + kVA * ((RT + 1) / 2), RT + kCT + (RT + 1) / 2>();
+    // region 2: the rest decoded
+    a_frags(st.fa[1], lds, c, 3, k.lane);
+    b_frags(st.fb[1], st.ring[SLOT], st.sb, 3);
+    adec_write<RT, (RT + 1) / 2, RT>(ad, lds, c + 1, k.wave, k.lane);
+    step_mfma(st.fa[0], st.fb[0], st.acc);
+    pin(st.fb[1]);
+    interleave<RT, kVB + kVA * (RT / 2), RT + RT / 2>();
+    // every wave's part of the A of k-tile c + 1 written (and its reads of
+    // ah[c % 2] done); once a stage, its copy of raw stage g + 1 landed
+    if (CC == 2) __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAfterCopy) & lgkmcnt_zero());
+    else __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // region 3: step 0 of k-tile c + 1 read and decoded; blocks 2h + 1 of
+    // k-tile c + 2 load into slot SLOT. The copy of raw stage g + 2 (into raw
+    // buffer g % 2) issues with the weight loads it will be waited for with:
+    // vmcnt drains in order, so a copy issued earlier would hold up the next
+    // wait for the weights by a memory latency
+    if (CC == 2) a_stage_load<RT, kCoh>(lds, ap, k.wave, min(c / kStage + 2, k.NS - 1));
+    b_load_half<MODE, 1>(st.ring[SLOT], p, cn);
+    half2v sb1[kCT];
+    b_scales(st.ring[NXT], sel, sb1);
+    a_frags(st.fa[0], lds, c + 1, 0, k.lane);
+    b_frags(st.fb[0], st.ring[NXT], sb1, 0);
+    step_mfma(st.fa[1], st.fb[1], st.acc);
+    pin(st.fb[0]);
+    interleave<RT, kVB + 4 * kCT, RT + kCT>();
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) st.sb[j] = sb1[j];
+}
+
+// Blocks of one or two row tiles: each wave decodes its own A fragments from
+// the raw stage -- RT of them a K-step, no more than it decodes for B -- which
+// saves the decoded tile's LDS traffic and leaves one barrier per raw stage
+// instead of one per k-tile.
+template <int RT>
+struct ARaw {
+    uint4 a[RT];                    // codes of chunk 2 (c % 4) + h of rows 32 i + nn
+    uint32_t asf[RT];               // their 4 block scales of k-tile c
+};
+
+template <int RT>
+__device__ __forceinline__ void a_read(ARaw<RT>& r, const ALds& lds, int c, int nn, int h) {
+    const int buf = (c / kStage) & 1, cc = c % kStage;
+    const int pos = chunk_swizzle(2 * cc + h, nn) * 16;       // rows 32 i + nn: same low bits
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        r.a[i] = *reinterpret_cast<const uint4*>(&lds.u.raw.codes[buf][(32 * i + nn) * kARowBytes + pos]);
+        r.asf[i] = *reinterpret_cast<const uint32_t*>(&lds.u.raw.sf[buf][(32 * i + nn) * kASfBytes + 4 * cc]);
+    }
+}
+
+template <int RT>
+__device__ __forceinline__ void a_own_frags(half8 (&fa)[RT], const ARaw<RT>& ar, const half2v (&sa)[RT], int s) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const uint32_t w = s == 0 ? ar.a[i].x : s == 1 ? ar.a[i].y : s == 2 ? ar.a[i].z : ar.a[i].w;
+        fa[i] = nvfp4x8_to_f16(w, s < 2 ? splat_lo(sa[i]) : splat_hi(sa[i]));
+    }
+}
+
+template <int RT>
+__device__ __forceinline__ void a_scales(const ARaw<RT>& ar, int h, half2v (&sa)[RT]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) sa[i] = e4m3x2_to_f16(ar.asf[i] >> (16 * h));
+}
+
+template <int RT>
+__device__ __forceinline__ void pin_own(half8 (&fa)[RT], half8 (&fb)[kCT]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i) asm volatile("" : "+v"(fa[i]));
+    pin(fb);
+}
+
+template <int MODE, int RT>
+struct KStateOwn {
+    floatx16 acc[RT][kCT];
+    BRaw<MODE> ring[2];             // weight k-tile c in slot c % 2
+    ARaw<RT> ar[2];                 // raw A of k-tile c in slot c % 2
+    half8 fa[2][RT], fb[2][kCT];    // fragments of the current and the next K-step
+    half2v sa[RT], sb[kCT];         // the current k-tile's block scales
+};
+
+// One k-tile c of the own-decode form: 4 K-step regions; while the MFMAs of
+// step s run the wave decodes the fragments of step s + 1 (in the last region
+// those of step 0 of k-tile c + 1), the weights of k-tile c + 2 load into ring
+// slot c % 2 and the raw A of k-tile c + 2 is read into A slot c % 2. A barrier in
+// k-tile 4g + 2 publishes raw stage g + 1 (copied during k-tile 4g - 2) and
+// frees raw buffer g % 2 for stage g + 2: every read of stage g was issued by
+// then (the raw A of k-tile c is read during k-tile c - 2).
+template <int MODE, int RT, bool kCoh, int CC>
+__device__ __forceinline__ void ktile_own(KStateOwn<MODE, RT>& st, ALds& lds, const ASrc& ap, const BSrc& p,
+                                          const uint32_t (&sel)[2], const KPos& k, int c) {
+    constexpr int d = CC & 1, SLOT = d, NXT = d ^ 1;
+    constexpr int kAfterCopy = 4 * BRaw<MODE>::kLoads;
+    static_assert(kAfterCopy <= 63, "vmcnt range");
+    constexpr int kV = 8 * (RT + kCT);                              // VALU of one step's fragments
+    const int cn = min(c + 2, k.KT - 1);
+    // region 0
+    a_own_frags(st.fa[1], st.ar[d], st.sa, 1);
+    b_frags(st.fb[1], st.ring[SLOT], st.sb, 1);
+    b_load_sf(st.ring[SLOT], p, cn);
+    step_mfma(st.fa[0], st.fb[0], st.acc);
+    pin_own(st.fa[1], st.fb[1]);
+    interleave<RT, kV, 2 * BRaw<MODE>::kSW>();
+    // region 1
+    a_own_frags(st.fa[0], st.ar[d], st.sa, 2);
+    b_frags(st.fb[0], st.ring[SLOT], st.sb, 2);
+    b_load_half<MODE, 0>(st.ring[SLOT], p, cn);
+    step_mfma(st.fa[1], st.fb[1], st.acc);
+    pin_own(st.fa[0], st.fb[0]);
+    interleave<RT, kV, kCT>();
+    if (CC == 2) {
+        // every wave: its reads of stage g done, its copy of stage g + 1 landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAfterCopy) & lgkmcnt_zero());
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // region 2
+    a_own_frags(st.fa[1], st.ar[d], st.sa, 3);
+    b_frags(st.fb[1], st.ring[SLOT], st.sb, 3);
+    step_mfma(st.fa[0], st.fb[0], st.acc);
+    pin_own(st.fa[1], st.fb[1]);
+    interleave<RT, kV, 0>();
+    // region 3: step 0 of k-tile c + 1; the copy of raw stage g + 2 (into raw
+    // buffer g % 2, free since the barrier) issues with the weight loads it
+    // will be waited for with
+    half2v sa1[RT], sb1[kCT];
+    a_scales(st.ar[d ^ 1], k.h, sa1);
+    b_scales(st.ring[NXT], sel, sb1);
+    a_own_frags(st.fa[0], st.ar[d ^ 1], sa1, 0);
+    b_frags(st.fb[0], st.ring[NXT], sb1, 0);
+    if (CC == 2) a_stage_load<RT, kCoh>(lds, ap, k.wave, min(c / kStage + 2, k.NS - 1));
+    b_load_half<MODE, 1>(st.ring[SLOT], p, cn);
+    a_read(st.ar[d], lds, cn, k.nn, k.h);
+    step_mfma(st.fa[1], st.fb[1], st.acc);
+    pin_own(st.fa[0], st.fb[0]);
+    interleave<RT, kV + 2 * (RT + kCT), kCT + 2 * RT>();
+#pragma unroll
+    for (int i = 0; i < RT; ++i) st.sa[i] = sa1[i];
+#pragma unroll
+    for (int j = 0; j < kCT; ++j) st.sb[j] = sb1[j];
+}
+
+// The epilogue of a wave's block, one 32 x 32 tile (GEMM1: a gate tile and
+// its up tile) at a time, the wave's two slabs alternating.
+template <int MODE, int RT, bool kPub>
+__device__ __forceinline__ void epilogue(const floatx16 (&acc)[RT][kCT], const ExpArgs& a, ALds& lds, int e, int row0,
+                                         int cb, int wave, int lane, const uint32_t (&vmask)[4]) {
+    if (MODE == 1) {
+        const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
+#define MOE_EPI1(i)                                                                                          \
+    if (RT > i) swiglu_quant_tile<kPub>(acc[RT > i ? i : 0][0], acc[RT > i ? i : 0][1], ga, uc, lane, vmask[i], a, \
+                                        row0 + 32 * i, 32 * cb, lds.u.slab[wave][i & 1])
+        MOE_EPI1(0); MOE_EPI1(1); MOE_EPI1(2); MOE_EPI1(3);
+#undef MOE_EPI1
+    } else {
+        const float alpha = a.w.g2_alphas[e];
+#define MOE_EPI2(i, j) \
+    if (RT > i) bf16_tile(acc[RT > i ? i : 0][j], alpha, lane, vmask[i], a, row0 + 32 * i, 64 * cb + 32 * j, \
+                          lds.u.slab[wave][j])
+        MOE_EPI2(0, 0); MOE_EPI2(0, 1); MOE_EPI2(1, 0); MOE_EPI2(1, 1);
+        MOE_EPI2(2, 0); MOE_EPI2(2, 1); MOE_EPI2(3, 0); MOE_EPI2(3, 1);
+#undef MOE_EPI2
+    }
+}
+
 // One wave's block: rows [row0, row0 + 32 RT) of expert e, column block cb
 // (computed but not stored when store is false: a column group past the end).
 // vmask[i]: bit r is set when row 32 i + r of the block has a route.
@@ -402,19 +636,20 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
     const int h = lane >> 5, nn = lane & 31, n = lane & 15, hh = (lane >> 4) & 1;
     const int K = MODE == 1 ? a.H : a.I;
     const int NS = K / (64 * kStage);
+    constexpr bool kCoh = kPub && MODE == 2;
 
     BSrc p;
     if (MODE == 1) {
-        const int pair0 = cb * kCT;                                 // 4 pairs: 64 intermediates
+        const int pair0 = cb * kCT;                                 // 2 pairs: 32 intermediates
         p.b = buffer_rsrc(a.w.w13 + e * a.w.w13_expert_stride_bytes + pair0 * a.w.w13_pair_stride_bytes);
         p.bs = buffer_rsrc(a.w.w13_sf + e * a.w.w13_sf_expert_stride_bytes + pair0 * a.w.w13_sf_pair_stride_bytes);
         p.b_step = (int)a.w.w13_pair_stride_bytes;
         p.bs_step = (int)a.w.w13_sf_pair_stride_bytes;
-        // column nn of tile 2t + g: pair 2t + nn / 16, half g, row n
+        // column nn of tile g: pair nn / 16, half g, row n
         p.b_off = hh * (uint32_t)p.b_step + (uint32_t)(2 * h * 16 + n) * 16;
         p.bs_off = hh * (uint32_t)p.bs_step + 64 * h + 4 * (n >> 1);
     } else {
-        const int pair0 = cb * kCT;                                 // 4 pairs: 128 output columns
+        const int pair0 = cb * kCT;                                 // 2 pairs: 64 output columns
         p.b = buffer_rsrc(a.w.w2 + e * a.w.w2_expert_stride_bytes + pair0 * a.w.w2_pair_stride_bytes);
         p.bs = buffer_rsrc(a.w.w2_sf + e * a.w.w2_sf_expert_stride_bytes + pair0 * a.w.w2_sf_pair_stride_bytes);
         p.b_step = (int)a.w.w2_pair_stride_bytes;
@@ -432,120 +667,84 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
         sel[1] = sel[0] + 0x0101u;
     }
 
-    floatx16 acc[RT][kCT];
+    KPos k;
+    k.KT = NS * kStage;
+    k.NS = NS;
+    k.wave = wave;
+    k.lane = lane;
+    k.nn = nn;
+    k.h = h;
+    if constexpr (RT <= 2) {
+        KStateOwn<MODE, RT> st;
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < kCT; ++j)
+            for (int j = 0; j < kCT; ++j)
 #pragma unroll
-            for (int x = 0; x < 16; ++x) acc[i][j][x] = 0.0f;
-
-    // Software pipeline over k-tiles c (A stage g = c / 4, buffer g % 2; ring
-    // slot c % 2 for the weights, c % 2 for the A fragments' raw data). Each
-    // k-tile is 4 step regions of RT x 4 MFMAs; while the MFMAs of step s run,
-    // the fragments of step s + 1 are decoded, and in the last region those of
-    // step 0 of k-tile c + 1, while the weights and A data of k-tile c + 2 load
-    // into the slots that k-tile c has finished with. A barrier in k-tile
-    // 4g + 2 publishes A stage g + 1 (copied during k-tile 4g - 2) and frees
-    // buffer g % 2 for stage g + 2: every read of stage g was issued by then
-    // (the A data of k-tile c is read during k-tile c - 2). Past the end the
-    // copies repeat the last stage into the free buffer.
-    const int KT = NS * kStage;
-    static_assert(kAhead == 2, "ring slots c % 2");
-    // weight loads issued between one stage copy (k-tile 4g - 2, step 3) and
-    // the barrier that waits for it (k-tile 4g + 2, after step 1): 4 k-tiles'
-    // worth
-    constexpr int kAfterCopy = 4 * BRaw<MODE>::kLoads < 63 ? 4 * BRaw<MODE>::kLoads : 63;
-
-    a_stage_load<kPub && MODE == 2>(lds, ap, wave, 0);
-    a_stage_load<kPub && MODE == 2>(lds, ap, wave, min(1, NS - 1));
-    BRaw<MODE> ring[2];
-    b_load(ring[0], p, 0);
-    b_load(ring[1], p, min(1, KT - 1));
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-    __syncthreads();
-    ARaw<RT> ar[2];
-    a_read(ar[0], lds, 0, 0, nn, h);
-    a_read(ar[1], lds, 0, min(1, KT - 1) % kStage, nn, h);
-    half2v sa[RT], sb[kCT];
-    Frags<RT> f[2];
-    tile_scales(ar[0], ring[0], h, sel, sa, sb);
-    decode_step(ar[0], ring[0], sa, sb, 0, f[0]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    for (int c0 = 0; c0 < KT; c0 += kStage) {
-        const int g = c0 / kStage;
-#pragma unroll
-        for (int cc = 0; cc < kStage; ++cc) {
-            const int c = c0 + cc;
-            const int d = cc & 1;                      // c % 2
-            const int cn = min(c + 2, KT - 1);
-            // step 0, 1, 2: decode the next step of this k-tile; the weight
-            // scales, then blocks 2h, of k-tile c + 2 load into slot d
-            decode_step(ar[d], ring[d], sa, sb, 1, f[1]);
-            b_load_sf(ring[d], p, cn);
-            step_mfma(f[0], acc);
-            pin(f[1]);
-            interleave<RT>(2 * BRaw<MODE>::kSW);
-            decode_step(ar[d], ring[d], sa, sb, 2, f[0]);
-            b_load_half<MODE, 0>(ring[d], p, cn);
-            step_mfma(f[1], acc);
-            pin(f[0]);
-            interleave<RT>(kCT);
-            if (cc == 2) {
-                // every wave: its reads of stage g done, its copy of stage g + 1 landed
-                __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kAfterCopy) & lgkmcnt_zero());
-                __syncthreads();
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            decode_step(ar[d], ring[d], sa, sb, 3, f[1]);
-            step_mfma(f[0], acc);
-            pin(f[1]);
-            interleave<RT>(0);
-            // step 3: k-tile c + 1 step 0 decoded; blocks 2h + 1 of k-tile c + 2
-            // load into slot d, its A data into A slot d
-            {
-                half2v sa1[RT], sb1[kCT];
-                tile_scales(ar[d ^ 1], ring[d ^ 1], h, sel, sa1, sb1);
-                decode_step(ar[d ^ 1], ring[d ^ 1], sa1, sb1, 0, f[0]);
-                // the copy of A stage g + 2 (into buffer g % 2, free since the
-                // barrier) issues with the weight loads it will be waited for
-                // with: vmcnt drains in order, so a copy issued earlier would
-                // hold up the next wait for the weights by a full memory latency
-                if (cc == 2) a_stage_load<kPub && MODE == 2>(lds, ap, wave, min(g + 2, NS - 1));
-                b_load_half<MODE, 1>(ring[d], p, cn);
-                a_read(ar[d], lds, (cn / kStage) & 1, cn % kStage, nn, h);
-                step_mfma(f[1], acc);
-                pin(f[0]);
-                interleave<RT>(kCT + 2 * RT);
-#pragma unroll
-                for (int i = 0; i < RT; ++i) sa[i] = sa1[i];
-#pragma unroll
-                for (int j = 0; j < kCT; ++j) sb[j] = sb1[j];
-            }
+                for (int x = 0; x < 16; ++x) st.acc[i][j][x] = 0.0f;
+        // Prologue: raw stages 0 and 1, weight k-tiles 0 and 1, the raw A of
+        // k-tiles 0 and 1, the fragments of step 0.
+        a_stage_load<RT, kCoh>(lds, ap, wave, 0);
+        a_stage_load<RT, kCoh>(lds, ap, wave, min(1, NS - 1));
+        b_load(st.ring[0], p, 0);
+        b_load(st.ring[1], p, min(1, k.KT - 1));
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+        __syncthreads();
+        a_read(st.ar[0], lds, 0, nn, h);
+        a_read(st.ar[1], lds, min(1, k.KT - 1), nn, h);
+        a_scales(st.ar[0], h, st.sa);
+        b_scales(st.ring[0], sel, st.sb);
+        a_own_frags(st.fa[0], st.ar[0], st.sa, 0);
+        b_frags(st.fb[0], st.ring[0], st.sb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int c0 = 0; c0 < k.KT; c0 += kStage) {
+            ktile_own<MODE, RT, kCoh, 0>(st, lds, ap, p, sel, k, c0);
+            ktile_own<MODE, RT, kCoh, 1>(st, lds, ap, p, sel, k, c0 + 1);
+            ktile_own<MODE, RT, kCoh, 2>(st, lds, ap, p, sel, k, c0 + 2);
+            ktile_own<MODE, RT, kCoh, 3>(st, lds, ap, p, sel, k, c0 + 3);
         }
-    }
-
-    if (!store) return;
-    // epilogue, one 32 x 32 tile (GEMM1: a gate tile and its up tile) at a time
-    if (MODE == 1) {
-        const float ga = a.w.g1_alphas[e], uc = a.w.g1_scale_c[e];
-#define MOE_EPI1(i, t)                                                                          \
-    if (RT > i) swiglu_quant_tile<kPub>(acc[RT > i ? i : 0][2 * t], acc[RT > i ? i : 0][2 * t + 1], ga, uc, lane, \
-                                        vmask[i], a, row0 + 32 * i, 64 * cb + 32 * t, lds.slab[wave][t])
-        MOE_EPI1(0, 0); MOE_EPI1(0, 1); MOE_EPI1(1, 0); MOE_EPI1(1, 1);
-        MOE_EPI1(2, 0); MOE_EPI1(2, 1); MOE_EPI1(3, 0); MOE_EPI1(3, 1);
-#undef MOE_EPI1
+        // the epilogue's slabs reuse the raw stages: every wave's copies landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+        __syncthreads();
+        if (store) epilogue<MODE, RT, kPub>(st.acc, a, lds, e, row0, cb, wave, lane, vmask);
     } else {
-        const float alpha = a.w.g2_alphas[e];
-#define MOE_EPI2(i, j) \
-    if (RT > i) bf16_tile(acc[RT > i ? i : 0][j], alpha, lane, vmask[i], a, row0 + 32 * i, 128 * cb + 32 * j, \
-                          lds.slab[wave][j & 1])
-        MOE_EPI2(0, 0); MOE_EPI2(0, 1); MOE_EPI2(0, 2); MOE_EPI2(0, 3);
-        MOE_EPI2(1, 0); MOE_EPI2(1, 1); MOE_EPI2(1, 2); MOE_EPI2(1, 3);
-        MOE_EPI2(2, 0); MOE_EPI2(2, 1); MOE_EPI2(2, 2); MOE_EPI2(2, 3);
-        MOE_EPI2(3, 0); MOE_EPI2(3, 1); MOE_EPI2(3, 2); MOE_EPI2(3, 3);
-#undef MOE_EPI2
+        KState<MODE, RT> st;
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int j = 0; j < kCT; ++j)
+#pragma unroll
+                for (int x = 0; x < 16; ++x) st.acc[i][j][x] = 0.0f;
+        // Prologue: raw stages 0 and 1, weight k-tiles 0 and 1, the A of
+        // k-tile 0 decoded, the fragments of its step 0.
+        a_stage_load<RT, kCoh>(lds, ap, wave, 0);
+        a_stage_load<RT, kCoh>(lds, ap, wave, min(1, NS - 1));
+        b_load(st.ring[0], p, 0);
+        b_load(st.ring[1], p, min(1, k.KT - 1));
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+        __syncthreads();
+        {
+            ADec<RT> ad;
+            adec_read(ad, lds, 0, wave, nn, h);
+            adec_write<RT, 0, RT>(ad, lds, 0, wave, lane);
+        }
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
+        __syncthreads();
+        b_scales(st.ring[0], sel, st.sb);
+        a_frags(st.fa[0], lds, 0, 0, lane);
+        b_frags(st.fb[0], st.ring[0], st.sb, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-tiles four at a time (one raw stage)
+        for (int c0 = 0; c0 < k.KT; c0 += kStage) {
+            ktile<MODE, RT, kCoh, 0>(st, lds, ap, p, sel, k, c0);
+            ktile<MODE, RT, kCoh, 1>(st, lds, ap, p, sel, k, c0 + 1);
+            ktile<MODE, RT, kCoh, 2>(st, lds, ap, p, sel, k, c0 + 2);
+            ktile<MODE, RT, kCoh, 3>(st, lds, ap, p, sel, k, c0 + 3);
+        }
+        // the epilogue's slabs reuse the raw stages: every wave's copies landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+        __syncthreads();
+        if (store) epilogue<MODE, RT, kPub>(st.acc, a, lds, e, row0, cb, wave, lane, vmask);
     }
 }
 
@@ -703,13 +902,14 @@ __device__ __forceinline__ void tiled_item(const ExpArgs& a, ALds& lds, int bx, 
 template <typename T>
 using KernArg = const T __attribute__((address_space(4)))*;
 
-// Both GEMMs in one launch, one persistent workgroup per CU looping over the
+// Both GEMMs in one launch, persistent workgroups (two a CU) looping over the
 // queues' items. A GEMM2 item only waits for GEMM1 items that running
 // workgroups have taken (a queue yields all its GEMM1 items before any GEMM2
 // item, and a workgroup holds a taken item only while its current one waits
 // for nothing), so every wait ends. The last workgroup out returns the queue
 // counters to 0 for the next call on the same routing.
-__global__ void __launch_bounds__(64 * kWaves) tiled_fused_kernel(ExpArgs a, int ncg1, int ncb1, int ncg2, int ncb2) {
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kWgPerCu)))
+tiled_fused_kernel(ExpArgs a, int ncg1, int ncb1, int ncg2, int ncb2) {
     __shared__ ALds lds;
     __shared__ int s_next;
     __shared__ uint32_t s_done;
@@ -759,7 +959,7 @@ int launch_tiled(const ExpArgs& a, hipStream_t s) {
     // the routed row blocks are read from the metadata on the device; the
     // queues' item indices are 24-bit
     const int nx = (int)(a.L.rows_max / kBlockRows);
-    const int ncb1 = a.I / 64, ncb2 = a.H / 128;   // column blocks of one wave
+    const int ncb1 = a.I / 32, ncb2 = a.H / 64;    // column blocks of one wave
     const int ncg1 = (ncb1 + kWaves - 1) / kWaves, ncg2 = (ncb2 + kWaves - 1) / kWaves;
     if ((int64_t)((nx + kXcds - 1) / kXcds) * (ncg1 + ncg2) >= (1 << 24))
         return fail(MOE_EUNSUPPORTED, "moe_experts_fwd: too many row blocks for the work queues");
@@ -775,9 +975,9 @@ int launch_tiled(const ExpArgs& a, hipStream_t s) {
             return fail(MOE_ELAUNCH, "moe_experts_fwd: cannot read the device's compute unit count");
         if (dev < kMaxDevices) s_cus[dev].store(cus, std::memory_order_relaxed);
     }
-    // one workgroup per CU (a workgroup takes a whole CU's registers), a
+    // two workgroups per CU (each wave takes half of a SIMD's registers), a
     // multiple of the 8 XCDs
-    const int grid = (cus + kXcds - 1) / kXcds * kXcds;
+    const int grid = (kWgPerCu * cus + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL(tiled_fused_kernel, dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a, ncg1, ncb1, ncg2, ncb2);
     return MOE_OK;
 }
