@@ -152,32 +152,39 @@ __device__ void topk_rank(const RouteArgs& a, int t, bool active, int lane, int 
     }
 }
 
-// A 64-bit value of lane i ^ m (quad xor 1 and 2) or of the mirrored lane
-// (half-row, row) by DPP, both halves with the same control.
-template <int ctrl>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, ctrl, 0xF, 0xF, true);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, true);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
 __device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
 
-// The largest 64-bit value over the wave, uniform: the maximum over each row
-// of 16 lanes by DPP, then over the four rows' lane 0, 16, 32, 48.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
-    v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
-    v = max_u64(v, dpp_u64<kDppRowHalfMirror>(v));
-    v = max_u64(v, dpp_u64<kDppRowMirror>(v));
-    uint64_t m = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
-        m = max_u64(m, ((uint64_t)hi << 32) | lo);
+// v[idx] for a wave-uniform idx < N, by a tree of selects on idx's bits (an
+// index loop would be lowered to a stack array and a load).
+template <int N>
+__device__ __forceinline__ float pick(const float* v, int idx) {
+    if constexpr (N == 1) {
+        return v[0];
+    } else {
+        const float lo = pick<N / 2>(v, idx), hi = pick<N - N / 2>(v + N / 2, idx - N / 2);
+        return idx >= N / 2 ? hi : lo;
     }
-    return m;
+}
+
+// The largest u32 over the wave, uniform: the maximum over each row of 16
+// lanes by DPP, then over the four rows' lanes 0, 16, 32, 48.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadXor2, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowHalfMirror, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowMirror, 0xF, 0xF, true));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// The largest 64-bit value over the wave, uniform: the largest high word, then
+// the largest low word among the lanes that hold it (two 32-bit maxima, each
+// step one DPP instruction, instead of a 64-bit comparison per step).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Top-k of token t by one wave, any E up to 64 kPer: K rounds of a wave-wide
@@ -187,26 +194,20 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // after each round. The K choices come out by key descending and the
 // renormalizing sum runs over them in that order, as in the rank-count form.
 // Registers and DPP only: no LDS, no barrier.
+// Expert e's selection key and score from its logit: the ordered key in the
+// high word, the complement of the index in the low word (one 64-bit
+// comparison decides key descending, index ascending).
+__device__ __forceinline__ void topk_key(const RouteArgs& a, int e, float logit, uint64_t& kk, float& sc) {
+    sc = sigmoid32(logit);
+    const uint32_t ok = order_key(a.bias ? __fadd_rn(sc, a.bias[e]) : sc);
+    kk = ((uint64_t)ok << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// The K rounds of token t over the keys the wave holds (kk[j], sc[j]: expert
+// lane + 64 j; 0 below every real composite, whose high word is non-zero).
 template <int kPer>
-__device__ void topk_max(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
-    if (a.is_padding && a.is_padding[t]) {
-        if (lane < a.K) emit(a, t, lane, -1, 0.0f, s_ids);
-        return;
-    }
-    const float* row = a.logits + (int64_t)t * a.logits_row_stride;
-    uint64_t kk[kPer];
-    float sc[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int e = lane + 64 * j;
-        kk[j] = 0u;                                // below every real composite (its high word is non-zero)
-        sc[j] = 0.0f;
-        if (e < a.E) {
-            sc[j] = sigmoid32(row[e]);
-            const uint32_t ok = order_key(a.bias ? __fadd_rn(sc[j], a.bias[e]) : sc[j]);
-            kk[j] = ((uint64_t)ok << 32) | (uint32_t)~(uint32_t)e;
-        }
-    }
+__device__ __forceinline__ void topk_rounds(const RouteArgs& a, int t, int lane, int32_t* s_ids,
+                                            uint64_t (&kk)[kPer], const float (&sc)[kPer]) {
     float total = 0.0f, my_s = 0.0f;
     int my_id = -1;
     for (int k = 0; k < a.K; ++k) {
@@ -216,10 +217,7 @@ __device__ void topk_max(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
         best = wave_max_u64(best);
         const int e = (int)~(uint32_t)best;       // uniform
         const int owner = e & 63, slot = e >> 6;
-        float s_own = sc[0];
-#pragma unroll
-        for (int j = 1; j < kPer; ++j)
-            if (j == slot) s_own = sc[j];
+        const float s_own = pick<kPer>(sc, slot);
         const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_own), owner));
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
@@ -232,25 +230,90 @@ __device__ void topk_max(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
              __fmul_rn(__fdiv_rn(my_s, __fadd_rn(total, 1e-15f)), a.route_scale), s_ids);
 }
 
+// One token, its logits loaded here (the form for many experts a lane).
+template <int kPer>
+__device__ void topk_max(const RouteArgs& a, int t, int lane, int32_t* s_ids) {
+    if (a.is_padding && a.is_padding[t]) {
+        if (lane < a.K) emit(a, t, lane, -1, 0.0f, s_ids);
+        return;
+    }
+    const float* row = a.logits + (int64_t)t * a.logits_row_stride;
+    uint64_t kk[kPer];
+    float sc[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = lane + 64 * j;
+        kk[j] = 0u;
+        sc[j] = 0.0f;
+        if (e < a.E) topk_key(a, e, row[e], kk[j], sc[j]);
+    }
+    topk_rounds<kPer>(a, t, lane, s_ids, kk, sc);
+}
+
+// The K-round form for a wave's tokens first + w, + step, ... (up to 4
+// experts a lane): the logits of up to kPre of them load together before
+// their rounds, so that a wave with several tokens waits for one memory
+// latency instead of one per token.
+template <int kPer>
+__device__ __forceinline__ void topk_max_tokens(const RouteArgs& a, int first, int step, int lane, int w,
+                                                int32_t* s_ids) {
+    constexpr int kPre = kPer <= 2 ? 4 : 2;
+    for (int base = first; base < a.T; base += kPre * step) {
+        float lg[kPre][kPer];
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int t = base + q * step + w;
+            const float* row = a.logits + (int64_t)t * a.logits_row_stride;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) lg[q][j] = t < a.T && lane + 64 * j < a.E ? row[lane + 64 * j] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) {
+            const int t = base + q * step + w;
+            if (t >= a.T) continue;                // uniform over the wave
+            if (a.is_padding && a.is_padding[t]) {
+                if (lane < a.K) emit(a, t, lane, -1, 0.0f, s_ids);
+                continue;
+            }
+            uint64_t kk[kPer];
+            float sc[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int e = lane + 64 * j;
+                kk[j] = 0u;
+                sc[j] = 0.0f;
+                if (e < a.E) topk_key(a, e, lg[q][j], kk[j], sc[j]);
+            }
+            topk_rounds<kPer>(a, t, lane, s_ids, kk, sc);
+        }
+    }
+}
+
 // Top-k of tokens [first, T) with stride `step`, one token per wave: the
 // rank count up to 64 experts (every thread of the workgroup takes part in
 // every round: it holds barriers), the K-round wave maximum beyond (measured,
 // moe_route_quant back to back: decode_b8 (E = 64) 6.4 µs by rank count, 6.7
-// by rounds; E = 128: expert_tp8_b32 (32 tokens, one workgroup) 26.2 -> 17.5
-// µs, decode_b64_zipf 17.5 -> 15.3, prefill_t4096 32.6 -> 29.2).
-__device__ void topk_tokens(const RouteArgs& a, int first, int step, int32_t* lds_topk,
+// by rounds; E = 128: expert_tp8_b32 (32 tokens, one workgroup) 26.2 µs by
+// rank count, 17.5 by rounds, 15.5 with the logits loaded ahead and the
+// 64-bit maximum as two 32-bit ones; decode_b64_zipf 17.5 -> 15.3 -> 14.5;
+// prefill_t4096 32.6 -> 29.2 -> 26.2, with the scan's batched loads).
+__device__ __forceinline__ void topk_tokens(const RouteArgs& a, int first, int step, int32_t* lds_topk,
                             int32_t* s_ids) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int base = first; base < a.T; base += step) {
-        const int t = base + w;
-        if (a.E <= kRankMaxExperts) {
+    if (a.E <= kRankMaxExperts) {
+        for (int base = first; base < a.T; base += step) {
+            const int t = base + w;
             topk_rank(a, t, t < a.T, lane, w, lds_topk, s_ids);
-            continue;
         }
-        if (t >= a.T) continue;                    // uniform over the wave
-        if (a.E <= 128) topk_max<2>(a, t, lane, s_ids);
-        else if (a.E <= 256) topk_max<4>(a, t, lane, s_ids);
-        else topk_max<kMaxPerLane>(a, t, lane, s_ids);
+    } else if (a.E <= 128) {
+        topk_max_tokens<2>(a, first, step, lane, w, s_ids);
+    } else if (a.E <= 256) {
+        topk_max_tokens<4>(a, first, step, lane, w, s_ids);
+    } else {
+        for (int base = first; base < a.T; base += step) {
+            const int t = base + w;
+            if (t < a.T) topk_max<kMaxPerLane>(a, t, lane, s_ids);   // uniform over the wave
+        }
     }
 }
 
@@ -293,7 +356,7 @@ __device__ __forceinline__ void clear_sync(const RouteArgs& a, int i, int step) 
 // from an LDS copy of the tile map.
 constexpr int kWaveMaxRoutes = 512;
 
-__device__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
+__device__ __forceinline__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
     const int El = a.local_num;
     int32_t* count = lds;                          // [El]
     int32_t* offs = count + El;                    // [El + 1]
@@ -308,12 +371,23 @@ __device__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* l
     int32_t* tile_expert = a.meta + a.L.tile_expert;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
 
+    // wave 0's local experts of routes 64 c + lane, loaded once for both passes
+    // (all in flight together: from global memory each chunk's load would
+    // otherwise wait a memory latency, twice)
+    constexpr int kChunks = kWaveMaxRoutes / 64;
+    int re[kChunks];
     if (w == 0) {
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int r = 64 * c + lane;
+            re[c] = r < R ? local_expert(a, ids[r]) : -1;
+        }
         for (int x = lane; x < El; x += 64) count[x] = 0;
         wave_lds_sync();
-        for (int base = 0; base < R; base += 64) {
-            const int r = base + lane;
-            const int e = r < R ? local_expert(a, ids[r]) : -1;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            if (64 * c >= R) break;
+            const int e = re[c];
             const uint64_t match = same_expert_lanes(e);
             if (e >= 0 && (match & lt_mask) == 0) count[e] += __popcll(match);   // one lane per expert
             wave_lds_sync();
@@ -349,9 +423,11 @@ __device__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* l
     __syncthreads();
     if (w == 0) {
         // stable ranks, chunk by chunk, scattered at once
-        for (int base = 0; base < R; base += 64) {
-            const int r = base + lane;
-            const int e = r < R ? local_expert(a, ids[r]) : -1;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            if (64 * c >= R) break;
+            const int r = 64 * c + lane;
+            const int e = re[c];
             const uint64_t match = same_expert_lanes(e);
             const int pos = e >= 0 ? running[e] + __popcll(match & lt_mask) : -1;
             wave_lds_sync();
@@ -374,7 +450,7 @@ __device__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* l
 }
 
 // The permutation metadata from the top-k ids (global or LDS). One workgroup.
-__device__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
+__device__ __forceinline__ void permute_block(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
     const int El = a.local_num;
     int32_t* cnt = lds;                           // [kRouteWaves][El]
     int32_t* count = cnt + kRouteWaves * El;      // [El]  routes per expert
@@ -535,14 +611,24 @@ __global__ void __launch_bounds__(kRouteThreads) perm_scan_kernel(RouteArgs a, i
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int32_t* cnt = a.meta + a.L.perm_counts;
     int32_t* tile_expert = a.meta + a.L.tile_expert;
-    // each thread owns a contiguous run of experts
+    // each thread owns a contiguous run of experts. Its chunk counts load
+    // kScanBatch at a time, all in flight together (a chunk's counts of
+    // consecutive experts are adjacent: the wave's loads coalesce); up to
+    // kScanBatch chunks they stay in registers for the in-place pass below.
+    constexpr int kScanBatch = 64;
     const int per = (El + kRouteThreads - 1) / kRouteThreads;
     const int e0 = tid * per, e1 = min(El, e0 + per);
+    const bool held = per == 1 && nchunks <= kScanBatch;
+    int v[kScanBatch];
     int my_total = 0;
     for (int x = e0; x < e1; ++x) {
         int c = 0;
-#pragma unroll 8
-        for (int b = 0; b < nchunks; ++b) c += cnt[(int64_t)b * El + x];   // independent loads, pipelined
+        for (int b0 = 0; b0 < nchunks; b0 += kScanBatch) {
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i) v[i] = b0 + i < nchunks ? cnt[(int64_t)(b0 + i) * El + x] : 0;
+#pragma unroll
+            for (int i = 0; i < kScanBatch; ++i) c += v[i];
+        }
         count[x] = c;
         my_total += (c + m - 1) / m * m;
     }
@@ -555,15 +641,16 @@ __global__ void __launch_bounds__(kRouteThreads) perm_scan_kernel(RouteArgs a, i
     for (int x = e0; x < e1; ++x) {
         offs[x] = acc;
         int base = acc;                            // the chunks' first rows, in place
-        for (int b0 = 0; b0 < nchunks; b0 += 8) {
-            int c[8];
+        for (int b0 = 0; b0 < nchunks; b0 += kScanBatch) {
+            if (!held) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = b0 + i < nchunks ? cnt[(int64_t)(b0 + i) * El + x] : 0;
+                for (int i = 0; i < kScanBatch; ++i) v[i] = b0 + i < nchunks ? cnt[(int64_t)(b0 + i) * El + x] : 0;
+            }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < kScanBatch; ++i)
                 if (b0 + i < nchunks) {
                     cnt[(int64_t)(b0 + i) * El + x] = base;
-                    base += c[i];
+                    base += v[i];
                 }
         }
         acc += (count[x] + m - 1) / m * m;
