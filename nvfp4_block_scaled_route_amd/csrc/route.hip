@@ -17,10 +17,13 @@
 // a second pass gives every route its rank among the earlier routes of its
 // expert (ballot matching over the expert index bits within a wave: a stable
 // counting sort, no ordering atomics, deterministic) and scatters it at once.
-// Up to 512 routes one wave counts and ranks them, chunk by chunk, while the
+// Up to 128 routes one wave counts and ranks them, chunk by chunk, while the
 // workgroup's other waves write the per-row and per-tile fields; beyond, the
 // whole workgroup does it (LDS atomics for the counts, a scan across its waves
-// for the ranks).
+// for the ranks; measured, moe_route_quant: decode_b64_zipf's 512 routes 13.8
+// -> 9.4 µs, expert_tp8_b32's 256 15.5 -> 14.3, while decode_b8's 64 take
+// 6.2 µs by one wave and 6.8 by the workgroup). Past 512 routes of more than
+// 32 tokens the grid does it (below).
 // Small batches run top-k and the permutation in one workgroup, the top-k ids
 // staying in LDS; larger ones take a top-k grid, then the permutation.
 // moe_route_quant appends the quantizer's workgroups to the first launch: they
@@ -347,14 +350,14 @@ __device__ __forceinline__ void clear_sync(const RouteArgs& a, int i, int step) 
     if (i < kQueueWords) a.meta[a.L.queue + i] = 0;
 }
 
-// The permutation metadata for up to 512 routes, by one workgroup. Wave 0
+// The permutation metadata for up to 128 routes, by one workgroup. Wave 0
 // counts the routes per expert (chunks of 64 routes, one per lane; experts in
 // runs of ceil(El / 64) per lane) and scans the padded offsets. Then, while wave
 // 0 ranks the routes and scatters them, the other waves write the per-row and
 // per-tile fields -- tile -> expert, -1 on padding rows and past the last tile,
 // the cleared sync words -- as coalesced strided stores, each row's expert read
 // from an LDS copy of the tile map.
-constexpr int kWaveMaxRoutes = 512;
+constexpr int kWaveMaxRoutes = 128;
 
 __device__ __forceinline__ void permute_small(const RouteArgs& a, const int32_t* ids, int32_t* lds) {
     const int El = a.local_num;
@@ -372,7 +375,7 @@ __device__ __forceinline__ void permute_small(const RouteArgs& a, const int32_t*
     const uint64_t lt_mask = (1ull << lane) - 1ull;
 
     // wave 0's local experts of routes 64 c + lane, loaded once for both passes
-    // (all in flight together: from global memory each chunk's load would
+    // (in flight together: from global memory each chunk's load would
     // otherwise wait a memory latency, twice)
     constexpr int kChunks = kWaveMaxRoutes / 64;
     int re[kChunks];
@@ -584,6 +587,7 @@ __global__ void __launch_bounds__(kRouteThreads) route_kernel(RouteArgs a, int m
 //            chunk's waves in LDS), added to the chunk's first row; and a
 //            share of the padding rows and of the sync words per workgroup
 constexpr int kChunk = kRouteThreads;
+constexpr int kGridPermMinRoutes = 512;           // more routes than this: the grid-wide permutation
 
 __global__ void __launch_bounds__(kRouteThreads) perm_count_kernel(RouteArgs a) {
     extern __shared__ int32_t lds[];                   // [El]
@@ -793,7 +797,7 @@ static int route_launch(const float* logits, int64_t logits_row_stride, const fl
     const int64_t R = (int64_t)T * K;
     const size_t scan_lds =
         sizeof(int32_t) * ((size_t)2 * local_num_experts + 1 + kRouteWaves + (size_t)a.L.tiles_max);
-    const bool grid_perm = T > kFusedMaxTokens && R > kWaveMaxRoutes && scan_lds <= 64 * 1024;
+    const bool grid_perm = T > kFusedMaxTokens && R > kGridPermMinRoutes && scan_lds <= 64 * 1024;
     hipStream_t s = (hipStream_t)stream;
     if (T <= kFusedMaxTokens) {
         const size_t lds = sizeof(int32_t) * (((size_t)T * K + 3) & ~(size_t)3) +
