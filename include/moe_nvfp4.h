@@ -98,7 +98,7 @@ int64_t moe_rows_max(int T, int K, int E_local, int tile_m);
  *   fin_part        [128*T]      that form's working space: per token, the fp32
  *                                partial sums of squares its workgroups exchange
  *   perm_counts     [ceil(T*K/512) * E_local]  moe_route's working space when it
- *                                routes more than 32 tokens: per chunk of 512
+ *                                routes more than 8 tokens and 512 routes: per chunk of 512
  *                                routes, the routes of each expert, then the
  *                                chunk's first row in each expert
  *   queue           [16]         (inside the first 64 words) the work queues of

@@ -23,7 +23,7 @@
 // for the ranks; measured, moe_route_quant: decode_b64_zipf's 512 routes 13.8
 // -> 9.4 µs, expert_tp8_b32's 256 15.5 -> 14.3, while decode_b8's 64 take
 // 6.2 µs by one wave and 6.8 by the workgroup). Past 512 routes of more than
-// 32 tokens the grid does it (below).
+// 8 tokens the grid does it (below).
 // Small batches run top-k and the permutation in one workgroup, the top-k ids
 // staying in LDS; larger ones take a top-k grid, then the permutation.
 // moe_route_quant appends the quantizer's workgroups to the first launch: they
@@ -36,7 +36,11 @@ constexpr int kRouteThreads = 512;                 // 8 waves
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;  // 16
 constexpr int kRankMaxExperts = 64;                // rank-count top-k up to here; the wave maximum beyond
-constexpr int kFusedMaxTokens = 32;                // one workgroup routes up to here
+// One workgroup routes up to a token a wave; more tokens take the top-k grid
+// (a token a wave) and then the permutation, since a wave's K rounds for
+// several tokens run one after another (expert_tp8_b32, 32 tokens: 14.3 µs in
+// one workgroup, 8.9 µs in the two launches).
+constexpr int kFusedMaxTokens = kRouteWaves;
 
 enum RouteMode { kTopkOnly = 0, kPermuteOnly = 1, kFused = 2 };
 
@@ -792,7 +796,7 @@ static int route_launch(const float* logits, int64_t logits_row_stride, const fl
     const int64_t qblocks = x ? ((int64_t)T * (H / 16) + kRouteThreads - 1) / kRouteThreads : 0;
     if (qblocks > 0x3FFFFFFF) return fail(MOE_EUNSUPPORTED, "%s: too large", name);
     const size_t topk_lds = topk_lds_bytes(E, K), perm_lds = permute_lds_bytes(local_num_experts, a.L.tiles_max);
-    // more than 512 routes of more than 32 tokens: the grid-wide permutation,
+    // more than 512 routes of more than 8 tokens: the grid-wide permutation,
     // as long as its scan's LDS (tile map included) fits; else one workgroup
     const int64_t R = (int64_t)T * K;
     const size_t scan_lds =
