@@ -75,19 +75,28 @@ __device__ __forceinline__ Cols<W> pack(const float v[W]) {
 }
 
 // Route row p at columns [W*c, W*c + W): with several partials their fp32 sum
-// in order, rounded once to bf16.
-template <int W>
+// in order, rounded once to bf16. With B > 1 the partials' loads go out B at
+// a time before their additions, instead of each waiting for the one before.
+template <int W, int B = 1>
 __device__ __forceinline__ Cols<W> load_row(const FinArgs& a, int p, int c) {
     const uint16_t* base = a.rows + (int64_t)p * a.rows_stride + W * c;
     Cols<W> q = load_cols<W>(base);
     if (a.n_partials == 1) return q;
     float v[W];
     unpack<W>(q, v);
-    for (int part = 1; part < a.n_partials; ++part) {
-        float u[W];
-        unpack<W>(load_cols<W>(base + part * a.partial_stride), u);
+    for (int part0 = 1; part0 < a.n_partials; part0 += B) {
+        Cols<W> u[B];
 #pragma unroll
-        for (int i = 0; i < W; ++i) v[i] = __fadd_rn(v[i], u[i]);
+        for (int j = 0; j < B; ++j)
+            if (part0 + j < a.n_partials) u[j] = load_cols<W>(base + (part0 + j) * a.partial_stride);
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (part0 + j >= a.n_partials) break;
+            float f[W];
+            unpack<W>(u[j], f);
+#pragma unroll
+            for (int i = 0; i < W; ++i) v[i] = __fadd_rn(v[i], f[i]);
+        }
     }
     return pack<W>(v);
 }
