@@ -201,11 +201,14 @@ def test_route_zero_tokens():
 
 
 @pytest.mark.parametrize("T,E,K,m", [(5, 256, 8, 16), (20, 512, 6, 32), (32, 128, 8, 16),
-                                     (16, 3, 3, 16), (33, 200, 7, 16)])
+                                     (16, 3, 3, 16), (33, 200, 7, 16), (6, 48, 8, 16),
+                                     (8, 100, 24, 16), (12, 64, 8, 16)])
 def test_route_tied_keys_both_paths(T, E, K, m):
-    """Many equal keys: the rank count (E <= 256) and the arg-max rounds (E > 256)
-    must both take ties to the lower index, in one workgroup (T <= 32) and in
-    the top-k grid (T > 32)."""
+    """Many equal keys: the rank count (E <= 64) and the arg-max rounds (E > 64,
+    2, 4 or 16 experts a lane) must both take ties to the lower index, in one
+    workgroup (T <= 8) and in the top-k grid (T > 8); and the permutation by
+    one wave (up to 128 routes), by the workgroup (8 tokens x 24: 192 routes,
+    from the top-k ids in LDS) and after the grid (from global memory)."""
     rng = np.random.default_rng(T * 7 + E)
     logits = rng.choice(np.array([-3, -0.5, 0, 0.25, 1, 4], np.float32), (T, E))
     bias = rng.choice(np.array([0.0, -0.0, 0.125], np.float32), E)
