@@ -37,13 +37,15 @@
 // One persistent workgroup per half CU takes work items -- (routed row block,
 // column group) of GEMM1, then of GEMM2 -- from 8 queues, one per XCD: the
 // routed row blocks (their count is read from the routing metadata) are split
-// into 8 equal contiguous chunks, and queue x holds chunk x's GEMM1 items, row
-// block major, then its GEMM2 items. A workgroup takes from its own XCD's queue
-// (workgroups are dealt to the 8 XCDs round robin), so the column groups of a
-// row block, and the row blocks of one expert, run on the same XCD at about
-// the same time; when that queue is empty it takes from the others, so that no
-// XCD idles while another still has work (items differ in length: a block runs
-// 1 to 4 row tiles).
+// into 8 equal contiguous chunks, and queue x holds chunk x's GEMM1 items, then
+// its GEMM2 items, each expert's run of blocks in the chunk column group major:
+// the items that read one weight column group (one per block of the expert)
+// follow one another, and those that read one block's rows are as many items
+// apart as the expert has blocks there (2 to 3 here), so both are read while
+// the XCD's L2 still holds them. A workgroup takes from its own XCD's queue
+// (workgroups are dealt to the 8 XCDs round robin); when that queue is empty it
+// takes from the others, so that no XCD idles while another still has work
+// (items differ in length: a block runs 1 to 4 row tiles).
 //
 // GEMM1's columns are arranged so that a lane holds the gate and the up value of
 // the same intermediate in two accumulators (column tiles 0 and 1 take the gate
@@ -750,6 +752,7 @@ __device__ __forceinline__ void run_block(const ExpArgs& a, ALds& lds, const ASr
 
 // The work queues (meta's queue words): queue x holds the GEMM1 items of the
 // row blocks [x bpx, (x + 1) bpx), ncg1 a block, then their GEMM2 items.
+// Position v of a queue's GEMM1 (or GEMM2) items names a cell by item_cell.
 struct Queues {
     int32_t* q;             // items taken from each queue; q[kXcds]: workgroups finished
     int nblocks, bpx, ncg1, ncg2, home;
@@ -797,6 +800,21 @@ __device__ __forceinline__ int take_item(const Queues& Q, uint32_t* done) {
     return item;
 }
 
+// The cell (row block *bx, column group *cg) at position v of one GEMM's items
+// of the chunk [b0, b0 + nb): v / ncg names a block, whose expert's blocks in
+// the chunk, [gs, ge), hold the positions [(gs - b0) ncg, (ge - b0) ncg); those
+// go column group major. Every block below the routed count belongs to an
+// expert whose padded rows start and end on block boundaries.
+__device__ __forceinline__ void item_cell(const ExpArgs& a, int b0, int nb, int v, int ncg, int* bx, int* cg) {
+    const int bm = b0 + v / ncg;
+    const int e = __builtin_amdgcn_readfirstlane(a.meta[a.L.tile_expert + bm * kBlockRows / a.tile_m]);
+    const int gs = max(__builtin_amdgcn_readfirstlane(a.meta[a.L.expert_offsets + e]) / kBlockRows, b0);
+    const int ge = min(__builtin_amdgcn_readfirstlane(a.meta[a.L.expert_offsets + e + 1]) / kBlockRows, b0 + nb);
+    const int g = ge - gs, u = v - (gs - b0) * ncg;
+    *bx = gs + u % g;
+    *cg = u / g;
+}
+
 // One work item of GEMM MODE (1: GEMM1 + SwiGLU + requant, 2: GEMM2): row
 // block bx, column group cg. GEMM1 publishes its part of a row block's
 // intermediate with agent-coherent stores and counts itself on the block's
@@ -826,7 +844,7 @@ __device__ __forceinline__ void tiled_item(const ExpArgs& a, ALds& lds, int bx, 
     const bool store = cb < ncb;
     cb = min(cb, ncb - 1);
 
-    const int nn = lane & 31, h = lane >> 5;
+    const int nn = lane & 31;
     // bit r of vmask[i]: row 32 i + r of the block has a route
     uint32_t vmask[4];
     int rt = 0;
@@ -936,9 +954,15 @@ tiled_fused_kernel(ExpArgs a, int ncg1, int ncb1, int ncg2, int ncb2) {
         asm volatile("" : "+s"(pa));
         const ExpArgs& ai = *(const ExpArgs*)pa;
         const int x = it >> 24, v = it & 0xFFFFFF;
-        const int n1 = queue_blocks(Q, x) * ncg1, b0 = x * Q.bpx;
-        if (v < n1) tiled_item<1>(ai, lds, b0 + v / ncg1, v % ncg1, ncg1, ncb1, ncg1, Q, &s_done, &s_next);
-        else tiled_item<2>(ai, lds, b0 + (v - n1) / ncg2, (v - n1) % ncg2, ncg2, ncb2, ncg1, Q, &s_done, &s_next);
+        const int nb = queue_blocks(Q, x), n1 = nb * ncg1, b0 = x * Q.bpx;
+        int bx, cg;
+        if (v < n1) {
+            item_cell(ai, b0, nb, v, ncg1, &bx, &cg);
+            tiled_item<1>(ai, lds, bx, cg, ncg1, ncb1, ncg1, Q, &s_done, &s_next);
+        } else {
+            item_cell(ai, b0, nb, v - n1, ncg2, &bx, &cg);
+            tiled_item<2>(ai, lds, bx, cg, ncg2, ncb2, ncg1, Q, &s_done, &s_next);
+        }
         __syncthreads();
         it = __builtin_amdgcn_readfirstlane(s_next);
     }
