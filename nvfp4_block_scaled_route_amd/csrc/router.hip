@@ -9,21 +9,26 @@
 // products of two fp32 values are exact in fp64, so the only error before the
 // final rounding is that of the fp64 sums (about 2^-53 relative per step).
 //
-// Up to 256 tokens, one wave computes 8 tokens x 1 expert over all of D: per round a lane loads
-// 4 consecutive weights and the same 4 columns of the 8 token rows (16-byte
-// loads, a wave covering 256 consecutive columns), four rounds' loads issued
-// together (decode is bound by the latency of these loads, not their bytes),
-// then the 8 sums are reduced across the wave. A workgroup's 4 waves take 4 consecutive experts of the same
-// 8 tokens, so the token rows they all read are shared in the CU's cache. At
-// decode sizes the weight ([E, D] fp32) is read once from memory.
+// Up to 256 tokens a workgroup computes 8 tokens x NE experts (NE = 1, 2 or 4
+// as the tokens grow, rl_experts). Its 4 waves take every fourth 256-column
+// round of D: per round a lane loads 4 consecutive weights of each expert and
+// the same 4 columns of the 8 token rows (16-byte loads; each token column
+// serves the NE experts), and a wave issues the loads of up to 4 of its rounds
+// (2 at NE = 4) together, so that at D <= 4096 it waits for memory once or
+// twice: decode is bound by that latency, not by the bytes. Each wave then
+// folds its 8 sums of an expert across its lanes -- over lane bits 5, 4 and 3
+// a lane keeps half of its token sums and adds its partner's, then bits 2, 1
+// and 0 sum the one left: 10 exchanges for the 8 sums -- and wave 0 adds the 4
+// waves' sums in wave order. The token rows are read by the E / NE workgroups
+// of a token group from the cache; the weight ([E, D] fp32) once from memory,
+// then by the other token groups from the cache.
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kRlTokens = 8;                 // tokens per wave
-constexpr int kRlThreads = 256;              // 4 experts per workgroup
-constexpr int kRlWaves = kRlThreads / 64;
-constexpr int kRlUnroll = 4;                 // rounds of 256 columns per batch of loads
+constexpr int kRlTokens = 8;                 // tokens per workgroup
+constexpr int kRlThreads = 256;
+constexpr int kRlWaves = kRlThreads / 64;    // waves splitting D
 
 struct RlArgs {
     const float* x;
@@ -33,12 +38,6 @@ struct RlArgs {
     float* logits;
 };
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-
 __device__ __forceinline__ double dot4(const float4& a, const float4& b, double acc) {
     acc = __dadd_rn(acc, __dmul_rn((double)a.x, (double)b.x));
     acc = __dadd_rn(acc, __dmul_rn((double)a.y, (double)b.y));
@@ -47,55 +46,96 @@ __device__ __forceinline__ double dot4(const float4& a, const float4& b, double 
     return acc;
 }
 
+// Lane l holds, for tokens j and j + H of its 2H sums, its own and lane
+// l ^ M's; it keeps token j + H where bit M is set and j elsewhere, adding
+// the partner's sum of the token it keeps (fp64 addition commutes, so both
+// lanes of a pair form the same sum).
+template <int H>
+__device__ __forceinline__ void fold(const double (&in)[2 * H], double (&out)[H], int lane, int mask) {
+    const bool up = (lane & mask) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+        const double keep = up ? in[j + H] : in[j], give = up ? in[j] : in[j + H];
+        out[j] = keep + __shfl_xor(give, mask);
+    }
+}
+
+// NE experts (rows e0 .. e0 + NE - 1; past E they repeat row E - 1 and are not
+// written), U of a wave's rounds per batch of loads.
+template <int NE, int U>
 __global__ void __launch_bounds__(kRlThreads) router_logits_kernel(RlArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int e = (int)blockIdx.y * kRlWaves + (threadIdx.x >> 6);
+    __shared__ double part[kRlWaves][NE][kRlTokens];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e0 = (int)blockIdx.y * NE;
     const int t0 = (int)blockIdx.x * kRlTokens;
-    if (e >= a.E) return;
     const int nt = min(kRlTokens, a.T - t0);
-    double acc[kRlTokens];
+    double acc[NE][kRlTokens];
 #pragma unroll
-    for (int i = 0; i < kRlTokens; ++i) acc[i] = 0.0;
-    const float* wrow = a.w + (int64_t)e * a.D;
+    for (int j = 0; j < NE; ++j)
+#pragma unroll
+        for (int i = 0; i < kRlTokens; ++i) acc[j][i] = 0.0;
+    const float* wrow[NE];
+#pragma unroll
+    for (int j = 0; j < NE; ++j) wrow[j] = a.w + (int64_t)min(e0 + j, a.E - 1) * a.D;
     const float* xrow = a.x + (int64_t)t0 * a.x_row_stride;
-    // kRlUnroll rounds of 256 columns at a time: all their loads issue before
-    // the first product, so a row of D columns costs D / 1024 memory round
-    // trips rather than D / 256
-    int d0 = 0;
-    for (; d0 + 256 * kRlUnroll <= a.D; d0 += 256 * kRlUnroll) {
-        float4 w4[kRlUnroll], x4[kRlUnroll][kRlTokens];
+    const int nr = (a.D + 255) / 256;           // rounds; the last may be partial (D % 4 == 0)
+    // The loads carry no lane-dependent branch (those made the compiler wait
+    // for one round's loads before issuing the next): a lane past D in the
+    // last round reads an in-bounds column and its products are dropped by a
+    // select, and the rows of tokens past T repeat the last token's row (their
+    // sums are never written).
+    int64_t xo[kRlTokens];
 #pragma unroll
-        for (int u = 0; u < kRlUnroll; ++u) {
-            const int d = d0 + 256 * u + 4 * lane;
-            w4[u] = *reinterpret_cast<const float4*>(wrow + d);
+    for (int i = 0; i < kRlTokens; ++i) xo[i] = (int64_t)min(i, nt - 1) * a.x_row_stride;
+    for (int r0 = wave; r0 < nr; r0 += kRlWaves * U) {
+        float4 w4[U][NE], x4[U][kRlTokens];
 #pragma unroll
-            for (int i = 0; i < kRlTokens; ++i)
-                if (i < nt) x4[u][i] = *reinterpret_cast<const float4*>(xrow + (int64_t)i * a.x_row_stride + d);
+        for (int u = 0; u < U; ++u) {
+            if (r0 + kRlWaves * u >= nr) break;          // uniform
+            const int d = min(256 * (r0 + kRlWaves * u) + 4 * lane, a.D - 4);
+#pragma unroll
+            for (int j = 0; j < NE; ++j) w4[u][j] = *reinterpret_cast<const float4*>(wrow[j] + d);
+#pragma unroll
+            for (int i = 0; i < kRlTokens; ++i) x4[u][i] = *reinterpret_cast<const float4*>(xrow + xo[i] + d);
         }
 #pragma unroll
-        for (int u = 0; u < kRlUnroll; ++u)
+        for (int u = 0; u < U; ++u) {
+            if (r0 + kRlWaves * u >= nr) break;
+            const bool in = 256 * (r0 + kRlWaves * u) + 4 * lane < a.D;
 #pragma unroll
-            for (int i = 0; i < kRlTokens; ++i)
-                if (i < nt) acc[i] = dot4(x4[u][i], w4[u], acc[i]);
+            for (int j = 0; j < NE; ++j)
+#pragma unroll
+                for (int i = 0; i < kRlTokens; ++i) {
+                    const double v = dot4(x4[u][i], w4[u][j], acc[j][i]);
+                    acc[j][i] = in ? v : acc[j][i];
+                }
+        }
     }
-    for (int d = d0 + 4 * lane; d < a.D; d += 256) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wrow + d);
-        float4 x4[kRlTokens];
 #pragma unroll
-        for (int i = 0; i < kRlTokens; ++i)
-            if (i < nt) x4[i] = *reinterpret_cast<const float4*>(xrow + (int64_t)i * a.x_row_stride + d);
-#pragma unroll
-        for (int i = 0; i < kRlTokens; ++i)
-            if (i < nt) acc[i] = dot4(x4[i], w4, acc[i]);
+    for (int j = 0; j < NE; ++j) {
+        double s4[4], s2[2], s1[1];
+        fold<4>(acc[j], s4, lane, 32);
+        fold<2>(s4, s2, lane, 16);
+        fold<1>(s2, s1, lane, 8);
+        double v = s1[0];                       // token lane >> 3, summed over lane bits 3-5
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 1);
+        if ((lane & 7) == 0) part[wave][j][lane >> 3] = v;
     }
-    float mine = 0.0f;
+    __syncthreads();
+    const int i = lane & 7, j = lane >> 3;      // wave 0: lane 8 j + i sums token i of expert e0 + j
+    if (wave == 0 && j < NE && i < nt && e0 + j < a.E) {
+        double sum = part[0][j][i];
 #pragma unroll
-    for (int i = 0; i < kRlTokens; ++i) {
-        const double s = wave_sum_d(acc[i]);
-        if (lane == i) mine = __double2float_rn(s);
+        for (int w = 1; w < kRlWaves; ++w) sum += part[w][j][i];
+        a.logits[(int64_t)(t0 + i) * a.E + e0 + j] = __double2float_rn(sum);
     }
-    if (lane < nt) a.logits[(int64_t)(t0 + lane) * a.E + e] = mine;
 }
+
+// Experts a workgroup takes: more tokens share each expert's weight row among
+// fewer token groups, and fewer workgroups then re-read the token rows.
+static int rl_experts(int T) { return T <= 16 ? 1 : T <= 64 ? 2 : 4; }
 
 // Many tokens: an LDS-tiled product on the fp64 matrix instruction. A
 // workgroup computes 16 tokens x 64 experts, a wave 16 x 16 with
@@ -202,8 +242,11 @@ static void logits_launch(const float* x, int64_t x_row_stride, const float* w, 
         hipLaunchKernelGGL(router_logits_tiled_kernel, grid, dim3(256), 0, s, a);
         return;
     }
-    const dim3 grid((unsigned)((T + kRlTokens - 1) / kRlTokens), (unsigned)((E + kRlWaves - 1) / kRlWaves));
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRlThreads), 0, s, a);
+    const int ne = rl_experts(T);
+    const dim3 grid((unsigned)((T + kRlTokens - 1) / kRlTokens), (unsigned)((E + ne - 1) / ne));
+    if (ne == 1) hipLaunchKernelGGL((router_logits_kernel<1, 4>), grid, dim3(kRlThreads), 0, s, a);
+    else if (ne == 2) hipLaunchKernelGGL((router_logits_kernel<2, 4>), grid, dim3(kRlThreads), 0, s, a);
+    else hipLaunchKernelGGL((router_logits_kernel<4, 2>), grid, dim3(kRlThreads), 0, s, a);
 }
 
 }  // namespace moe

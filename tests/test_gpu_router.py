@@ -62,11 +62,14 @@ def test_router_logits_prefill_sampled():
 
 
 @pytest.mark.parametrize("T,D,E,pad", [(1, 4, 1, 0), (7, 60, 3, 4), (8, 256, 64, 0), (9, 2052, 257, 8),
-                                       (33, 4096, 128, 0), (5, 6144, 16, 4), (300, 1000, 100, 4),
+                                       (33, 4096, 128, 0), (5, 6144, 16, 4), (40, 512, 7, 4),
+                                       (100, 1000, 130, 4), (256, 2052, 65, 0), (300, 1000, 100, 4),
                                        (257, 64, 64, 0), (320, 4100, 130, 0)])
 def test_router_logits_shapes(T, D, E, pad):
-    """Up to 256 tokens the wave-per-expert kernel, beyond it the LDS-tiled one
-    (partial token, expert and column tiles)."""
+    """Up to 256 tokens the kernel of 8-token groups whose waves split D (1, 2
+    or 4 experts a workgroup as T grows: partial token groups, expert groups
+    and 256-column rounds), beyond it the LDS-tiled one (partial token, expert
+    and column tiles)."""
     rng = np.random.default_rng(T * D + E)
     x = rng.standard_normal((T, D)).astype(np.float32)
     w = (rng.standard_normal((E, D)) / np.sqrt(D)).astype(np.float32)
