@@ -2,7 +2,11 @@
 
 A step is the whole hot path on one batch of seeded synthetic input:
 moe_route -> nvfp4_quant -> moe_experts_fwd -> moe_finalize, replayed from HIP
-graphs (one per weight copy). The weights rotate over enough copies (>= 1 GiB)
+graphs of 16 consecutive steps (as a model's forward pass holds its layers
+back to back in one graph; the steps past a multiple of 16 one to a graph).
+``ms_per_step_one_per_graph`` replays every step from a graph of its own,
+which adds a graph launch to each. Each step has its own weight copy: the
+weights rotate over enough copies (>= 1 GiB)
 that the 256 MB Infinity Cache cannot hold them between uses, so weight bytes
 come from HBM (the cold-cache timing the flashinfer_ops page's tuning
 configuration asks for). Inputs are resident in HBM before timing starts.
@@ -32,6 +36,7 @@ import argparse
 import json
 import os
 import sys
+import math
 import time
 
 import numpy as np
@@ -58,6 +63,7 @@ def parse():
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense f16 matrix peak
+LAYER_GROUP = 16                  # layer steps a timed graph holds
 MFMA_F64_PEAK_TFLOPS = 78.6       # MI355X fp64 peak (matrix and vector)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
@@ -298,7 +304,10 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
         LY.run_layer(bufs, x, gscale, logits, None, None, w, norm_w, wl.gain_center, wl.eps,
                      bool(wl.weight_before_norm), slices=sl, stream=stream)
 
-    # eager warm-up, then one graph per weight copy, captured on a side stream
+    # eager warm-up, then the graphs, captured on a side stream: one per weight
+    # copy holding one layer step, and graphs of LAYER_GROUP consecutive steps,
+    # weight copies rotating, as a model's forward pass holds its layers back
+    # to back in one graph
     for i in range(3):
         step(weights[i % copies])
     torch.cuda.synchronize()
@@ -310,19 +319,15 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
         with torch.cuda.graph(g, stream=cap):
             step(w)
         graphs.append(g)
+    q, r = divmod(steps, LAYER_GROUP)
+    gsteps = []
+    for k in range(copies // math.gcd(LAYER_GROUP, copies) if q else 0):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for j in range(LAYER_GROUP):
+                step(weights[(k * LAYER_GROUP + j) % copies])
+        gsteps.append(g)
     torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % copies].replay()
-    torch.cuda.synchronize()
-
-    # timed region: `steps` whole-layer steps
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % copies].replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / steps
-    bufs.check_sync()            # no wait gave up: the timed steps computed valid rows
 
     # the dominant kernel, timed with HIP events on the stream it is launched on
     counts = bufs.meta[bufs.layout.expert_counts:bufs.layout.expert_counts + wl.E].cpu().numpy()
@@ -380,10 +385,34 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
     k_ms = float(np.mean([a.elapsed_time(b) for a, b in evg])) / group
     achieved = ab["total"] / (k_ms * 1e-3) / 1e9
 
+    # the layer steps: `warmup` untimed replays, then the timed region (after
+    # the expert-step timing above, so that the chip is at its working clock)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+
+    def timed(replays):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for g in replays:
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    # timed region: `steps` whole-layer steps, LAYER_GROUP to a replay (the
+    # rest one to a replay); then the same steps one to a replay, each of which
+    # then also pays a graph launch
+    ms_per_step = timed([gsteps[i % len(gsteps)] for i in range(q)] +
+                        [graphs[(q * LAYER_GROUP + i) % copies] for i in range(r)]) / steps
+    ms_single = timed([graphs[i % copies] for i in range(steps)]) / steps
+    bufs.check_sync()            # no wait gave up: the timed steps computed valid rows
+
     routes = wl.T * wl.K
     rec = {
         "value": routes / (ms_per_step * 1e-3), "unit": "routed rows/s", "ms_per_step": ms_per_step,
-        "steps": steps, "warmup": warmup,
+        "steps": steps, "warmup": warmup, "steps_per_graph": LAYER_GROUP if q else 1,
+        "ms_per_step_one_per_graph": ms_single,
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
                    "tp": wl.tp, "tile_m": wl.tile_m, "weight_copies": copies},
     }
@@ -435,7 +464,7 @@ def measure(N, LY, W, name: str, steps: int, warmup: int, rotate_bytes: float, e
                 extra["moe_experts_fwd_bf16"] = time_bf16(N, W, wl, x, bufs, counts, n_k)
         extra.update(time_router(N, W, wl, bufs, n_k))
         rec["extra_kernels"] = extra
-    del graphs, g_steps, weights, bufs
+    del graphs, gsteps, g_steps, weights, bufs
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return rec, inp
@@ -459,6 +488,7 @@ def main():
         "unit": "routed rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "steps_per_graph": head["steps_per_graph"], "ms_per_step_one_per_graph": head["ms_per_step_one_per_graph"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16", "data": "synthetic",
         "config": head["config"],
