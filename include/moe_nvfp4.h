@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 7
+#define MOE_NVFP4_ABI_VERSION 8
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* null pointer, bad size, stride or alignment */
@@ -432,11 +432,15 @@ int moe_experts_fwd_noalloc(const uint8_t* a_codes, const uint8_t* a_sf, int32_t
  * (w2's global scale times up/gate, formed by the caller); w->g1_scale_c is
  * not read. Products of bf16 and NVFP4 values are exact in fp32.
  *   x       device bf16 [T, H], row stride x_row_stride elements (>= H, % 8 == 0)
- *   meta    moe_route's metadata for the same T, K, E_local, tile_m (read only)
+ *   meta    moe_route's metadata for the same T, K, E_local, tile_m; its sync
+ *           words are used and left at 0, and sync_status reports a wait that
+ *           gave up, as in moe_experts_fwd
  *   inter   device bf16 [rows_max, I] out: the intermediate, permuted row order
  *   rows    device bf16 [rows_max, rows_stride] out, as moe_experts_fwd
- * Two launches on `stream`. H % 64 == 0, I % 64 == 0, both <= MOE_MAX_HIDDEN. */
-int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+ * One launch on `stream` where H and I are multiples of 256 and T*K >= 128
+ * (GEMM2's workgroups wait for GEMM1's through the sync words), else two.
+ * H % 64 == 0, I % 64 == 0, both <= MOE_MAX_HIDDEN. */
+int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, int32_t* meta,
                           const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
                           int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
                           void* stream);
@@ -451,11 +455,13 @@ int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, const int32_t
  *   inter[p,i] = bf16(silu(acc1_gate[i]) * acc1_up[i])
  *   rows[p, n] = bf16(sum_i inter[p, i] * w2[e, n, i])
  *   x      device bf16 [T, H], row stride x_row_stride elements (>= H, % 8 == 0)
- *   meta   moe_route's metadata for the same T, K, E_local, tile_m (read only)
+ *   meta   moe_route's metadata for the same T, K, E_local, tile_m; its sync
+ *          words are used as by moe_experts_fwd_w4a16
  *   w13    device bf16 [E_local, 2I, H], w2 device bf16 [E_local, H, I], contiguous
  *   inter  device bf16 [rows_max, I] out;  rows as moe_experts_fwd
- * Two launches on `stream`. H % 64 == 0, I % 64 == 0, both <= MOE_MAX_HIDDEN. */
-int moe_experts_fwd_bf16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+ * One launch on `stream` where H and I are multiples of 256, else two.
+ * H % 64 == 0, I % 64 == 0, both <= MOE_MAX_HIDDEN. */
+int moe_experts_fwd_bf16(const uint16_t* x, int64_t x_row_stride, int32_t* meta,
                          const uint16_t* w13, const uint16_t* w2, int T, int K, int E_local, int H,
                          int I, int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
                          void* stream);

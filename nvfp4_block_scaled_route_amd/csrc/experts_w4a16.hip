@@ -30,6 +30,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr int kW16Threads = 256;   // 4 independent waves per workgroup
+constexpr int kCacheSc1 = 16;      // buffer-instruction cache policy: agent-coherent (sc1)
 
 struct W16Args {
     const uint16_t* x;          // GEMM1: bf16 [T, x_row_stride]; GEMM2: the intermediate
@@ -152,7 +153,9 @@ __device__ __forceinline__ void w16_stream(const W16Streams& p, int KT, floatx4&
 }
 
 // GEMM1 epilogue: lane (q, n) holds rows 4q + i of intermediate 16j + n.
-template <bool kBf16>
+// kPub: GEMM2 workgroups of the same launch read the intermediate, so it is
+// written with agent-coherent stores.
+template <bool kBf16, bool kPub = false>
 __device__ __forceinline__ void w16_gemm1_epilogue(const W16Args& a, const RowTile& rt, int ex, int j, int n, int q,
                                                    const floatx4& acc_g, const floatx4& acc_u) {
     const ExpArgs& e = a.e;
@@ -168,7 +171,11 @@ __device__ __forceinline__ void w16_gemm1_epilogue(const W16Args& a, const RowTi
         const float eg = expf(-__builtin_fabsf(g));
         const float sig = __fdiv_rn(g >= 0.0f ? 1.0f : eg, __fadd_rn(1.0f, eg));
         const float h = __fmul_rn(__fmul_rn(g, sig), u);
-        if ((rt.vmask >> m) & 1u) a.inter[(int64_t)(rt.row0 + m) * e.I + j * 16 + n] = (uint16_t)f32_to_bf16(h);
+        if ((rt.vmask >> m) & 1u) {
+            uint16_t* dst = a.inter + (int64_t)(rt.row0 + m) * e.I + j * 16 + n;
+            if (kPub) __hip_atomic_store(dst, (uint16_t)f32_to_bf16(h), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *dst = (uint16_t)f32_to_bf16(h);
+        }
     }
 }
 
@@ -259,40 +266,32 @@ constexpr int kW16Chunk = 256;                  // columns per LDS chunk
 constexpr int kW16RowBytes = kW16Chunk * 2 + 16;
 constexpr int kW16BufBytes = 16 * kW16RowBytes;
 
-// Runs all KT k-tiles (KT % D == 0): the weights stream D k-tiles ahead (4,
-// one chunk, or 8, two), the activations one chunk ahead. srow: the bf16 row
-// this thread stages (row threadIdx.x / 16 of the tile), 32 bytes at column
-// 16 (threadIdx.x % 16) of each chunk.
-template <bool kBf16, int D>
-__device__ __forceinline__ void w16_wg_run(const W16Streams& p, const uint16_t* srow, int KT, uint8_t* lds,
-                                           floatx4& acc0, floatx4& acc1) {
+// 16 bytes of a staged row: plain, or agent-coherent (sc1: the row was
+// published by another XCD in this launch) through a buffer load on `base`.
+template <bool kCoh>
+__device__ __forceinline__ u32x4 w16_row16(const uint16_t* base, const uint16_t* p) {
+    if constexpr (kCoh) {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+        return __builtin_amdgcn_raw_buffer_load_b128(r, (int)((p - base) * 2), 0, kCacheSc1);
+    } else {
+        return *reinterpret_cast<const u32x4*>(p);
+    }
+}
+
+// The chunk loop of w16_wg_run once chunk 0 is in LDS and the first D weight
+// k-tiles are in flight in st: s0, s1 hold this thread's 32 bytes of chunk 1.
+template <bool kBf16, int D, bool kCoh>
+__device__ __forceinline__ void w16_wg_loop(W16Stage<kBf16> (&st)[D], const W16Streams& p, const uint16_t* base,
+                                            const uint16_t* srow, int KT, uint8_t* lds, u32x4 s0, u32x4 s1,
+                                            floatx4& acc0, floatx4& acc1) {
     constexpr int CK = kW16Chunk / 64;          // k-tiles per chunk
     constexpr int H = D / CK;                   // chunks per pass over the pipeline
-    static_assert(D % CK == 0, "the pipeline holds whole chunks");
     const int lane = threadIdx.x & 63, t = threadIdx.x;
     const int NC = KT / CK;
     uint8_t* wpos = lds + (t >> 4) * kW16RowBytes + (t & 15) * 32;
     const uint8_t* rpos = lds + (lane & 15) * kW16RowBytes + (lane >> 4) * 32;
-    const u32x4* src = reinterpret_cast<const u32x4*>(srow + (t & 15) * 16);
-    W16Stage<kBf16> st[D];
-    // chunk 0's rows, then the first weights and chunk 1's rows go out before
-    // chunk 0 is stored, so that their latencies overlap
-    const u32x4 f0 = src[0], f1 = src[1];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-        w16_load_w<kBf16>(st[d], p, d);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    u32x4 s0 = f0, s1 = f1;
-    if (NC > 1) {
-        s0 = src[kW16Chunk / 8];                // chunk 1: + 256 bf16 = 32 x 16 bytes
-        s1 = src[kW16Chunk / 8 + 1];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    reinterpret_cast<u32x4*>(wpos)[0] = f0;
-    reinterpret_cast<u32x4*>(wpos)[1] = f1;
-    __syncthreads();
+    const uint16_t* src = srow + (t & 15) * 16;
     for (int c0 = 0; c0 < NC; c0 += H) {
 #pragma unroll
         for (int h = 0; h < H; ++h) {
@@ -314,11 +313,46 @@ __device__ __forceinline__ void w16_wg_run(const W16Streams& p, const uint16_t* 
             }
             __syncthreads();
             if (c + 2 < NC) {
-                s0 = src[(c + 2) * (kW16Chunk / 8)];
-                s1 = src[(c + 2) * (kW16Chunk / 8) + 1];
+                s0 = w16_row16<kCoh>(base, src + (c + 2) * kW16Chunk);
+                s1 = w16_row16<kCoh>(base, src + (c + 2) * kW16Chunk + 8);
             }
         }
     }
+}
+
+// Runs all KT k-tiles (KT % D == 0): the weights stream D k-tiles ahead (4,
+// one chunk, or 8, two), the activations one chunk ahead. srow: the bf16 row
+// this thread stages (row threadIdx.x / 16 of the tile), 32 bytes at column
+// 16 (threadIdx.x % 16) of each chunk.
+template <bool kBf16, int D>
+__device__ __forceinline__ void w16_wg_run(const W16Streams& p, const uint16_t* srow, int KT, uint8_t* lds,
+                                           floatx4& acc0, floatx4& acc1) {
+    constexpr int CK = kW16Chunk / 64;
+    static_assert(D % CK == 0, "the pipeline holds whole chunks");
+    const int t = threadIdx.x;
+    const int NC = KT / CK;
+    uint8_t* wpos = lds + (t >> 4) * kW16RowBytes + (t & 15) * 32;
+    const uint16_t* src = srow + (t & 15) * 16;
+    W16Stage<kBf16> st[D];
+    // chunk 0's rows, then the first weights and chunk 1's rows go out before
+    // chunk 0 is stored, so that their latencies overlap
+    const u32x4 f0 = w16_row16<false>(srow, src), f1 = w16_row16<false>(srow, src + 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        w16_load_w<kBf16>(st[d], p, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    u32x4 s0 = f0, s1 = f1;
+    if (NC > 1) {
+        s0 = w16_row16<false>(srow, src + kW16Chunk);
+        s1 = w16_row16<false>(srow, src + kW16Chunk + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    reinterpret_cast<u32x4*>(wpos)[0] = f0;
+    reinterpret_cast<u32x4*>(wpos)[1] = f1;
+    __syncthreads();
+    w16_wg_loop<kBf16, D, false>(st, p, srow, srow, KT, lds, s0, s1, acc0, acc1);
 }
 
 // GEMM1: the 4 units of a workgroup are intermediate pairs of one tile (I/16
@@ -380,6 +414,101 @@ __global__ void __launch_bounds__(kW16Threads) w16_wg_gemm2_kernel(W16Args a) {
     w16_gemm2_epilogue<kBf16>(e, rt, ex, c, n, q, acc0, acc1);
 }
 
+// Both GEMMs in one launch (H and I multiples of 256): workgroups [0, g1_blocks)
+// are w16_wg_gemm1_kernel's, the rest w16_wg_gemm2_kernel's, as in the W4A4
+// one-launch kernel (experts.hip). A GEMM1 workgroup writes its part of the
+// bf16 intermediate with agent-coherent stores, waits until they have
+// completed and adds 1 to its tile's ready counter (meta's sub_sync). A GEMM2
+// workgroup issues its first weight k-tiles, waits (bounded, sync_status 1 if
+// it gives up) until all I/64 GEMM1 workgroups of its tile have added theirs,
+// counts itself on the tile's done counter -- the last of the tile's H/128
+// returns both counters to 0 -- and stages the intermediate with agent-coherent
+// loads. Workgroups are dispatched in index order, so every GEMM1 workgroup
+// has been dispatched before a GEMM2 workgroup waits, and GEMM1 waits for
+// nothing.
+template <bool kBf16>
+__global__ void __launch_bounds__(kW16Threads) w16_fused_kernel(W16Args a, uint32_t g1_blocks) {
+    constexpr int D = 4;
+    __shared__ __align__(16) uint8_t lds[2 * kW16BufBytes];
+    const ExpArgs& e = a.e;
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (blockIdx.x < g1_blocks) {
+        const uint32_t unit = blockIdx.x * (kW16Threads / 64) + wave;
+        const uint32_t n1 = e.I >> 4;
+        const int sub = (int)(unit / n1), j = (int)(unit - sub * n1);
+        const RowTile rt = row_tile(e, sub, n);     // one tile for the whole workgroup
+        if (rt.e < 0) return;
+        const int ex = rt.e;
+        W16Streams p;
+        if constexpr (kBf16) {
+            const uint8_t* w13 = e.w.w13 + ex * e.w.w13_expert_stride_bytes;
+            p.p0 = w13 + ((int64_t)(16 * j + n) * e.H + 16 * q) * 2;
+            p.p1 = w13 + ((int64_t)(e.I + 16 * j + n) * e.H + 16 * q) * 2;
+        } else {
+            p.p0 = e.w.w13 + ex * e.w.w13_expert_stride_bytes + j * e.w.w13_pair_stride_bytes + lane * 16;
+            p.p1 = e.w.w13_sf + ex * e.w.w13_sf_expert_stride_bytes + j * e.w.w13_sf_pair_stride_bytes + lane * 2;
+        }
+        int tok = e.meta[e.L.perm2tok + rt.row0 + (threadIdx.x >> 4)];
+        if (tok < 0 || tok >= e.T) tok = 0;
+        floatx4 acc_g = {0, 0, 0, 0}, acc_u = {0, 0, 0, 0};
+        w16_wg_run<kBf16, D>(p, a.x + (int64_t)tok * a.x_row_stride, e.H >> 6, lds, acc_g, acc_u);
+        w16_gemm1_epilogue<kBf16, true>(a, rt, ex, j, n, q, acc_g, acc_u);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(e.sync + kSubSyncStride * sub, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    const uint32_t unit = (blockIdx.x - g1_blocks) * (kW16Threads / 64) + wave;
+    const uint32_t n2 = e.H >> 5;
+    const int sub = (int)(unit / n2), c = (int)(unit - sub * n2);
+    const RowTile rt = row_tile(e, sub, n);
+    if (rt.e < 0) return;
+    const int ex = rt.e;
+    W16Streams p;
+    if constexpr (kBf16) {
+        const uint8_t* w2 = e.w.w2 + ex * e.w.w2_expert_stride_bytes;
+        p.p0 = w2 + ((int64_t)(32 * c + n) * e.I + 16 * q) * 2;
+        p.p1 = w2 + ((int64_t)(32 * c + 16 + n) * e.I + 16 * q) * 2;
+    } else {
+        p.p0 = e.w.w2 + ex * e.w.w2_expert_stride_bytes + c * e.w.w2_pair_stride_bytes + lane * 16;
+        p.p1 = e.w.w2_sf + ex * e.w.w2_sf_expert_stride_bytes + c * e.w.w2_sf_pair_stride_bytes + lane * 2;
+    }
+    W16Stage<kBf16> st[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        w16_load_w<kBf16>(st[d], p, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    int32_t* ready = e.sync + kSubSyncStride * sub;
+    if (wave == 0) wait_ready(ready, e.I >> 6, e.status);
+    __syncthreads();
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(ready + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (e.H >> 7) - 1) {
+        __hip_atomic_store(ready, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ready + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the tile's intermediate rows, staged as in w16_wg_run but agent-coherent
+    const int t = threadIdx.x;
+    const int KT = e.I >> 6, NC = KT / (kW16Chunk / 64);
+    const uint16_t* srow = a.inter + (int64_t)(rt.row0 + (t >> 4)) * e.I;
+    const uint16_t* src = srow + (t & 15) * 16;
+    const u32x4 f0 = w16_row16<true>(a.inter, src), f1 = w16_row16<true>(a.inter, src + 8);
+    u32x4 s0 = f0, s1 = f1;
+    if (NC > 1) {
+        s0 = w16_row16<true>(a.inter, src + kW16Chunk);
+        s1 = w16_row16<true>(a.inter, src + kW16Chunk + 8);
+    }
+    uint8_t* wpos = lds + (t >> 4) * kW16RowBytes + (t & 15) * 32;
+    reinterpret_cast<u32x4*>(wpos)[0] = f0;
+    reinterpret_cast<u32x4*>(wpos)[1] = f1;
+    __syncthreads();
+    floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    w16_wg_loop<kBf16, D, true>(st, p, a.inter, srow, KT, lds, s0, s1, acc0, acc1);
+    w16_gemm2_epilogue<kBf16>(e, rt, ex, c, n, q, acc0, acc1);
+}
+
 static int w16_depth(int kt, int cap) {
     for (int d = cap; d > 1; d >>= 1)
         if (kt % d == 0) return d;
@@ -390,7 +519,7 @@ static int w16_depth(int kt, int cap) {
 // the weight bytes of NVFP4 ones, so their pipeline is at most 2 deep (8 KB in
 // flight per wave either way).
 template <bool kBf16>
-static int w16_launch(const char* name, const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+static int w16_launch(const char* name, const uint16_t* x, int64_t x_row_stride, int32_t* meta,
                       const moe_nvfp4_weights& w, int T, int K, int E_local, int H, int I, int tile_m,
                       uint16_t* inter, uint16_t* rows, int64_t rows_stride, hipStream_t s) {
     if (x_row_stride < H || x_row_stride % 8)
@@ -403,7 +532,7 @@ static int w16_launch(const char* name, const uint16_t* x, int64_t x_row_stride,
     a.e.w = w; a.e.T = T; a.e.E_local = E_local; a.e.H = H; a.e.I = I; a.e.tile_m = tile_m;
     a.e.rows = rows; a.e.rows_stride = rows_stride;
     a.e.a_codes = nullptr; a.e.a_sf = nullptr; a.e.inter_codes = nullptr; a.e.inter_sf = nullptr;
-    a.e.sync = nullptr; a.e.status = nullptr;
+    a.e.sync = meta + a.e.L.sub_sync; a.e.status = meta + a.e.L.sync_status;
     if (a.e.L.rows_max == 0) return MOE_OK;
     const int64_t subs = a.e.L.rows_max / 16;
     const int64_t units1 = subs * (I / 16), units2 = subs * (H / 32);
@@ -411,6 +540,18 @@ static int w16_launch(const char* name, const uint16_t* x, int64_t x_row_stride,
     const int wpb = kW16Threads / 64;
     const dim3 g1((unsigned)((units1 + wpb - 1) / wpb)), g2((unsigned)((units2 + wpb - 1) / wpb)), b(kW16Threads);
     const int cap = kBf16 ? 2 : 4;
+    // both workgroup forms in one launch where they both apply (and the
+    // intermediate's byte offsets fit the coherent loads' 32 bits) and the
+    // weight stream is long enough for the hand-over's fixed cost (the
+    // intermediate's agent-coherent stores completing, the polls) to pay.
+    // Measured, back to back: BF16 at decode_b8 84.7 -> 81.1 us, W4A16 at
+    // decode_b64_zipf (512 routes) 132.7 -> 126.5 us, but W4A16 at decode_b8
+    // (64 routes, 112 MB of weights) 28.0 -> 28.8 us
+    const bool one_launch = kBf16 || (int64_t)T * K >= 128;
+    if (one_launch && H % kW16Chunk == 0 && I % kW16Chunk == 0 && a.e.L.rows_max * I * 2 < (1ll << 31)) {
+        hipLaunchKernelGGL((w16_fused_kernel<kBf16>), dim3(g1.x + g2.x), b, 0, s, a, g1.x);
+        return check_launch(name);
+    }
     // the workgroup forms where the shape allows: whole 256-column chunks, and
     // for GEMM2 four output pairs in one tile (H % 128 == 0). The weights
     // stream one chunk (4 k-tiles) ahead: 8 measured no faster, and neither did
@@ -451,7 +592,7 @@ static int w16_shape_check(const char* name, int T, int K, int E_local, int H, i
 
 }  // namespace moe
 
-extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, int32_t* meta,
                                      const moe_nvfp4_weights* w, int T, int K, int E_local, int H, int I,
                                      int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
                                      void* stream) {
@@ -470,7 +611,7 @@ extern "C" int moe_experts_fwd_w4a16(const uint16_t* x, int64_t x_row_stride, co
                              rows_stride, (hipStream_t)stream);
 }
 
-extern "C" int moe_experts_fwd_bf16(const uint16_t* x, int64_t x_row_stride, const int32_t* meta,
+extern "C" int moe_experts_fwd_bf16(const uint16_t* x, int64_t x_row_stride, int32_t* meta,
                                     const uint16_t* w13, const uint16_t* w2, int T, int K, int E_local, int H,
                                     int I, int tile_m, uint16_t* inter, uint16_t* rows, int64_t rows_stride,
                                     void* stream) {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = N.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 7
+    assert L.moe_abi_version() == 8
 
 
 @pytest.mark.parametrize("T,K,E,m", [(4, 2, 8, 16), (8, 8, 64, 16), (64, 8, 128, 16),

@@ -15,7 +15,7 @@ from oracle.finalize import finalize_routes
 from oracle.layer import rel_l2
 from oracle.routing import route as o_route
 
-from .gpu_common import DEV, dev, host, say
+from .gpu_common import DEV, dev, host, say, sync_counters
 
 pytestmark = pytest.mark.gpu
 
@@ -35,12 +35,20 @@ def _compare(wl: W.Workload):
     out = torch.empty((T, H), dtype=torch.int16, device=DEV)
     say(f"moe_experts_fwd_bf16 {wl.name} T={T} H={H} I={I} E={E} K={K} m={m}")
     N.moe_route(dev(inp.logits), None, None, K, 1.0, m, 0, E, ids, wts, meta)
-    N.moe_experts_fwd_bf16(dev(inp.x_bf16), meta, dev(w13), dev(w2), T, K, E, H, I, m, inter, rows)
+    xd, w13d, w2d = dev(inp.x_bf16), dev(w13), dev(w2)
+    N.moe_experts_fwd_bf16(xd, meta, w13d, w2d, T, K, E, H, I, m, inter, rows)
+    first = host(rows)
+    # a second call on the same metadata (the one-launch form's counters are
+    # back at 0): the same rows bit for bit
+    N.moe_experts_fwd_bf16(xd, meta, w13d, w2d, T, K, E, H, I, m, inter, rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(rows), first)
     e2p_dev = meta[L.exp2perm:L.exp2perm + T * K]
     N.moe_finalize(rows, 1, 0, e2p_dev, wts, dev(inp.norm_weight_bf16), wl.gain_center, wl.eps,
                    bool(wl.weight_before_norm), T, K, H, out)
     torch.cuda.synchronize()
     meta_h, inter_h, rows_h, out_h = host(meta), host(inter), host(rows), host(out)
+    assert meta_h[L.sync_status] == 0 and not sync_counters(meta_h, L).any()
     oids, ow = o_route(inp.logits, None, K)
     assert np.array_equal(host(ids), oids)
     p = meta_h[L.exp2perm:L.exp2perm + T * K]
@@ -64,10 +72,12 @@ def test_bf16_layer_on_workload(name):
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 32),
                                          (40, 256, 128, 4, 2, 64), (3, 1024, 512, 4, 2, 16),
-                                         (7, 512, 192, 8, 2, 16)])
+                                         (7, 512, 192, 8, 2, 16), (40, 512, 256, 4, 2, 64)])
 def test_bf16_layer_shapes(T, H, I, E, K, m):
     """Per-wave kernels at pipeline depths 1 (H/64 = 5, I/64 = 3) and 2, and the
-    LDS-staged workgroup kernels (K a multiple of 256); tiles of 16 to 64 rows."""
+    LDS-staged workgroup kernels (K a multiple of 256); tiles of 16 to 64 rows.
+    H and I both multiples of 256 take the one-launch form (H = 1024/I = 512,
+    and H = 512/I = 256 with 64-row tiles)."""
     wl = dataclasses.replace(W.WORKLOADS["tiny"], name=f"bf16_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E,
                              K=K, tile_m=m, seed=13)
     _compare(wl)

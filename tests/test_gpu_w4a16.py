@@ -16,7 +16,7 @@ from oracle.layer import rel_l2
 from oracle.routing import route as o_route
 from oracle.w4a16 import experts_w4a16, fold_scalars
 
-from .gpu_common import DEV, dev, host, say
+from .gpu_common import DEV, dev, host, say, sync_counters
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +41,14 @@ def _run(wl: W.Workload, fill=0x3F3F):
     say(f"moe_experts_fwd_w4a16 {wl.name} T={T} H={H} I={I} E={E} K={K} m={m}")
     N.moe_route(dev(inp.logits), None, None, K, 1.0, m, 0, E, ids, wts, meta)
     N.moe_experts_fwd_w4a16(x, meta, w, T, K, E, H, I, m, inter, rows)
+    first = host(rows)
+    # a second call on the same metadata: the one-launch form's counters are
+    # back at 0 after each call, and the rows come out bit for bit the same
+    N.moe_experts_fwd_w4a16(x, meta, w, T, K, E, H, I, m, inter, rows)
+    torch.cuda.synchronize()
     meta_h = host(meta)
+    assert meta_h[L.sync_status] == 0 and not sync_counters(meta_h, L).any()
+    assert np.array_equal(host(rows), first)
     e2p = meta_h[L.exp2perm:L.exp2perm + T * K]
     N.moe_finalize(rows, 1, 0, dev(e2p.astype(np.int32)), wts, dev(inp.norm_weight_bf16), wl.gain_center, wl.eps,
                    bool(wl.weight_before_norm), T, K, H, out)
@@ -80,12 +87,16 @@ def test_w4a16_on_workload(name):
 
 
 @pytest.mark.parametrize("T,H,I,E,K,m", [(6, 320, 192, 8, 2, 16), (5, 384, 256, 8, 3, 32),
-                                         (3, 1024, 512, 4, 2, 16), (40, 256, 128, 4, 2, 64), (7, 512, 192, 8, 2, 16)])
+                                         (3, 1024, 512, 4, 2, 16), (40, 256, 128, 4, 2, 64), (7, 512, 192, 8, 2, 16),
+                                         (72, 512, 256, 4, 2, 64), (48, 256, 768, 6, 3, 32)])
 def test_w4a16_shapes(T, H, I, E, K, m):
     """Per-wave kernels at pipeline depths 1 (H/64 = 5, I/64 = 3), 2 and 4, and
     the LDS-staged workgroup kernels (K a multiple of 256: GEMM1 at H = 256,
     512, 1024, GEMM2 at I = 256, 512, one or several chunks); tiles of 16 to 64
-    rows, several routed 16-row tiles per expert."""
+    rows, several routed 16-row tiles per expert. H and I both multiples of 256
+    with at least 128 routes take the one-launch form (H = 512/I = 256 with
+    64-row tiles, whose empty 16-row tiles neither publish nor wait; H = 256/
+    I = 768, three chunks); H = 1024/I = 512 with 6 routes stays in two."""
     wl = dataclasses.replace(W.WORKLOADS["tiny"], name=f"w4a16_{T}_{H}_{I}_{E}_{K}_{m}", T=T, H=H, I=I, E=E,
                              K=K, tile_m=m, seed=11)
     _compare(wl)
