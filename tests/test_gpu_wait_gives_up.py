@@ -54,6 +54,42 @@ def test_expert_step_wait_gives_up():
     bufs.check_sync()
 
 
+def test_tiled_expert_step_wait_gives_up():
+    """The persistent register-tiled kernel (many routes per expert): block 0's
+    GEMM2 items wait on the same counter word (its first 16-row tile's)."""
+    wl = dataclasses.replace(W.WORKLOADS["tiny"], name="tiled_wait", T=256, H=256, I=256, E=8, K=2, tile_m=128,
+                             seed=19)                                   # T*K >= 32 E: the tiled kernel
+    inp = W.make_inputs(wl, a2_gscale=1.0)                              # only the failure report is checked
+    w = upload_weights(inp)
+    bufs = LY.Buffers(LY.LayerShape(wl.T, wl.H, wl.I, wl.E, wl.K, wl.tile_m, 1), DEV)
+    L = bufs.layout
+    logits, x, gs = dev(inp.logits), dev(inp.x_bf16), dev(inp.a1_gscale)
+
+    def route():
+        N.moe_route_quant(logits, None, None, wl.K, 1.0, wl.tile_m, 0, wl.E, bufs.ids, bufs.weights, bufs.meta,
+                          x, gs, bufs.a_codes, bufs.a_sf)
+
+    def experts():
+        N.moe_experts_fwd(bufs.a_codes, bufs.a_sf, bufs.meta, w, wl.T, wl.K, wl.E, wl.H, wl.I, wl.tile_m,
+                          bufs.inter_codes, bufs.inter_sf, bufs.rows[0])
+
+    route()
+    bufs.meta[L.sub_sync] = UNREACHABLE
+    say("moe_experts_fwd (tiled) T=256 H=256 I=256 E=8 with block 0's ready counter preset out of reach")
+    experts()
+    torch.cuda.synchronize()
+    meta = host(bufs.meta)
+    assert meta[L.sync_status] == 1
+    assert not sync_counters(meta, L).any()
+    assert not meta[L.queue:L.queue + 16].any()
+    with pytest.raises(N.MoeError):
+        bufs.check_sync()
+    route()
+    experts()
+    torch.cuda.synchronize()
+    bufs.check_sync()
+
+
 def test_bf16_experts_wait_gives_up():
     wl = dataclasses.replace(W.WORKLOADS["tiny"], name="bf16_wait", T=8, H=256, I=256, E=8, K=2, tile_m=16,
                              seed=17)                                   # H, I % 256 == 0: one launch
