@@ -15,7 +15,7 @@ from nvfp4_block_scaled_route_amd import layer as LY
 from nvfp4_block_scaled_route_amd import native as N
 from nvfp4_block_scaled_route_amd import workloads as W
 
-from .gpu_common import DEV, dev, host, say, sync_counters, upload_weights
+from .gpu_common import DEV, dev, host, say, sync_counters, token_counters, upload_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +51,39 @@ def test_expert_step_wait_gives_up():
     route()
     experts()
     torch.cuda.synchronize()
+    bufs.check_sync()
+
+
+def test_finalize_in_launch_wait_gives_up():
+    """moe_experts_finalize's one-launch form: token 0's finalizer workgroups
+    wait on its arrival counter (preset out of reach), give up, and the token's
+    last finalizer still returns its counters to 0."""
+    wl = W.WORKLOADS["decode_b8"]
+    inp = W.make_inputs(wl)
+    w = upload_weights(inp)
+    bufs = LY.Buffers(LY.LayerShape(wl.T, wl.H, wl.I, wl.E, wl.K, wl.tile_m, 1), DEV)
+    L = bufs.layout
+    logits, x, gs, nw = dev(inp.logits), dev(inp.x_bf16), dev(inp.a1_gscale), dev(inp.norm_weight_bf16)
+
+    def run(preset):
+        N.moe_route_quant(logits, None, None, wl.K, 1.0, wl.tile_m, 0, wl.E, bufs.ids, bufs.weights, bufs.meta,
+                          x, gs, bufs.a_codes, bufs.a_sf)
+        if preset:
+            bufs.meta[L.tok_sync] = UNREACHABLE
+        N.moe_experts_finalize(bufs.a_codes, bufs.a_sf, bufs.meta, w, wl.T, wl.K, wl.E, wl.H, wl.I, wl.tile_m,
+                               bufs.inter_codes, bufs.inter_sf, bufs.rows, 1, bufs.rows.stride(0), bufs.weights, nw,
+                               wl.gain_center, wl.eps, bool(wl.weight_before_norm), bufs.out)
+        torch.cuda.synchronize()
+        return host(bufs.meta)
+
+    say("moe_experts_finalize decode_b8 with token 0's arrival counter preset out of reach")
+    meta = run(True)
+    assert meta[L.sync_status] == 1
+    assert not sync_counters(meta, L).any() and not token_counters(meta, L, wl.T).any()
+    with pytest.raises(N.MoeError):
+        bufs.check_sync()
+    meta = run(False)
+    assert meta[L.sync_status] == 0
     bufs.check_sync()
 
 
