@@ -414,7 +414,8 @@ __global__ void __launch_bounds__(kW16Threads) w16_wg_gemm2_kernel(W16Args a) {
     w16_gemm2_epilogue<kBf16>(e, rt, ex, c, n, q, acc0, acc1);
 }
 
-// Both GEMMs in one launch (H and I multiples of 256): workgroups [0, g1_blocks)
+// Both GEMMs in one launch (H and I multiples of 256; for W4A16, 128 routes or
+// more -- w16_launch): workgroups [0, g1_blocks)
 // are w16_wg_gemm1_kernel's, the rest w16_wg_gemm2_kernel's, as in the W4A4
 // one-launch kernel (experts.hip). A GEMM1 workgroup writes its part of the
 // bf16 intermediate with agent-coherent stores, waits until they have
